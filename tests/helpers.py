@@ -1,0 +1,103 @@
+"""Test-side glue: turn a synthetic workload into oracle inputs and buffers.
+
+Source shards are cut from the seeded global tensor with the oracle's own
+shard boxes; destinations start as poison-filled byte images so that bytes a
+reshard must not touch can be checked too.
+"""
+
+import numpy as np
+
+import oracle
+from oracle import layout as olayout
+from oracle import golden as ogolden
+from rl_weight_refit_amd import synth
+
+UINT = {1: np.uint8, 2: np.uint16, 4: np.uint32, 8: np.uint64}
+
+
+def odesc(tensor, side_name):
+    s = tensor[side_name]
+    dtype = tensor["dtype"]
+    if side_name == "dst" and s.get("quant") == "mxfp8":
+        dtype = "u8"
+    return {"shape": list(tensor["shape"]), "dtype": dtype, "mesh": list(s["mesh"]),
+            "placements": list(s["placements"]), "slot_of_coord": s.get("slot_of_coord"),
+            "quant": s.get("quant")}
+
+
+def src_desc_for(tensor):
+    d = odesc(tensor, "src")
+    d["dtype"] = tensor["dtype"]
+    return d
+
+
+def dense_bytes(arr):
+    return np.ascontiguousarray(arr).view(np.uint8).reshape(-1)
+
+
+def source_buffers(tensor, G):
+    """Per source slot: dense byte image of the slot's shard (oracle boxes)."""
+    desc = src_desc_for(tensor)
+    out = []
+    for box in olayout.slot_boxes(desc):
+        part = G[ogolden.box_slices(box)]
+        out.append({"buf": dense_bytes(part).copy(), "view": None})
+    return out
+
+
+def alloc_destinations(workload, poison=0xA5):
+    """Host images for every destination buffer, filled with `poison`.
+
+    Returns (named, per_tensor) where named[key] is the image of a shared
+    buffer and per_tensor[t][k] is the dict the oracle writes slot k through.
+    """
+    named = {}
+    for key, b in workload["buffers"].items():
+        nbytes = b["elems"] * synth.ELEM_BYTES[b["dtype"]]
+        named[key] = np.full(nbytes, poison, dtype=np.uint8)
+    per_tensor = []
+    for t in workload["tensors"]:
+        d = t["dst"]
+        desc = odesc(t, "dst")
+        esize = 1 if d.get("quant") == "mxfp8" else synth.ELEM_BYTES[t["dtype"]]
+        slots = []
+        boxes = olayout.slot_boxes(desc)
+        for k, box in enumerate(boxes):
+            if d["slots"] is None:
+                nbytes = olayout.box_volume(box) * esize
+                e = {"buf": np.full(nbytes, poison, dtype=np.uint8), "view": None}
+            else:
+                e = {"buf": named[d["slots"][k]["buf"]], "view": d["slots"][k]["view"]}
+            if d.get("quant") == "mxfp8":
+                if d.get("scale_slots") is None:
+                    ln = box[1]
+                    nsc = olayout.box_volume((None, list(ln[:-1]) + [-(-ln[-1] // 32)]))
+                    e["scale_buf"] = np.full(nsc, poison, dtype=np.uint8)
+                    e["scale_view"] = None
+                else:
+                    e["scale_buf"] = named[d["scale_slots"][k]["buf"]]
+                    e["scale_view"] = d["scale_slots"][k]["view"]
+            slots.append(e)
+        per_tensor.append(slots)
+    return named, per_tensor
+
+
+def golden_workload(workload, poison=0xA5, globals_=None):
+    """Run the oracle on a whole workload.
+
+    Returns (globals, sources, named, per_tensor): the global tensors, the
+    source byte images per tensor, and the destination images after the
+    oracle wrote them.
+    """
+    if globals_ is None:
+        globals_ = [synth.host_values(t) for t in workload["tensors"]]
+    sources = [source_buffers(t, G) for t, G in zip(workload["tensors"], globals_)]
+    named, per_tensor = alloc_destinations(workload, poison)
+    for t, src, dst in zip(workload["tensors"], sources, per_tensor):
+        ogolden.reshard(src_desc_for(t), odesc(t, "dst"), src, dst)
+    return globals_, sources, named, per_tensor
+
+
+def local_arrays(tensor, G, side_name):
+    desc = src_desc_for(tensor) if side_name == "src" else odesc(tensor, side_name)
+    return [np.ascontiguousarray(G[ogolden.box_slices(b)]) for b in olayout.slot_boxes(desc)]
