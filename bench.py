@@ -1,0 +1,319 @@
+#!/usr/bin/env python3
+"""Benchmark of the single-GPU M->N relayout on the DeepSeek-V3-shaped MoE
+layer: 256 experts, hidden 7168, expert intermediate 2048 (gate, up, down =
+22,548,578,304 bytes of bf16), source EP16 Shard(0) -> destination EP8 x TP8
+with fused gate/up (w13) destinations, N(0, 0.02) values generated on the
+GPU.
+
+One step = one pass of the whole path over that layer:
+  1. the bf16 -> bf16 relayout (reshard_execute of the plain plan), and
+  2. the BF16 -> MXFP8 install variant (reshard_execute of the MXFP8 plan).
+Both plans are built once before timing (plans are reused across refits);
+their CPU cost is reported separately as plan_us (p50 / p99 over 1000
+calls).  Inputs are resident in HBM before the timed region.
+
+Output: one JSON line.  value = algorithmic bytes (each needed source byte
+read once + every destination byte written, both variants) per second of
+the timed steps, in GB/s.  The roofline object is for the dominant kernel
+(the bulk copy kernel of step 1), timed with HIP events on the stream it is
+launched on.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "rs_bulk_kernel_moe_dsv3_counters.json")
+KERNEL_SOURCE = os.path.join(ROOT, "rl_weight_refit_amd", "csrc", "kernels.hip")
+
+
+def kernel_hash():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--variant", choices=["both", "copy", "mxfp8"], default="both")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--plan-reps", type=int, default=1000)
+    ap.add_argument("--ceiling-bytes", type=int, default=8 << 30)
+    return ap.parse_args()
+
+
+def spec(tensor, side_name):
+    s = tensor[side_name]
+    dtype = tensor["dtype"]
+    if side_name == "dst" and s.get("quant") == "mxfp8":
+        dtype = "u8"
+    return {"shape": tensor["shape"], "dtype": dtype, "mesh": s["mesh"],
+            "placements": s["placements"], "slot_of_coord": s.get("slot_of_coord"),
+            "views": None if s["slots"] is None else [e["view"] for e in s["slots"]],
+            "quant": s.get("quant") if side_name == "dst" else None,
+            "scale_views": None if s.get("scale_slots") is None
+            else [e["view"] for e in s["scale_slots"]]}
+
+
+def plan_of(binding, wl):
+    return binding.reshard_plan([spec(t, "src") for t in wl["tensors"]],
+                                [spec(t, "dst") for t in wl["tensors"]])
+
+
+def plan_times(binding, wl, reps):
+    src = [spec(t, "src") for t in wl["tensors"]]
+    dst = [spec(t, "dst") for t in wl["tensors"]]
+    ns = []
+    for i in range(reps + 10):
+        p = binding.reshard_plan(src, dst)
+        if i >= 10:
+            ns.append(p.info()["plan_ns"])
+        p.destroy()
+    ns.sort()
+    return {"p50": ns[len(ns) // 2] / 1e3, "p99": ns[min(len(ns) - 1, int(len(ns) * 0.99))] / 1e3}
+
+
+def device_sources(torch, binding, wl):
+    """Source shards cut from the seeded device-generated global tensors, with
+    the library's own shard boxes."""
+    from rl_weight_refit_amd import synth
+    out = []
+    for t in wl["tensors"]:
+        G = synth.device_values(t, "cuda")
+        sp = spec(t, "src")
+        nslots = int(np.prod(sp["mesh"]))
+        shards = []
+        for k in range(nslots):
+            off, ln = binding.reshard_shard_box(sp, k)
+            sl = tuple(slice(o, o + n) for o, n in zip(off, ln))
+            shards.append(G[sl].contiguous())
+        del G
+        out.append(shards)
+    torch.cuda.synchronize()
+    return out
+
+
+def device_destinations(torch, binding, wl):
+    from rl_weight_refit_amd import synth
+    named = {k: torch.empty(b["elems"] * synth.ELEM_BYTES[b["dtype"]], dtype=torch.uint8,
+                            device="cuda") for k, b in wl["buffers"].items()}
+    ptrs = []
+    for t in wl["tensors"]:
+        d = t["dst"]
+        ptrs += [named[e["buf"]].data_ptr() for e in d["slots"]]
+        if d.get("quant") == "mxfp8":
+            ptrs += [named[e["buf"]].data_ptr() for e in d["scale_slots"]]
+    return named, ptrs
+
+
+def copy_ceiling(torch, nbytes, stream):
+    """Plain device-to-device copy of nbytes (torch's copy kernel), GB/s of
+    read + write, best of 5."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    best = 0.0
+    with torch.cuda.stream(stream):
+        for _ in range(6):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            b.copy_(a)
+            e1.record(stream)
+            e1.synchronize()
+            best = max(best, 2 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del a, b
+    return best
+
+
+def cpu_baseline():
+    """The oracle (as it stands) on a bounded sample of the same workload: the
+    same layer shape and meshes with 8 experts instead of 256 (1/32 of the
+    bytes), bf16 relayout plus MXFP8 install, on the host."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from oracle import golden as ogolden
+    from rl_weight_refit_amd import synth
+    import helpers  # test-side glue: oracle inputs from a workload
+
+    total_bytes = 0
+    elapsed = 0.0
+    for quant in (None, "mxfp8"):
+        wl = synth.moe_experts(8, 7168, 2048, 8, 8, 8, seed=5, quant=quant)
+        for t in wl["tensors"]:
+            G = synth.host_values(t)
+            src = helpers.source_buffers(t, G)
+            del G
+            one = dict(wl)
+            one["tensors"] = [t]
+            _, per = helpers.alloc_destinations(one)
+            t0 = time.perf_counter()
+            ogolden.reshard(helpers.src_desc_for(t), helpers.odesc(t, "dst"), src, per[0])
+            elapsed += time.perf_counter() - t0
+            n = int(np.prod(t["shape"]))
+            # bf16 relayout: 2n read + 2n written; MXFP8: 2n read + n codes + n/32 scales
+            total_bytes += 4 * n if quant is None else 3 * n + n // 32
+            del src, per
+    return {"value": round(total_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "same layer shape with 8 of 256 experts (1/32 of the bytes), EP8 -> EP8xTP8, "
+                      "bf16 relayout + MXFP8 install, numpy on the host, %.1f s" % elapsed}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this relayout runs all source and destination "
+              "shards in one GPU's memory; --gpus %d is not supported" % args.gpus,
+              file=sys.stderr)
+        return 2
+    import torch
+    from rl_weight_refit_amd import binding, synth
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    binding.load()
+    torch.cuda.set_device(0)
+
+    wl_copy = synth.moe_dsv3()
+    wl_mx = synth.moe_dsv3(quant="mxfp8")
+    do_copy = args.variant in ("both", "copy")
+    do_mx = args.variant in ("both", "mxfp8")
+
+    plan_us = {}
+    if args.plan_reps > 0:
+        if do_copy:
+            plan_us["bf16"] = plan_times(binding, wl_copy, args.plan_reps)
+        if do_mx:
+            plan_us["mxfp8"] = plan_times(binding, wl_mx, args.plan_reps)
+    p_copy = plan_of(binding, wl_copy)
+    p_mx = plan_of(binding, wl_mx)
+    i_copy, i_mx = p_copy.info(), p_mx.info()
+    print("planned: bf16 %d regions %d launches; mxfp8 %d regions %d launches"
+          % (i_copy["n_regions"], i_copy["n_launches"], i_mx["n_regions"], i_mx["n_launches"]),
+          file=sys.stderr, flush=True)
+
+    stream = torch.cuda.Stream()
+    ceiling = copy_ceiling(torch, args.ceiling_bytes, stream) if args.ceiling_bytes else None
+    print("copy ceiling %.1f GB/s" % (ceiling or 0), file=sys.stderr, flush=True)
+
+    src = device_sources(torch, binding, wl_copy)
+    src_ptrs = [s.data_ptr() for shards in src for s in shards]
+    d_copy, ptr_copy = device_destinations(torch, binding, wl_copy) if do_copy else ({}, [])
+    d_mx, ptr_mx = device_destinations(torch, binding, wl_mx) if do_mx else ({}, [])
+    torch.cuda.synchronize()
+    print("buffers ready", file=sys.stderr, flush=True)
+
+    sh = stream.cuda_stream
+
+    def step(ev):
+        if do_copy:
+            ev[0].record(stream)
+            binding.reshard_execute(p_copy, src_ptrs, ptr_copy, sh)
+            ev[1].record(stream)
+        if do_mx:
+            ev[2].record(stream)
+            binding.reshard_execute(p_mx, src_ptrs, ptr_mx, sh)
+            ev[3].record(stream)
+
+    def events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    for _ in range(args.warmup):
+        step(events())
+    torch.cuda.synchronize()
+    evs = [events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    stream.synchronize()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print("timed %d steps in %.3f s" % (args.steps, wall), file=sys.stderr, flush=True)
+
+    t_copy = [e[0].elapsed_time(e[1]) for e in evs] if do_copy else []
+    t_mx = [e[2].elapsed_time(e[3]) for e in evs] if do_mx else []
+    bytes_copy = i_copy["bytes_read"] + i_copy["bytes_written"]
+    bytes_mx = i_mx["bytes_read"] + i_mx["bytes_written"]
+    step_bytes = (bytes_copy if do_copy else 0) + (bytes_mx if do_mx else 0)
+    value = step_bytes * args.steps / wall / 1e9
+
+    def stats(ts, nbytes):
+        if not ts:
+            return None
+        med = statistics.median(ts)
+        return {"ms_median": round(med, 4), "ms_min": round(min(ts), 4),
+                "ms_max": round(max(ts), 4),
+                "GBps": round(nbytes / (med * 1e-3) / 1e9, 1),
+                "pct_peak": round(100 * nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+                "pct_ceiling": round(100 * nbytes / (med * 1e-3) / 1e9 / ceiling, 2)
+                if ceiling else None,
+                "bytes": nbytes}
+
+    dominant = "rs_bulk_kernel" if do_copy else "rs_mx_kernel"
+    dom_ts = t_copy if do_copy else t_mx
+    dom_bytes = bytes_copy if do_copy else bytes_mx
+    achieved = dom_bytes / (statistics.mean(dom_ts) * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(PROFILE_COUNTERS):
+        with open(PROFILE_COUNTERS) as f:
+            c = json.load(f)
+        if c.get("kernel_source_sha256_16") == kernel_hash() and c.get("kernel") == dominant:
+            traffic = c.get("traffic_bytes_per_launch")
+
+    out = {
+        "metric": "reshard effective HBM GB/s (read+write) and % of MI355X HBM peak; plan us",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16->bf16 copy + bf16->mxfp8(e4m3/e8m0)" if args.variant == "both"
+        else ("bf16" if do_copy else "bf16->mxfp8"),
+        "data": "synthetic: N(0,0.02) bf16 generated on the GPU (torch generator, seed 5000+i)",
+        "config": {"workload": "moe_dsv3_layer: 256 experts x hidden 7168 x expert intermediate "
+                               "2048, gate/up/down bf16, EP16 Shard(0) -> EP8xTP8, fused w13; "
+                               "plus the BF16->MXFP8 install variant",
+                   "variant": args.variant, "step_bytes": step_bytes},
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "copy_ceiling_GBps": round(ceiling, 1) if ceiling else None,
+        "bf16": stats(t_copy, bytes_copy),
+        "mxfp8": stats(t_mx, bytes_mx),
+        "plan_us": plan_us,
+        "plan": {"bf16": {k: i_copy[k] for k in ("n_regions", "n_launches", "bytes_read",
+                                                  "bytes_written")},
+                 "mxfp8": {k: i_mx[k] for k in ("n_regions", "n_launches", "bytes_read",
+                                                 "bytes_written")}},
+        "roofline": {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
+        "device": torch.cuda.get_device_name(0),
+    }
+    del src, d_copy, d_mx
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        print("cpu baseline ...", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,199 @@
+// C ABI of the relayout library: plan objects, argument checks, device table
+// upload and kernel launches.  See include/reshard.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <sstream>
+#include <string>
+#include <vector>
+
+#include "planner.hpp"
+#include "reshard.h"
+#include "rs_device.hpp"
+
+namespace rs {
+hipError_t launch(uint32_t bucket, uint32_t grid, const LaunchArgs& args, hipStream_t stream);
+}
+
+struct rs_plan {
+  rs::PlanData d;
+  mutable std::mutex mu;
+  struct DevTable {
+    int device;
+    void* ptr;
+  };
+  mutable std::vector<DevTable> tables;  // one upload of d.image per device
+};
+
+namespace {
+
+thread_local std::string g_error;
+
+rs_status fail(rs_status s, const std::string& msg) {
+  g_error = msg;
+  return s;
+}
+
+bool debug_checks() {
+  const char* e = std::getenv("RESHARD_DEBUG_CHECKS");
+  return e && e[0] == '1';
+}
+
+}  // namespace
+
+extern "C" {
+
+rs_status reshard_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32_t n_tensors,
+                       const rs_plan_opts* opts, rs_plan** out) {
+  g_error.clear();
+  if (!out) return fail(RS_ERR_INVALID, "out is NULL\n");
+  *out = nullptr;
+  rs_plan* p = new (std::nothrow) rs_plan();
+  if (!p) return fail(RS_ERR_ALLOC, "cannot allocate a plan\n");
+  std::string err;
+  rs_status st;
+  try {
+    st = rs::build_plan(src, dst, n_tensors, opts, p->d, err);
+  } catch (const std::bad_alloc&) {
+    st = RS_ERR_ALLOC;
+    err = "host allocation failed while planning\n";
+  }
+  if (st != RS_OK) {
+    delete p;
+    return fail(st, err);
+  }
+  *out = p;
+  return RS_OK;
+}
+
+rs_status reshard_execute(const rs_plan* plan, void* const* src_ptrs, void* const* dst_ptrs,
+                          void* stream) {
+  g_error.clear();
+  if (!plan) return fail(RS_ERR_INVALID, "plan is NULL\n");
+  const rs::PlanData& d = plan->d;
+  std::ostringstream err;
+  int nerr = 0;
+  if (d.info.n_src_ptrs && !src_ptrs) {
+    err << "src_ptrs is NULL but the plan has " << d.info.n_src_ptrs << " source slots\n";
+    ++nerr;
+  }
+  if (d.info.n_dst_ptrs && !dst_ptrs) {
+    err << "dst_ptrs is NULL but the plan has " << d.info.n_dst_ptrs << " destination slots\n";
+    ++nerr;
+  }
+  if (nerr) return fail(RS_ERR_INVALID, err.str());
+  for (size_t i = 0; i < d.src_used.size(); ++i) {
+    if (d.src_used[i] && !src_ptrs[i]) {
+      err << "src_ptrs[" << i << "] is NULL but that source slot is read\n";
+      ++nerr;
+    } else if (src_ptrs[i] && reinterpret_cast<uintptr_t>(src_ptrs[i]) % d.src_align[i]) {
+      err << "src_ptrs[" << i << "] is not aligned to its element size " << int(d.src_align[i])
+          << "\n";
+      ++nerr;
+    }
+  }
+  for (size_t i = 0; i < d.dst_used.size(); ++i)
+    if (d.dst_used[i] && !dst_ptrs[i]) {
+      err << "dst_ptrs[" << i << "] is NULL but that destination slot is written\n";
+      ++nerr;
+    }
+  if (!nerr && debug_checks()) {
+    // Sources and destinations must not overlap (byte ranges each pointer's
+    // regions reach).
+    for (size_t i = 0; i < d.src_used.size(); ++i) {
+      if (!d.src_used[i]) continue;
+      const uintptr_t a0 = reinterpret_cast<uintptr_t>(src_ptrs[i]), a1 = a0 + d.src_span[i];
+      for (size_t j = 0; j < d.dst_used.size(); ++j) {
+        if (!d.dst_used[j]) continue;
+        const uintptr_t b0 = reinterpret_cast<uintptr_t>(dst_ptrs[j]), b1 = b0 + d.dst_span[j];
+        if (a0 < b1 && b0 < a1) {
+          err << "src_ptrs[" << i << "] and dst_ptrs[" << j << "] overlap\n";
+          ++nerr;
+        }
+      }
+    }
+  }
+  if (nerr) return fail(RS_ERR_INVALID, err.str());
+  if (d.launches.empty()) return RS_OK;
+
+  int dev = 0;
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess) return fail(RS_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(he) + "\n");
+  char* base = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(plan->mu);
+    for (const auto& t : plan->tables)
+      if (t.device == dev) base = static_cast<char*>(t.ptr);
+    if (!base) {
+      void* p = nullptr;
+      he = hipMalloc(&p, d.image.size());
+      if (he != hipSuccess)
+        return fail(RS_ERR_ALLOC, std::string("hipMalloc of the plan tables: ") + hipGetErrorString(he) + "\n");
+      he = hipMemcpy(p, d.image.data(), d.image.size(), hipMemcpyHostToDevice);
+      if (he != hipSuccess) {
+        (void)hipFree(p);
+        return fail(RS_ERR_HIP, std::string("upload of the plan tables: ") + hipGetErrorString(he) + "\n");
+      }
+      plan->tables.push_back({dev, p});
+      base = static_cast<char*>(p);
+    }
+  }
+  for (const rs::Launch& L : d.launches) {
+    rs::LaunchArgs args;
+    std::memset(&args, 0, sizeof(args));
+    args.regions = base + L.regions_off;
+    args.unit_region = L.units_off ? reinterpret_cast<const uint32_t*>(base + L.units_off) : nullptr;
+    args.n_regions = L.n_regions;
+    args.n_units = L.n_units;
+    for (size_t k = 0; k < L.pool.size(); ++k) {
+      const uint32_t e = L.pool[k];
+      args.ptr[k] = (e & rs::kDstBit) ? dst_ptrs[e & ~rs::kDstBit] : src_ptrs[e];
+    }
+    he = rs::launch(L.bucket, L.n_units, args, static_cast<hipStream_t>(stream));
+    if (he != hipSuccess)
+      return fail(RS_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(he) + "\n");
+  }
+  return RS_OK;
+}
+
+rs_status reshard_plan_info(const rs_plan* plan, rs_plan_info* info) {
+  g_error.clear();
+  if (!plan || !info) return fail(RS_ERR_INVALID, "plan or info is NULL\n");
+  *info = plan->d.info;
+  return RS_OK;
+}
+
+rs_status reshard_plan_region(const rs_plan* plan, uint64_t index, rs_region* out) {
+  g_error.clear();
+  if (!plan || !out) return fail(RS_ERR_INVALID, "plan or out is NULL\n");
+  if (index >= plan->d.regions.size()) return fail(RS_ERR_INVALID, "region index out of range\n");
+  *out = plan->d.regions[index];
+  return RS_OK;
+}
+
+rs_status reshard_shard_box(const rs_tensor_desc* desc, int64_t slot, int64_t* offsets,
+                            int64_t* lengths) {
+  g_error.clear();
+  std::string err;
+  const rs_status st = rs::shard_box(desc, slot, offsets, lengths, err);
+  if (st != RS_OK) return fail(st, err);
+  return RS_OK;
+}
+
+void reshard_plan_destroy(rs_plan* plan) {
+  if (!plan) return;
+  int cur = -1;
+  const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  for (const auto& t : plan->tables) {
+    if (hipSetDevice(t.device) == hipSuccess) (void)hipFree(t.ptr);
+  }
+  if (have_cur && !plan->tables.empty()) (void)hipSetDevice(cur);
+  delete plan;
+}
+
+const char* reshard_last_error(void) { return g_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,923 @@
+// CPU planner of the single-GPU M->N relayout.
+//
+// Steps (all integer arithmetic):
+//  1. Layout resolution: every slot's global box.  Shard(d) cuts dim d like
+//     torch.chunk (chunk = ceil(len/parts), trailing chunks short or empty);
+//     mesh dims sharding the same tensor dim nest in mesh-dim order.  The
+//     pages describe a layout as global shape + device mesh + placements
+//     (news summary of NVIDIA's Reshard announcement, "Recasting refit as a
+//     DTensor-to-DTensor transfer").
+//  2. Intersection: per tensor dim, a linear sweep over the sorted source and
+//     destination intervals gives the overlapping pieces; their Cartesian
+//     product gives the exact overlap boxes ("NCCL Reshard Refit
+//     (Experimental)", "xferdtensor Transports": the Python transport
+//     computes the exact shard overlaps and moves each destination region
+//     once).  One source replica is read per box (replicas hold the same
+//     bytes; cf. the geometry-based replica deduplication of the ModelExpress
+//     PR #3632) and destination replicas with equal views share that read.
+//  3. Views: a destination may be a slice of a fused buffer (gate/up in one
+//     w13 buffer, "Execution Flow: Setup Time"), so region addresses go
+//     through per-slot (base, strides) views and land in place.
+//  4. Coalescing, chunking and bucketing: element size folds into the
+//     innermost run, runs merge while both sides stay contiguous, outer dims
+//     merge when both sides allow it, long runs split into work units; each
+//     region goes to one of four kernels (bulk, LDS-staged thin, batched
+//     tiny, MXFP8).  All regions of a bucket run in one launch, which is the
+//     one-launch-per-batch idea of the coalesced collective in "NeMo-RL:
+//     Optimizing Non-Colocated Refit for Asynchronous RL", "Optimization #2".
+#include "planner.hpp"
+
+#include <algorithm>
+#include <chrono>
+#include <cstring>
+#include <map>
+#include <sstream>
+#include <utility>
+
+namespace rs {
+namespace {
+
+constexpr int64_t kMaxSlots = 65536;
+constexpr uint64_t kMaxRows = (1ull << 31) - 1;
+constexpr uint32_t kMaxUnitsPerLaunch = 1u << 23;
+constexpr int kMxBlock = 32;
+
+int esize_of(int32_t dt) {
+  switch (dt) {
+    case RS_U8: case RS_I8: return 1;
+    case RS_U16: case RS_I16: case RS_BF16: case RS_F16: return 2;
+    case RS_U32: case RS_I32: case RS_F32: return 4;
+    case RS_U64: case RS_I64: case RS_F64: return 8;
+    default: return 0;
+  }
+}
+
+struct Errors {
+  std::ostringstream text;
+  int invalid = 0, mismatch = 0, unsupported = 0;
+  template <class... A>
+  void add(int* counter, A&&... parts) {
+    ++*counter;
+    (text << ... << parts);
+    text << "\n";
+  }
+  rs_status status() const {
+    if (invalid) return RS_ERR_INVALID;
+    if (mismatch) return RS_ERR_MISMATCH;
+    if (unsupported) return RS_ERR_UNSUPPORTED;
+    return RS_OK;
+  }
+};
+
+struct Interval {
+  int64_t start, len;
+};
+
+// A validated layout (one side of one tensor).
+struct Layout {
+  int ndim = 0, esize = 0, dtype = 0, quant = 0;
+  int64_t shape[RS_MAX_DIMS] = {};
+  int mesh_ndim = 0;
+  int64_t mesh[RS_MAX_MESH] = {};
+  int pl[RS_MAX_MESH] = {};
+  int64_t nslots = 0;
+  std::vector<int32_t> coord_to_slot;  // linear mesh coord -> slot
+  std::vector<int32_t> slot_to_coord;  // slot -> linear mesh coord
+  std::vector<int> shard_md[RS_MAX_DIMS];   // mesh dims sharding tensor dim d, in order
+  std::vector<Interval> iv[RS_MAX_DIMS];    // interval index -> interval
+  std::vector<int> rep_md;                  // Replicate mesh dims, in order
+  int64_t nrep = 1;
+  std::vector<rs_view> views;               // resolved per slot
+  std::vector<rs_view> scale_views;         // MXFP8 destinations
+  std::vector<Interval> box;                // slot * ndim + d
+
+  int64_t coord_of(int64_t lin, int md) const {
+    int64_t div = 1;
+    for (int i = md + 1; i < mesh_ndim; ++i) div *= mesh[i];
+    return (lin / div) % mesh[md];
+  }
+  const Interval* slot_box(int64_t slot) const { return &box[slot * ndim]; }
+};
+
+void chunk(int64_t len, int64_t parts, int64_t idx, int64_t* start, int64_t* n) {
+  const int64_t cs = len > 0 ? (len + parts - 1) / parts : 0;
+  const int64_t a = std::min(idx * cs, len);
+  const int64_t b = std::min((idx + 1) * cs, len);
+  *start = a;
+  *n = b - a;
+}
+
+void dense_view(const Interval* box, int ndim, int64_t last_div, rs_view* v) {
+  std::memset(v, 0, sizeof(*v));
+  int64_t acc = 1;
+  for (int d = ndim - 1; d >= 0; --d) {
+    v->strides[d] = acc;
+    int64_t n = box[d].len;
+    if (d == ndim - 1 && last_div > 1) n = (n + last_div - 1) / last_div;
+    acc *= n;
+  }
+}
+
+bool parse_layout(const rs_tensor_desc* d, const char* side, int t, bool is_dst, Layout& L,
+                  Errors& E) {
+  const int before = E.invalid;
+  if (!d) {
+    E.add(&E.invalid, "tensor ", t, " ", side, ": description is NULL");
+    return false;
+  }
+  if (d->ndim < 1 || d->ndim > RS_MAX_DIMS) {
+    E.add(&E.invalid, "tensor ", t, " ", side, ": ndim ", d->ndim, " not in [1, ", RS_MAX_DIMS, "]");
+    return false;
+  }
+  L.ndim = d->ndim;
+  L.dtype = d->dtype;
+  L.esize = esize_of(d->dtype);
+  if (!L.esize) E.add(&E.invalid, "tensor ", t, " ", side, ": unknown dtype ", d->dtype);
+  for (int i = 0; i < L.ndim; ++i) {
+    L.shape[i] = d->global_shape[i];
+    if (L.shape[i] < 0)
+      E.add(&E.invalid, "tensor ", t, " ", side, ": global_shape[", i, "] = ", L.shape[i], " < 0");
+  }
+  if (d->mesh_ndim < 1 || d->mesh_ndim > RS_MAX_MESH) {
+    E.add(&E.invalid, "tensor ", t, " ", side, ": mesh_ndim ", d->mesh_ndim, " not in [1, ",
+          RS_MAX_MESH, "]");
+    return false;
+  }
+  L.mesh_ndim = d->mesh_ndim;
+  L.nslots = 1;
+  bool mesh_ok = true;
+  for (int i = 0; i < L.mesh_ndim; ++i) {
+    L.mesh[i] = d->mesh_shape[i];
+    L.pl[i] = d->placements[i];
+    if (L.mesh[i] < 1) {
+      E.add(&E.invalid, "tensor ", t, " ", side, ": mesh_shape[", i, "] = ", L.mesh[i], " < 1");
+      mesh_ok = false;
+    } else if (L.nslots <= kMaxSlots) {
+      L.nslots *= L.mesh[i];
+    }
+    if (L.pl[i] != RS_REPLICATE && (L.pl[i] < 0 || L.pl[i] >= L.ndim))
+      E.add(&E.invalid, "tensor ", t, " ", side, ": placements[", i, "] = ", L.pl[i],
+            " is neither Replicate (-1) nor a tensor dim < ", L.ndim);
+  }
+  if (mesh_ok && L.nslots > kMaxSlots) {
+    E.add(&E.invalid, "tensor ", t, " ", side, ": mesh has more than ", kMaxSlots, " slots");
+    mesh_ok = false;
+  }
+  if (d->quant != RS_Q_NONE && d->quant != RS_Q_MXFP8_E4M3)
+    E.add(&E.invalid, "tensor ", t, " ", side, ": unknown quant mode ", d->quant);
+  if (!is_dst && d->quant != RS_Q_NONE)
+    E.add(&E.invalid, "tensor ", t, " ", side, ": quant is a destination setting");
+  L.quant = is_dst ? d->quant : RS_Q_NONE;
+  if (!mesh_ok || E.invalid != before) return false;
+
+  L.coord_to_slot.resize(L.nslots);
+  L.slot_to_coord.assign(L.nslots, -1);
+  for (int64_t c = 0; c < L.nslots; ++c) {
+    const int64_t s = d->slot_of_coord ? d->slot_of_coord[c] : c;
+    if (s < 0 || s >= L.nslots || L.slot_to_coord[s] != -1) {
+      E.add(&E.invalid, "tensor ", t, " ", side, ": slot_of_coord is not a permutation of 0..",
+            L.nslots - 1, " (entry ", c, " = ", s, ")");
+      return false;
+    }
+    L.coord_to_slot[c] = static_cast<int32_t>(s);
+    L.slot_to_coord[s] = static_cast<int32_t>(c);
+  }
+
+  for (int i = 0; i < L.mesh_ndim; ++i) {
+    if (L.pl[i] == RS_REPLICATE) {
+      L.rep_md.push_back(i);
+      L.nrep *= L.mesh[i];
+    } else {
+      L.shard_md[L.pl[i]].push_back(i);
+    }
+  }
+  for (int dd = 0; dd < L.ndim; ++dd) {
+    std::vector<Interval> cur{{0, L.shape[dd]}};
+    for (int md : L.shard_md[dd]) {
+      std::vector<Interval> next;
+      next.reserve(cur.size() * L.mesh[md]);
+      for (const Interval& p : cur)
+        for (int64_t c = 0; c < L.mesh[md]; ++c) {
+          int64_t a, n;
+          chunk(p.len, L.mesh[md], c, &a, &n);
+          next.push_back({p.start + a, n});
+        }
+      cur.swap(next);
+    }
+    L.iv[dd] = std::move(cur);
+  }
+  L.box.resize(L.nslots * L.ndim);
+  for (int64_t s = 0; s < L.nslots; ++s) {
+    const int64_t lin = L.slot_to_coord[s];
+    for (int dd = 0; dd < L.ndim; ++dd) {
+      int64_t idx = 0;
+      for (int md : L.shard_md[dd]) idx = idx * L.mesh[md] + L.coord_of(lin, md);
+      L.box[s * L.ndim + dd] = L.iv[dd][idx];
+    }
+  }
+
+  L.views.resize(L.nslots);
+  for (int64_t s = 0; s < L.nslots; ++s) {
+    if (d->views) {
+      L.views[s] = d->views[s];
+      if (L.views[s].base < 0)
+        E.add(&E.invalid, "tensor ", t, " ", side, ": views[", s, "].base < 0");
+      for (int i = 0; i < L.ndim; ++i)
+        if (L.views[s].strides[i] < 0)
+          E.add(&E.invalid, "tensor ", t, " ", side, ": views[", s, "].strides[", i, "] < 0");
+    } else {
+      dense_view(L.slot_box(s), L.ndim, 1, &L.views[s]);
+    }
+  }
+  if (L.quant == RS_Q_MXFP8_E4M3) {
+    L.scale_views.resize(L.nslots);
+    for (int64_t s = 0; s < L.nslots; ++s) {
+      if (d->scale_views) {
+        L.scale_views[s] = d->scale_views[s];
+        if (L.scale_views[s].base < 0)
+          E.add(&E.invalid, "tensor ", t, " ", side, ": scale_views[", s, "].base < 0");
+        for (int i = 0; i < L.ndim; ++i)
+          if (L.scale_views[s].strides[i] < 0)
+            E.add(&E.invalid, "tensor ", t, " ", side, ": scale_views[", s, "].strides[", i, "] < 0");
+      } else {
+        dense_view(L.slot_box(s), L.ndim, kMxBlock, &L.scale_views[s]);
+      }
+    }
+  }
+  return E.invalid == before;
+}
+
+// Overlapping pieces of two partitions of one tensor dim.
+struct Piece {
+  int64_t si, di, start, len;
+};
+
+std::vector<Piece> sweep(const std::vector<Interval>& a, const std::vector<Interval>& b) {
+  std::vector<Piece> out;
+  size_t i = 0, j = 0;
+  auto skip = [](const std::vector<Interval>& v, size_t k) {
+    while (k < v.size() && v[k].len == 0) ++k;
+    return k;
+  };
+  i = skip(a, i);
+  j = skip(b, j);
+  while (i < a.size() && j < b.size()) {
+    const int64_t lo = std::max(a[i].start, b[j].start);
+    const int64_t ea = a[i].start + a[i].len, eb = b[j].start + b[j].len;
+    const int64_t hi = std::min(ea, eb);
+    if (hi > lo) out.push_back({int64_t(i), int64_t(j), lo, hi - lo});
+    if (ea <= eb) i = skip(a, i + 1);
+    if (eb <= ea) j = skip(b, j + 1);
+  }
+  return out;
+}
+
+// Linear mesh coordinate from per-dim interval indices and replicate coords.
+int64_t compose_coord(const Layout& L, const int64_t* ividx, int64_t rep_ordinal) {
+  int64_t coord[RS_MAX_MESH] = {};
+  for (int dd = 0; dd < L.ndim; ++dd) {
+    int64_t idx = ividx[dd];
+    for (int k = int(L.shard_md[dd].size()) - 1; k >= 0; --k) {
+      const int md = L.shard_md[dd][k];
+      coord[md] = idx % L.mesh[md];
+      idx /= L.mesh[md];
+    }
+  }
+  for (int k = int(L.rep_md.size()) - 1; k >= 0; --k) {
+    const int md = L.rep_md[k];
+    coord[md] = rep_ordinal % L.mesh[md];
+    rep_ordinal /= L.mesh[md];
+  }
+  int64_t lin = 0;
+  for (int md = 0; md < L.mesh_ndim; ++md) lin = lin * L.mesh[md] + coord[md];
+  return lin;
+}
+
+// Ordinal of a destination class: mixed radix over its sharding coords.
+int64_t class_ordinal(const Layout& L, const int64_t* ividx) {
+  int64_t ord = 0;
+  for (int dd = 0; dd < L.ndim; ++dd) ord = ord * int64_t(L.iv[dd].size()) + ividx[dd];
+  return ord;
+}
+
+bool same_view(const rs_view& a, const rs_view& b, int ndim) {
+  if (a.base != b.base) return false;
+  for (int i = 0; i < ndim; ++i)
+    if (a.strides[i] != b.strides[i]) return false;
+  return true;
+}
+
+// A region before it is split to fit the kernels.
+struct Dim {
+  uint64_t ext, ss, ds, sc;  // extent; byte strides on src, dst, scale sides
+};
+
+struct Raw {
+  uint32_t tensor;
+  bool mx;
+  uint32_t src_index;
+  std::vector<uint32_t> dst_index, sc_index;
+  uint64_t src_off, dst_off, sc_off;
+  uint64_t inner;                 // bytes (copy) or elements (mx)
+  uint64_t sc_inner;
+  std::vector<Dim> outer;         // outermost first
+};
+
+uint64_t rows_of(const std::vector<Dim>& o) {
+  uint64_t r = 1;
+  for (const Dim& d : o) r *= d.ext;
+  return r;
+}
+
+// Merge mergeable adjacent outer dims; drop extent-1 dims.
+void merge_outer(std::vector<Dim>& o, bool with_scale) {
+  std::vector<Dim> v;
+  for (const Dim& d : o)
+    if (d.ext != 1) v.push_back(d);
+  std::vector<Dim> m;
+  for (const Dim& d : v) {
+    if (!m.empty()) {
+      Dim& p = m.back();  // p outer, d inner
+      if (p.ss == d.ext * d.ss && p.ds == d.ext * d.ds && (!with_scale || p.sc == d.ext * d.sc)) {
+        p.ext *= d.ext;
+        p.ss = d.ss;
+        p.ds = d.ds;
+        p.sc = d.sc;
+        continue;
+      }
+    }
+    m.push_back(d);
+  }
+  o.swap(m);
+}
+
+struct Opts {
+  bool fanout = true;
+  uint64_t unit = 65536;
+  uint64_t tiny = 1024;
+  uint64_t thin = 128;
+};
+
+// Splits a raw region until the kernels can take it: at most 3 outer dims,
+// rows < 2^31, every extent < 2^32, and (copy) inner <= unit bytes.
+void finalize(Raw r, const Opts& o, std::vector<Raw>& out) {
+  if (!r.mx && r.inner > o.unit) {
+    const uint64_t q = r.inner / o.unit, rem = r.inner % o.unit;
+    if (rem) {
+      Raw tail = r;
+      tail.inner = rem;
+      tail.src_off += q * o.unit;
+      tail.dst_off += q * o.unit;
+      finalize(std::move(tail), o, out);
+    }
+    r.inner = o.unit;
+    r.outer.push_back({q, o.unit, o.unit, 0});
+    merge_outer(r.outer, false);
+  }
+  const uint64_t rows = rows_of(r.outer);
+  if (rows == 0 || r.inner == 0) return;
+  bool ext_big = false;
+  for (const Dim& d : r.outer) ext_big |= d.ext > 0xFFFFFFFFull;
+  if (r.outer.size() > 3 || rows > kMaxRows || ext_big) {
+    // Peel the outermost dim: either one index at a time (too many dims) or
+    // in halves (too many rows).
+    Dim top = r.outer.front();
+    std::vector<Dim> rest(r.outer.begin() + 1, r.outer.end());
+    if (r.outer.size() > 3) {
+      for (uint64_t i = 0; i < top.ext; ++i) {
+        Raw s = r;
+        s.outer = rest;
+        s.src_off += i * top.ss;
+        s.dst_off += i * top.ds;
+        s.sc_off += i * top.sc;
+        finalize(std::move(s), o, out);
+      }
+    } else {
+      const uint64_t h = top.ext / 2;
+      for (int part = 0; part < 2; ++part) {
+        Raw s = r;
+        s.outer = rest;
+        const uint64_t n = part ? top.ext - h : h;
+        const uint64_t first = part ? h : 0;
+        s.outer.insert(s.outer.begin(), Dim{n, top.ss, top.ds, top.sc});
+        s.src_off += first * top.ss;
+        s.dst_off += first * top.ds;
+        s.sc_off += first * top.sc;
+        finalize(std::move(s), o, out);
+      }
+    }
+    return;
+  }
+  out.push_back(std::move(r));
+}
+
+struct Final {
+  Raw raw;
+  uint32_t bucket;
+  uint32_t flags;
+  uint64_t rows;
+  uint32_t rows_per_unit;
+  uint32_t units;
+};
+
+// Fills the fields shared by the public and device views.
+void outer_fields(const std::vector<Dim>& o, uint64_t ext[3], uint64_t ss[3], uint64_t ds[3],
+                  uint64_t sc[3]) {
+  // Device convention: index 0 is the innermost outer dim.
+  for (int k = 0; k < 3; ++k) {
+    ext[k] = 1;
+    ss[k] = ds[k] = sc[k] = 0;
+  }
+  const int n = int(o.size());
+  for (int k = 0; k < n; ++k) {
+    const Dim& d = o[n - 1 - k];
+    ext[k] = d.ext;
+    ss[k] = d.ss;
+    ds[k] = d.ds;
+    sc[k] = d.sc;
+  }
+}
+
+bool packed(const uint64_t ext[3], const uint64_t st[3], int nouter, uint64_t inner) {
+  uint64_t want = inner;
+  for (int k = 0; k < nouter; ++k) {
+    if (st[k] != want) return false;
+    want *= ext[k];
+  }
+  return true;
+}
+
+void align_up(std::vector<uint8_t>& img, size_t a) {
+  img.resize((img.size() + a - 1) / a * a, 0);
+}
+
+}  // namespace
+
+rs_status shard_box(const rs_tensor_desc* d, int64_t slot, int64_t* off, int64_t* len,
+                    std::string& err) {
+  Errors E;
+  Layout L;
+  if (!parse_layout(d, "desc", 0, d && d->quant != RS_Q_NONE, L, E)) {
+    err = E.text.str();
+    return E.status() == RS_OK ? RS_ERR_INVALID : E.status();
+  }
+  if (slot < 0 || slot >= L.nslots || !off || !len) {
+    err = "slot out of range or NULL output\n";
+    return RS_ERR_INVALID;
+  }
+  const Interval* b = L.slot_box(slot);
+  for (int i = 0; i < L.ndim; ++i) {
+    off[i] = b[i].start;
+    len[i] = b[i].len;
+  }
+  return RS_OK;
+}
+
+rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32_t n,
+                     const rs_plan_opts* popts, PlanData& out, std::string& err) {
+  const auto t0 = std::chrono::steady_clock::now();
+  Errors E;
+  Opts o;
+  if (n < 0) E.add(&E.invalid, "n_tensors = ", n, " < 0");
+  if (n > 0 && (!src || !dst)) E.add(&E.invalid, "src or dst description array is NULL");
+  if (popts) {
+    if (popts->struct_size != sizeof(rs_plan_opts))
+      E.add(&E.invalid, "opts.struct_size = ", popts->struct_size, ", expected ",
+            sizeof(rs_plan_opts));
+    const uint64_t u = popts->unit_bytes ? popts->unit_bytes : o.unit;
+    if (u < 4096 || u > (1u << 24) || (u & (u - 1)))
+      E.add(&E.invalid, "opts.unit_bytes = ", u, " is not a power of two in [4096, 2^24]");
+    for (int i = 0; i < 4; ++i)
+      if (popts->reserved[i]) E.add(&E.invalid, "opts.reserved[", i, "] must be 0");
+    o.fanout = popts->fanout != 0;
+    o.unit = u;
+    o.tiny = popts->tiny_bytes;
+    o.thin = popts->thin_bytes ? popts->thin_bytes : o.thin;
+  }
+  if (E.status() != RS_OK) {
+    err = E.text.str();
+    return E.status();
+  }
+
+  std::vector<Layout> S(n), D(n);
+  uint64_t n_src_ptrs = 0, n_dst_ptrs = 0;
+  std::vector<uint64_t> src_base(n), dst_base(n), sc_base(n);
+  for (int t = 0; t < n; ++t) {
+    const bool okS = parse_layout(&src[t], "src", t, false, S[t], E);
+    const bool okD = parse_layout(&dst[t], "dst", t, true, D[t], E);
+    if (!okS || !okD) continue;
+    if (S[t].ndim != D[t].ndim) {
+      E.add(&E.mismatch, "tensor ", t, ": src ndim ", S[t].ndim, " != dst ndim ", D[t].ndim);
+      continue;
+    }
+    for (int i = 0; i < S[t].ndim; ++i)
+      if (S[t].shape[i] != D[t].shape[i])
+        E.add(&E.mismatch, "tensor ", t, ": global_shape[", i, "] src ", S[t].shape[i], " != dst ",
+              D[t].shape[i]);
+    if (D[t].quant == RS_Q_MXFP8_E4M3) {
+      if (S[t].dtype != RS_BF16)
+        E.add(&E.mismatch, "tensor ", t, ": MXFP8 install needs a bf16 source (dtype ",
+              S[t].dtype, ")");
+      if (D[t].dtype != RS_U8)
+        E.add(&E.mismatch, "tensor ", t, ": MXFP8 destination dtype must be RS_U8 (dtype ",
+              D[t].dtype, ")");
+    } else if (S[t].dtype != D[t].dtype) {
+      E.add(&E.mismatch, "tensor ", t, ": src dtype ", S[t].dtype, " != dst dtype ", D[t].dtype);
+    }
+  }
+  for (int t = 0; t < n; ++t) {
+    src_base[t] = n_src_ptrs;
+    n_src_ptrs += S[t].nslots;
+    dst_base[t] = n_dst_ptrs;
+    n_dst_ptrs += D[t].nslots;
+    sc_base[t] = n_dst_ptrs;
+    if (D[t].quant == RS_Q_MXFP8_E4M3) n_dst_ptrs += D[t].nslots;
+  }
+  if (E.status() != RS_OK) {
+    err = E.text.str();
+    return E.status();
+  }
+
+  out.src_used.assign(n_src_ptrs, 0);
+  out.dst_used.assign(n_dst_ptrs, 0);
+  out.src_align.assign(n_src_ptrs, 1);
+  out.src_span.assign(n_src_ptrs, 0);
+  out.dst_span.assign(n_dst_ptrs, 0);
+
+  // ---- steps 2 and 3: overlap boxes -> byte regions -------------------------
+  std::vector<Raw> raws;
+  for (int t = 0; t < n; ++t) {
+    const Layout& A = S[t];
+    const Layout& B = D[t];
+    const int nd = A.ndim;
+    const bool mx = B.quant == RS_Q_MXFP8_E4M3;
+    std::vector<Piece> pieces[RS_MAX_DIMS];
+    bool empty = false;
+    for (int dd = 0; dd < nd; ++dd) {
+      pieces[dd] = sweep(A.iv[dd], B.iv[dd]);
+      empty |= pieces[dd].empty();
+    }
+    if (empty) continue;
+    if (mx) {
+      for (int64_t s = 0; s < A.nslots; ++s) out.src_align[src_base[t] + s] = 2;
+    }
+    size_t odo[RS_MAX_DIMS] = {};
+    while (true) {
+      int64_t si[RS_MAX_DIMS], di[RS_MAX_DIMS], start[RS_MAX_DIMS], len[RS_MAX_DIMS];
+      for (int dd = 0; dd < nd; ++dd) {
+        const Piece& p = pieces[dd][odo[dd]];
+        si[dd] = p.si;
+        di[dd] = p.di;
+        start[dd] = p.start;
+        len[dd] = p.len;
+      }
+      const int64_t cls = class_ordinal(B, di);
+      // Destination slots of this class, each with its source replica.
+      struct Target {
+        int64_t dslot, sslot;
+      };
+      std::vector<Target> targets;
+      for (int64_t rep = 0; rep < B.nrep; ++rep) {
+        const int64_t dlin = compose_coord(B, di, rep);
+        const int64_t dslot = B.coord_to_slot[dlin];
+        const int64_t choice = (o.fanout ? cls : dlin) % A.nrep;
+        const int64_t slin = compose_coord(A, si, choice);
+        targets.push_back({dslot, A.coord_to_slot[slin]});
+      }
+      // Group destination replicas that read the same source through the same
+      // views; each group becomes one region (one read, n_dst writes).
+      std::vector<bool> done(targets.size(), false);
+      for (size_t a = 0; a < targets.size(); ++a) {
+        if (done[a]) continue;
+        std::vector<size_t> grp{a};
+        done[a] = true;
+        if (o.fanout) {
+          for (size_t b = a + 1; b < targets.size() && grp.size() < size_t(kMaxFan); ++b) {
+            if (done[b] || targets[b].sslot != targets[a].sslot) continue;
+            if (!same_view(B.views[targets[b].dslot], B.views[targets[a].dslot], nd)) continue;
+            if (mx && !same_view(B.scale_views[targets[b].dslot],
+                                 B.scale_views[targets[a].dslot], nd))
+              continue;
+            grp.push_back(b);
+            done[b] = true;
+          }
+        }
+        const int64_t ss = targets[a].sslot, ds0 = targets[a].dslot;
+        const Interval* sb = A.slot_box(ss);
+        const Interval* db = B.slot_box(ds0);
+        const rs_view& sv = A.views[ss];
+        const rs_view& dv = B.views[ds0];
+        Raw r;
+        r.tensor = t;
+        r.mx = mx;
+        r.src_index = uint32_t(src_base[t] + ss);
+        for (size_t g : grp) {
+          r.dst_index.push_back(uint32_t(dst_base[t] + targets[g].dslot));
+          if (mx) r.sc_index.push_back(uint32_t(sc_base[t] + targets[g].dslot));
+        }
+        int64_t so = sv.base, dof = dv.base, sco = 0;
+        for (int dd = 0; dd < nd; ++dd) {
+          so += (start[dd] - sb[dd].start) * sv.strides[dd];
+          dof += (start[dd] - db[dd].start) * dv.strides[dd];
+        }
+        if (!mx) {
+          const uint64_t es = A.esize;
+          r.src_off = uint64_t(so) * es;
+          r.dst_off = uint64_t(dof) * es;
+          r.sc_off = 0;
+          r.sc_inner = 0;
+          // Element size folds into the innermost run; runs grow while both
+          // sides stay contiguous.
+          std::vector<Dim> dims;
+          for (int dd = 0; dd < nd; ++dd)
+            dims.push_back({uint64_t(len[dd]), uint64_t(sv.strides[dd]) * es,
+                            uint64_t(dv.strides[dd]) * es, 0});
+          std::vector<Dim> keep;
+          for (const Dim& x : dims)
+            if (x.ext != 1) keep.push_back(x);
+          uint64_t run = es;
+          while (!keep.empty() && keep.back().ss == run && keep.back().ds == run) {
+            run *= keep.back().ext;
+            keep.pop_back();
+          }
+          r.inner = run;
+          r.outer = keep;
+          merge_outer(r.outer, false);
+        } else {
+          const rs_view& cv = B.scale_views[ds0];
+          const int last = nd - 1;
+          const int64_t c0 = start[last] - db[last].start;
+          const int64_t kloc = db[last].len;
+          const int64_t c1 = c0 + len[last];
+          if (c0 % kMxBlock != 0 || (c1 % kMxBlock != 0 && c1 != kloc)) {
+            E.add(&E.unsupported, "tensor ", t, ": an MXFP8 block of destination slot ", ds0,
+                  " would span two source shards (columns ", c0, "..", c1,
+                  " of its last dim); block-aligned source splits are required");
+          }
+          if ((sv.strides[last] != 1 && len[last] > 1) || (dv.strides[last] != 1 && len[last] > 1))
+            E.add(&E.unsupported, "tensor ", t,
+                  ": MXFP8 install needs a contiguous last dim on both sides");
+          for (int dd = 0; dd < last; ++dd)
+            sco += (start[dd] - db[dd].start) * cv.strides[dd];
+          sco += cv.base + (c0 / kMxBlock) * cv.strides[last];
+          r.src_off = uint64_t(so) * 2;
+          r.dst_off = uint64_t(dof);
+          r.sc_off = uint64_t(sco);
+          r.inner = uint64_t(len[last]);
+          r.sc_inner = uint64_t(cv.strides[last]);
+          for (int dd = 0; dd < last; ++dd)
+            r.outer.push_back({uint64_t(len[dd]), uint64_t(sv.strides[dd]) * 2,
+                               uint64_t(dv.strides[dd]), uint64_t(cv.strides[dd])});
+          merge_outer(r.outer, true);
+        }
+        raws.push_back(std::move(r));
+      }
+      int dd = nd - 1;
+      while (dd >= 0 && ++odo[dd] == pieces[dd].size()) odo[dd--] = 0;
+      if (dd < 0) break;
+    }
+  }
+  if (E.status() != RS_OK) {
+    err = E.text.str();
+    return E.status();
+  }
+
+  // ---- step 4: split, bucket, size work units ------------------------------
+  std::vector<Raw> split;
+  for (Raw& r : raws) finalize(std::move(r), o, split);
+  raws.clear();
+
+  std::vector<Final> fin;
+  fin.reserve(split.size());
+  uint64_t bytes_read = 0, bytes_written = 0, bytes_nofan = 0;
+  for (Raw& r : split) {
+    Final f;
+    f.rows = rows_of(r.outer);
+    const int nouter = int(r.outer.size());
+    uint64_t ext[3], ss[3], ds[3], sc[3];
+    outer_fields(r.outer, ext, ss, ds, sc);
+    f.flags = uint32_t(nouter);
+    const uint64_t nd = r.dst_index.size();
+    if (r.mx) {
+      f.bucket = kMx;
+      const uint64_t row_bytes = r.inner * 2;
+      const uint64_t rpu = std::max<uint64_t>(1, o.unit / row_bytes);
+      f.rows_per_unit = uint32_t(std::min<uint64_t>(rpu, f.rows));
+      const uint64_t nb = (r.inner + kMxBlock - 1) / kMxBlock;
+      bytes_read += f.rows * row_bytes;
+      bytes_written += nd * f.rows * (r.inner + nb);
+      bytes_nofan += nd * f.rows * row_bytes;
+    } else {
+      const uint64_t total = f.rows * r.inner;
+      if (packed(ext, ss, nouter, r.inner)) f.flags |= kFlagSrcPacked;
+      if (packed(ext, ds, nouter, r.inner)) f.flags |= kFlagDstPacked;
+      uint64_t rpu;
+      if (total <= o.tiny) {
+        f.bucket = kTiny;
+        rpu = f.rows;
+      } else if (r.inner < o.thin) {
+        f.bucket = kThin;
+        rpu = std::max<uint64_t>(1, kThinTile / r.inner);
+      } else {
+        f.bucket = kBulk;
+        rpu = std::max<uint64_t>(1, o.unit / r.inner);
+      }
+      f.rows_per_unit = uint32_t(std::min<uint64_t>(rpu, f.rows));
+      bytes_read += total;
+      bytes_written += nd * total;
+      bytes_nofan += nd * total;
+    }
+    f.units = uint32_t((f.rows + f.rows_per_unit - 1) / f.rows_per_unit);
+    // Bookkeeping for execute-time checks.
+    {
+      uint64_t span_s = r.src_off, span_d = r.dst_off, span_c = r.sc_off;
+      const uint64_t ib = r.mx ? r.inner * 2 : r.inner;
+      const uint64_t ob = r.mx ? r.inner : r.inner;
+      for (int k = 0; k < 3; ++k) {
+        span_s += (ext[k] - 1) * ss[k];
+        span_d += (ext[k] - 1) * ds[k];
+        span_c += (ext[k] - 1) * sc[k];
+      }
+      span_s += ib;
+      span_d += ob;
+      span_c += r.mx ? ((r.inner + kMxBlock - 1) / kMxBlock - 1) * r.sc_inner + 1 : 0;
+      out.src_used[r.src_index] = 1;
+      out.src_span[r.src_index] = std::max(out.src_span[r.src_index], span_s);
+      for (uint32_t di : r.dst_index) {
+        out.dst_used[di] = 1;
+        out.dst_span[di] = std::max(out.dst_span[di], span_d);
+      }
+      for (uint32_t ci : r.sc_index) {
+        out.dst_used[ci] = 1;
+        out.dst_span[ci] = std::max(out.dst_span[ci], span_c);
+      }
+    }
+    f.raw = std::move(r);
+    fin.push_back(std::move(f));
+  }
+
+  // ---- device image: per bucket, launch groups bounded by the pointer pool --
+  out.image.clear();
+  out.launches.clear();
+  out.regions.clear();
+  uint64_t nreg_bucket[kBuckets] = {}, nunit_bucket[kBuckets] = {};
+  for (uint32_t bucket = 0; bucket < kBuckets; ++bucket) {
+    std::vector<const Final*> list;
+    for (const Final& f : fin)
+      if (f.bucket == bucket) list.push_back(&f);
+    size_t i = 0;
+    while (i < list.size()) {
+      // Greedy group: regions in order while their pointers fit the pool.
+      std::map<uint32_t, uint16_t> pool;
+      std::vector<const Final*> grp;
+      uint64_t units = 0;
+      while (i < list.size()) {
+        const Final* f = list[i];
+        std::vector<uint32_t> need{f->raw.src_index};
+        for (uint32_t di : f->raw.dst_index) need.push_back(di | kDstBit);
+        for (uint32_t ci : f->raw.sc_index) need.push_back(ci | kDstBit);
+        size_t add = 0;
+        for (uint32_t k : need) add += pool.count(k) ? 0 : 1;
+        if (!grp.empty() && (pool.size() + add > size_t(kPool) ||
+                             units + f->units > kMaxUnitsPerLaunch))
+          break;
+        for (uint32_t k : need)
+          if (!pool.count(k)) {
+            const uint16_t idx = uint16_t(pool.size());
+            pool[k] = idx;
+          }
+        grp.push_back(f);
+        units += f->units;
+        ++i;
+      }
+      Launch L;
+      L.bucket = bucket;
+      L.n_regions = uint32_t(grp.size());
+      L.pool.resize(pool.size());
+      for (auto& kv : pool) L.pool[kv.second] = kv.first;
+      align_up(out.image, 256);
+      L.regions_off = out.image.size();
+      const size_t rsz = bucket == kMx ? sizeof(MxRegion) : sizeof(CopyRegion);
+      out.image.resize(out.image.size() + rsz * grp.size(), 0);
+      uint32_t ub = 0;
+      std::vector<uint32_t> unit_region;
+      for (size_t k = 0; k < grp.size(); ++k) {
+        const Final& f = *grp[k];
+        const Raw& r = f.raw;
+        uint64_t ext[3], ss[3], ds[3], sc[3];
+        outer_fields(r.outer, ext, ss, ds, sc);
+        uint8_t* dstp = out.image.data() + L.regions_off + rsz * k;
+        if (bucket == kMx) {
+          MxRegion m;
+          std::memset(&m, 0, sizeof(m));
+          m.src_off = r.src_off;
+          m.dst_off = r.dst_off;
+          m.sc_off = r.sc_off;
+          for (int q = 0; q < 3; ++q) {
+            m.sstr[q] = ss[q];
+            m.dstr[q] = ds[q];
+            m.scstr[q] = sc[q];
+          }
+          m.e0 = uint32_t(ext[0]);
+          m.e1 = uint32_t(ext[1]);
+          m.rows = uint32_t(f.rows);
+          m.inner = uint32_t(r.inner);
+          m.rows_per_unit = f.rows_per_unit;
+          m.unit_begin = ub;
+          m.flags = f.flags;
+          m.sc_inner = uint32_t(r.sc_inner);
+          m.src_ptr = pool[r.src_index];
+          m.n_dst = uint16_t(r.dst_index.size());
+          for (size_t j = 0; j < r.dst_index.size(); ++j) {
+            m.dst_ptr[j] = pool[r.dst_index[j] | kDstBit];
+            m.sc_ptr[j] = pool[r.sc_index[j] | kDstBit];
+          }
+          std::memcpy(dstp, &m, sizeof(m));
+        } else {
+          CopyRegion c;
+          std::memset(&c, 0, sizeof(c));
+          c.src_off = r.src_off;
+          c.dst_off = r.dst_off;
+          uint64_t al = r.src_off | r.dst_off | r.inner;
+          for (int q = 0; q < 3; ++q) {
+            c.sstr[q] = ss[q];
+            c.dstr[q] = ds[q];
+            if (ext[q] > 1) al |= ss[q] | ds[q];
+          }
+          c.e0 = uint32_t(ext[0]);
+          c.e1 = uint32_t(ext[1]);
+          c.rows = uint32_t(f.rows);
+          c.inner = uint32_t(r.inner);
+          c.rows_per_unit = f.rows_per_unit;
+          c.unit_begin = ub;
+          c.flags = f.flags | (uint32_t(al & 15) << 8);
+          c.src_ptr = pool[r.src_index];
+          c.n_dst = uint16_t(r.dst_index.size());
+          for (size_t j = 0; j < r.dst_index.size(); ++j) c.dst_ptr[j] = pool[r.dst_index[j] | kDstBit];
+          std::memcpy(dstp, &c, sizeof(c));
+        }
+        if (bucket != kTiny)
+          for (uint32_t u = 0; u < f.units; ++u) unit_region.push_back(uint32_t(k));
+        ub += f.units;
+
+        rs_region pub;
+        std::memset(&pub, 0, sizeof(pub));
+        pub.tensor = r.tensor;
+        pub.bucket = bucket;
+        pub.src_index = r.src_index;
+        pub.n_dst = uint32_t(r.dst_index.size());
+        for (size_t j = 0; j < r.dst_index.size(); ++j) {
+          pub.dst_index[j] = r.dst_index[j];
+          if (r.mx) pub.scale_index[j] = r.sc_index[j];
+        }
+        pub.src_off = r.src_off;
+        pub.dst_off = r.dst_off;
+        pub.scale_off = r.sc_off;
+        pub.inner = r.inner;
+        for (int q = 0; q < 3; ++q) {
+          pub.ext[q] = ext[q];
+          pub.src_stride[q] = ss[q];
+          pub.dst_stride[q] = ds[q];
+          pub.scale_stride[q] = sc[q];
+        }
+        pub.scale_inner_stride = r.sc_inner;
+        out.regions.push_back(pub);
+      }
+      if (bucket == kTiny) {
+        L.n_units = uint32_t((grp.size() + kThreads - 1) / kThreads);
+        L.units_off = 0;
+      } else {
+        L.n_units = ub;
+        align_up(out.image, 256);
+        L.units_off = out.image.size();
+        out.image.resize(out.image.size() + 4 * unit_region.size());
+        std::memcpy(out.image.data() + L.units_off, unit_region.data(), 4 * unit_region.size());
+      }
+      nreg_bucket[bucket] += grp.size();
+      nunit_bucket[bucket] += L.n_units;
+      out.launches.push_back(std::move(L));
+    }
+  }
+  align_up(out.image, 256);
+
+  rs_plan_info& I = out.info;
+  std::memset(&I, 0, sizeof(I));
+  I.n_tensors = uint64_t(n);
+  I.n_src_ptrs = n_src_ptrs;
+  I.n_dst_ptrs = n_dst_ptrs;
+  I.n_regions = out.regions.size();
+  for (int b = 0; b < kBuckets; ++b) {
+    I.n_regions_bucket[b] = nreg_bucket[b];
+    I.n_units_bucket[b] = nunit_bucket[b];
+  }
+  I.n_launches = out.launches.size();
+  I.bytes_read = bytes_read;
+  I.bytes_written = bytes_written;
+  I.bytes_read_no_fanout = bytes_nofan;
+  I.plan_ns = uint64_t(std::chrono::duration_cast<std::chrono::nanoseconds>(
+                           std::chrono::steady_clock::now() - t0)
+                           .count());
+  return RS_OK;
+}
+
+}  // namespace rs

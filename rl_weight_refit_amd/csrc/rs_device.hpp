@@ -1,0 +1,80 @@
+// Device-side region tables shared by the planner (which fills them) and the
+// HIP kernels (which walk them).  Plain data; no HIP types, so the planner
+// compiles as ordinary C++.
+#pragma once
+
+#include <stdint.h>
+
+namespace rs {
+
+constexpr int kThreads = 256;         // threads per workgroup (4 wave64s)
+constexpr int kPool = 240;            // device pointers passed per launch (kernel arguments)
+constexpr int kMaxFan = 16;           // destination replicas per region
+constexpr uint32_t kThinTile = 16384; // LDS tile of the thin bucket, bytes
+constexpr uint32_t kLongRow = 2048;   // bulk rows at least this long are walked row by row
+
+enum Bucket : uint32_t { kBulk = 0, kThin = 1, kTiny = 2, kMx = 3, kBuckets = 4 };
+
+// Region flags.
+enum : uint32_t {
+  kFlagOuterMask = 3u,      // number of outer dims (0..3)
+  kFlagSrcPacked = 1u << 2, // consecutive rows are contiguous on the source side
+  kFlagDstPacked = 1u << 3, // ... on the destination side
+};
+
+// A copy region: rows x inner bytes.  Row r = i0 + e0*(i1 + e1*i2) starts at
+// src_off + i0*sstr[0] + i1*sstr[1] + i2*sstr[2] (same on the destination
+// side with dstr), relative to the region's buffer pointers.
+struct alignas(16) CopyRegion {
+  uint64_t src_off;
+  uint64_t dst_off;
+  uint64_t sstr[3];
+  uint64_t dstr[3];
+  uint32_t e0, e1;
+  uint32_t rows;
+  uint32_t inner;
+  uint32_t rows_per_unit;
+  uint32_t unit_begin;      // first work unit of this region in its launch
+  uint32_t flags;           // bits 0-7: kFlag*; bits 8-11: low bits of the OR of
+                            // offsets, strides and inner (they bound the vector width)
+  uint16_t src_ptr;         // index into the launch's pointer pool
+  uint16_t n_dst;
+  uint16_t dst_ptr[kMaxFan];
+};
+static_assert(sizeof(CopyRegion) == 128, "CopyRegion must stay 128 bytes");
+
+// An MXFP8 install region: rows x inner bf16 elements (inner along the
+// destination's last dim, starting on a 32-element block boundary).  Element
+// bytes go to dst, block scales to scale (one byte per block,
+// sc_inner bytes apart).
+struct alignas(16) MxRegion {
+  uint64_t src_off;
+  uint64_t dst_off;
+  uint64_t sc_off;
+  uint64_t sstr[3];
+  uint64_t dstr[3];
+  uint64_t scstr[3];
+  uint32_t e0, e1;
+  uint32_t rows;
+  uint32_t inner;           // elements
+  uint32_t rows_per_unit;
+  uint32_t unit_begin;
+  uint32_t flags;
+  uint32_t sc_inner;
+  uint16_t src_ptr;
+  uint16_t n_dst;
+  uint16_t dst_ptr[kMaxFan];
+  uint16_t sc_ptr[kMaxFan];
+};
+static_assert(sizeof(MxRegion) == 208, "MxRegion must stay 208 bytes");
+
+// Kernel arguments of one launch.
+struct LaunchArgs {
+  const void* regions;          // CopyRegion[] or MxRegion[]
+  const uint32_t* unit_region;  // work unit -> region index (bulk, thin, mx)
+  uint32_t n_regions;
+  uint32_t n_units;
+  void* ptr[kPool];
+};
+
+}  // namespace rs

@@ -240,10 +240,11 @@ def moe_dsv3(quant=None):
 # ---------------------------------------------------------------------------
 
 def f32_to_bf16_bits(x):
-    """Round-to-nearest-even bf16 bit patterns of finite float32 values."""
-    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
-    return b.astype(np.uint16)
+    """Round-to-nearest-even bf16 bit patterns of finite float32 values
+    (torch's CPU conversion, which rounds to nearest even)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
 def host_values(tensor):
@@ -261,7 +262,8 @@ def host_values(tensor):
     if v["kind"] == "uniform":
         x = rng.uniform(-1.0, 1.0, size=shape).astype(np.float32)
     elif v["kind"] == "normal":
-        x = (rng.standard_normal(size=shape, dtype=np.float32) * np.float32(v["std"]))
+        x = rng.standard_normal(size=shape, dtype=np.float32)
+        x *= np.float32(v["std"])
     else:
         raise ValueError(v["kind"])
     if dt == "f32":

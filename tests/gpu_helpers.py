@@ -1,0 +1,114 @@
+"""GPU-side test glue: device buffers for a workload, one HIP-path run through
+the C ABI, and comparisons with the oracle.
+
+Destinations are filled with a poison byte and followed by a guard area of
+the same poison, so stray writes past a buffer or outside a view show up.
+Pointers can be offset by a few bytes from the allocation to exercise the
+kernels' misaligned paths.
+"""
+
+import sys
+
+import numpy as np
+import torch
+
+from oracle import golden as ogolden
+from oracle import layout as olayout
+from rl_weight_refit_amd import binding
+
+import helpers
+import lib_helpers as lh
+
+GUARD = 4096
+
+
+def log(msg):
+    sys.stdout.write(msg + "\n")
+    sys.stdout.flush()
+
+
+class DevBuf:
+    """A device byte buffer with a leading misalignment and a trailing guard."""
+
+    def __init__(self, nbytes, fill=None, data=None, shift=0, guard=GUARD, poison=0xA5):
+        self.nbytes = int(nbytes)
+        self.shift = int(shift)
+        total = self.shift + self.nbytes + guard
+        self.t = torch.full((max(total, 1),), poison, dtype=torch.uint8, device="cuda")
+        if data is not None:
+            self.t[self.shift:self.shift + self.nbytes].copy_(torch.from_numpy(np.ascontiguousarray(data)))
+        self.poison = poison
+        self.guard = guard
+
+    @property
+    def ptr(self):
+        return self.t.data_ptr() + self.shift
+
+    def body(self):
+        return self.t[self.shift:self.shift + self.nbytes]
+
+    def host(self):
+        return self.body().cpu().numpy()
+
+    def guard_ok(self):
+        g = self.t[self.shift + self.nbytes:self.shift + self.nbytes + self.guard]
+        head = self.t[:self.shift]
+        return bool((g == self.poison).all()) and bool((head == self.poison).all())
+
+
+def device_run(workload, sources, per_tensor_dst_host, poison=0xA5, src_shift=0, dst_shift=0,
+               plan=None, stream=None, **plan_kw):
+    """Upload sources, allocate poisoned destinations shaped like the host
+    images, execute the HIP path, return the device buffers in pointer order.
+    """
+    src_dev = []
+    for t_src in sources:
+        src_dev.append([DevBuf(e["buf"].size, data=e["buf"], shift=src_shift) for e in t_src])
+    # Shared (fused) buffers are the same numpy object in the host images.
+    seen = {}
+    dst_ptrs = []
+    dst_dev_flat = []
+    for t, slots in zip(workload["tensors"], per_tensor_dst_host):
+        for key in ("buf", "scale_buf"):
+            if key == "scale_buf" and t["dst"].get("quant") != "mxfp8":
+                continue
+            for e in slots:
+                hb = e[key]
+                if id(hb) not in seen:
+                    seen[id(hb)] = DevBuf(hb.size, shift=dst_shift, poison=poison)
+                dst_ptrs.append(seen[id(hb)].ptr)
+                dst_dev_flat.append((hb, seen[id(hb)]))
+    src_ptrs = [b.ptr for ts in src_dev for b in ts]
+    if plan is None:
+        plan = lh.plan_workload(workload, **plan_kw)
+    s = stream if stream is not None else torch.cuda.current_stream()
+    binding.reshard_execute(plan, src_ptrs, dst_ptrs, s.cuda_stream)
+    torch.cuda.synchronize()
+    return plan, src_dev, dst_dev_flat
+
+
+def check_against_oracle(workload, poison=0xA5, src_shift=0, dst_shift=0, globals_=None,
+                         **plan_kw):
+    """Full byte-for-byte comparison of every destination buffer with the
+    oracle's golden image (poison outside the views included), guards intact,
+    sources unchanged."""
+    G, sources, named, per = helpers.golden_workload(workload, poison=poison, globals_=globals_)
+    # Fresh poisoned host images shaped like the oracle's, for allocation only.
+    plan, src_dev, dst_dev = device_run(workload, sources, per, poison=poison,
+                                        src_shift=src_shift, dst_shift=dst_shift, **plan_kw)
+    checked = set()
+    for host_img, dev in dst_dev:
+        if id(dev) in checked:
+            continue
+        checked.add(id(dev))
+        got = dev.host()
+        if not np.array_equal(got, host_img):
+            bad = np.nonzero(got != host_img)[0]
+            raise AssertionError("%s: %d bytes differ, first at %d (got %#x want %#x)"
+                                 % (workload["name"], bad.size, bad[0], got[bad[0]],
+                                    host_img[bad[0]]))
+        assert dev.guard_ok(), "%s: guard bytes overwritten" % workload["name"]
+    for t_src, t_dev in zip(sources, src_dev):
+        for e, d in zip(t_src, t_dev):
+            assert np.array_equal(d.host(), e["buf"]), "source modified"
+    return plan

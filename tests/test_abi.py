@@ -1,0 +1,73 @@
+"""The C-ABI library loads, exports every function include/reshard.h declares,
+and its structs have the layout the Python binding marshals (checked by
+compiling the header with gcc).  No GPU needed."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from rl_weight_refit_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "reshard.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:rs_status|void|const char\*)\s+(reshard_\w+)\s*\(",
+                                 text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("reshard_plan", "reshard_execute", "reshard_plan_destroy", "reshard_last_error",
+              "reshard_plan_info", "reshard_plan_region", "reshard_shard_box"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = binding.load()
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing
+
+
+STRUCTS = {
+    "rs_view": (binding.View, ["base", "strides"]),
+    "rs_tensor_desc": (binding.TensorDesc, ["ndim", "dtype", "global_shape", "mesh_ndim",
+                                            "placements", "mesh_shape", "slot_of_coord", "views",
+                                            "quant", "scale_views"]),
+    "rs_plan_opts": (binding.PlanOpts, ["struct_size", "fanout", "unit_bytes", "tiny_bytes",
+                                        "thin_bytes", "reserved"]),
+    "rs_plan_info": (binding.PlanInfo, [f[0] for f in binding.PlanInfo._fields_]),
+    "rs_region": (binding.Region, [f[0] for f in binding.Region._fields_]),
+}
+
+
+def test_struct_layouts_match_header(tmp_path):
+    src = ['#include <stdio.h>', '#include <stddef.h>', '#include "reshard.h"', 'int main(void){']
+    for s, (_, fields) in STRUCTS.items():
+        src.append('printf("%s size %%zu\\n", sizeof(%s));' % (s, s))
+        for f in fields:
+            src.append('printf("%s.%s %%zu\\n", offsetof(%s, %s));' % (s, f, s, f))
+    src.append("return 0;}")
+    c = tmp_path / "layout.c"
+    c.write_text("\n".join(src))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(c), "-o", str(exe)],
+                   check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    got = dict(l.rsplit(" ", 1) for l in out if l)
+    for s, (cls, fields) in STRUCTS.items():
+        assert int(got["%s size" % s]) == ctypes.sizeof(cls), s
+        for f in fields:
+            assert int(got["%s.%s" % (s, f)]) == getattr(cls, f).offset, (s, f)
+
+
+def test_last_error_is_empty_after_success():
+    plan = binding.reshard_plan([{"shape": [4], "dtype": "u8", "mesh": [1], "placements": [-1]}],
+                                [{"shape": [4], "dtype": "u8", "mesh": [2], "placements": [0]}])
+    plan.info()
+    assert binding.reshard_last_error() == ""

@@ -1,0 +1,150 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle,
+byte for byte, on every workload family at sizes the oracle finishes in
+seconds: the pages' worked example, 200 tiny random layouts, the 500 uneven
+layouts with their A -> B -> A round trips, fused dense and MoE layers
+(ragged variants included), the MXFP8 install, misaligned pointers and every
+kernel bucket forced on its own.  Destinations start poisoned, with guard
+bytes after each buffer; sources must come back unchanged.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from rl_weight_refit_amd import binding, synth
+
+import gpu_helpers as gh
+import helpers
+import lib_helpers as lh
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _cuda():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.load()
+    yield
+
+
+def test_worked_example():
+    gh.log("worked 8x8")
+    gh.check_against_oracle(synth.worked_example())
+
+
+@pytest.mark.parametrize("seed", range(200))
+def test_tiny_layouts(seed):
+    gh.check_against_oracle(synth.tiny_case(seed))
+
+
+@pytest.mark.parametrize("seed", range(0, 200, 3))
+@pytest.mark.parametrize("dtype", ["u8", "bf16"])
+def test_tiny_layouts_narrow(seed, dtype):
+    gh.check_against_oracle(synth.tiny_case(seed, dtype=dtype))
+
+
+@pytest.mark.parametrize("seed", range(0, 200, 5))
+@pytest.mark.parametrize("shifts", [(1, 0), (0, 3), (5, 9), (8, 8)])
+def test_tiny_layouts_misaligned_pointers(seed, shifts):
+    gh.check_against_oracle(synth.tiny_case(seed, dtype="u8"), src_shift=shifts[0],
+                            dst_shift=shifts[1])
+
+
+@pytest.mark.parametrize("seed", range(0, 200, 4))
+def test_tiny_layouts_no_fanout(seed):
+    gh.check_against_oracle(synth.tiny_case(seed), fanout=False)
+
+
+def _round_trip(wl):
+    """A -> B on the GPU (checked against the oracle), then B -> A on the GPU
+    from the GPU's own B buffers: A must come back bit for bit."""
+    G, sources, named, per = helpers.golden_workload(wl)
+    plan, src_dev, dst_dev = gh.device_run(wl, sources, per)
+    for host_img, dev in dst_dev:
+        assert np.array_equal(dev.host(), host_img)
+        assert dev.guard_ok()
+    back = synth.reverse(wl)
+    bplan = lh.plan_workload(back)
+    out = [gh.DevBuf(e["buf"].size, poison=0x3C) for e in sources[0]]
+    binding.reshard_execute(bplan, [d.ptr for _, d in dst_dev], [o.ptr for o in out],
+                            torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    for e, o in zip(sources[0], out):
+        assert np.array_equal(o.host(), e["buf"])
+        assert o.guard_ok()
+
+
+@pytest.mark.parametrize("seed", range(500))
+def test_uneven_layouts_round_trip(seed):
+    _round_trip(synth.uneven_case(seed))
+
+
+@pytest.mark.parametrize("kw", [{}, {"unit_bytes": 4096}, {"fanout": False},
+                                {"tiny_bytes": 0, "thin_bytes": 1},
+                                {"tiny_bytes": 0, "thin_bytes": 4096}])
+@pytest.mark.parametrize("seed", range(0, 500, 25))
+def test_uneven_layouts_bucket_variants(seed, kw):
+    gh.check_against_oracle(synth.uneven_case(seed), **kw)
+
+
+@pytest.mark.parametrize("shifts", [(4, 0), (0, 2), (6, 10)])
+@pytest.mark.parametrize("seed", range(0, 500, 50))
+def test_uneven_layouts_misaligned(seed, shifts):
+    gh.check_against_oracle(synth.uneven_case(seed), src_shift=shifts[0], dst_shift=shifts[1])
+
+
+def test_dense_ffn_ragged():
+    gh.check_against_oracle(synth.dense_ffn(hidden=256, inter=1000, src_tp=4, dst_tp=2,
+                                            dst_dp=2))
+
+
+def test_dense_ffn_full_size():
+    """hidden 4096, intermediate 14336: TP4 -> TP2 x DP2 with fused gate/up."""
+    gh.log("dense ffn 4096 x 14336")
+    gh.check_against_oracle(synth.dense_ffn())
+
+
+@pytest.mark.parametrize("kw", [{}, {"fanout": False}, {"unit_bytes": 4096}])
+def test_dense_ffn_plan_variants(kw):
+    gh.check_against_oracle(synth.dense_ffn(hidden=512, inter=1536), **kw)
+
+
+MOE_SMALL = [
+    (16, 512, 192, 8, 4, 4),     # several tiles per region
+    (12, 200, 100, 3, 2, 4),     # ragged: 100 / 4 per TP shard, 200 hidden
+    (32, 256, 64, 16, 8, 8),     # the DSV3 meshes at a small size
+    (6, 96, 40, 3, 2, 3),        # uneven intermediate split
+]
+
+
+@pytest.mark.parametrize("shape", MOE_SMALL)
+def test_moe_experts_small(shape):
+    gh.check_against_oracle(synth.moe_experts(*shape, seed=9))
+
+
+@pytest.mark.parametrize("shape", MOE_SMALL)
+def test_moe_experts_small_mxfp8(shape):
+    gh.check_against_oracle(synth.moe_experts(*shape, seed=9, quant="mxfp8"))
+
+
+def test_mxfp8_extreme_values():
+    """Blocks spanning many binades, zeros, negative zeros, bf16 subnormals,
+    the largest bf16 and NaN/Inf blocks (the NaN/Inf convention is the
+    library's, shared by the oracle; it is not pinned by any page)."""
+    wl = synth.moe_experts(4, 64, 96, 2, 2, 2, seed=3, quant="mxfp8")
+    rng = np.random.default_rng(4)
+    globals_ = []
+    for t in wl["tensors"]:
+        shape = t["shape"]
+        scale = np.exp2(rng.integers(-140, 120, size=shape[:-1] + [1])).astype(np.float64)
+        x = np.clip(rng.standard_normal(shape) * scale, -3e38, 3e38).astype(np.float32)
+        b = (x.view(np.uint32) >> 16).astype(np.uint16)
+        b[rng.random(shape) < 0.05] = 0x8000
+        b[rng.random(shape) < 0.05] = 0x0000
+        b[rng.random(shape) < 0.03] = rng.integers(1, 0x80, size=1)[0]
+        b[rng.random(shape) < 0.001] = 0x7F7F
+        b[rng.random(shape) < 0.001] = 0x7FC0
+        b[rng.random(shape) < 0.001] = 0xFF80
+        globals_.append(b)
+    gh.check_against_oracle(wl, globals_=globals_)

@@ -1,0 +1,221 @@
+"""Planner tests on the CPU (no GPU): the library's layout resolution, region
+tables and argument checks, compared with the oracle.
+
+The plan's region table is executed here by a test-only host interpreter
+(tests/lib_helpers.py) and the resulting destination images are compared
+byte for byte with the oracle's golden images, together with a per-byte write
+count (every destination byte inside a view is written exactly once, nothing
+outside is touched).
+"""
+
+import numpy as np
+import pytest
+
+from oracle import layout as olayout
+from rl_weight_refit_amd import binding, synth
+
+import helpers
+import lib_helpers as lh
+
+
+def test_library_loads():
+    binding.load()
+
+
+@pytest.mark.parametrize("seed", range(200))
+def test_shard_box_matches_oracle_tiny(seed):
+    t = synth.tiny_case(seed)["tensors"][0]
+    for side in ("src", "dst"):
+        sp = lh.spec(t, side)
+        od = helpers.src_desc_for(t) if side == "src" else helpers.odesc(t, side)
+        want = olayout.slot_boxes(od)
+        got = [tuple(binding.reshard_shard_box(sp, k)) for k in range(len(want))]
+        assert [tuple(map(list, w)) for w in want] == [tuple(map(list, g)) for g in got]
+
+
+@pytest.mark.parametrize("seed", range(0, 500, 7))
+def test_shard_box_matches_oracle_uneven(seed):
+    t = synth.uneven_case(seed)["tensors"][0]
+    for side in ("src", "dst"):
+        sp = lh.spec(t, side)
+        want = olayout.slot_boxes(helpers.odesc(t, side))
+        got = [binding.reshard_shard_box(sp, k) for k in range(len(want))]
+        assert [list(map(list, w)) for w in want] == [list(g) for g in got]
+
+
+def test_worked_example_regions():
+    """Eight 4x2 int32 regions: destination k takes rows 0-3 from source 0 and
+    rows 4-7 from source 1 (the pages' 8x8 example)."""
+    wl = synth.worked_example()
+    plan = lh.plan_workload(wl)
+    regs = plan.regions()
+    assert len(regs) == 8
+    seen = set()
+    for r in regs:
+        rows = int(np.prod(r["ext"]))
+        assert rows * r["inner"] == 32            # 4 x 2 int32
+        k = r["dst_index"][0]
+        s = r["src_index"]
+        seen.add((k, s))
+        assert r["dst_off"] == 32 * s             # rows 4s.. of destination k (8 bytes per row)
+        assert r["src_off"] == 8 * k              # columns 2k, 2k+1 of the 4x8 source
+    assert seen == {(k, s) for k in range(4) for s in range(2)}
+
+
+def run_interpreted(wl, **kw):
+    G, sources, named, per = helpers.golden_workload(wl, poison=0xA5)
+    _, per2 = None, None
+    named2, per2 = helpers.alloc_destinations(wl, poison=0xA5)
+    src_flat, dst_flat = lh.flat_lists(wl, sources, per2)
+    count = [np.zeros(b.size, np.int32) for b in dst_flat]
+    plan = lh.plan_workload(wl, **kw)
+    lh.interpret(plan, src_flat, dst_flat, count)
+    gsrc, gdst = lh.flat_lists(wl, sources, per)
+    for j, (a, b) in enumerate(zip(dst_flat, gdst)):
+        np.testing.assert_array_equal(a, b, err_msg="destination pointer %d" % j)
+    return plan, dst_flat, count
+
+
+def assert_exact_once(count):
+    # Shared (fused) buffers appear several times in the flat list; merge by identity.
+    for c in count:
+        assert c.max(initial=0) <= 1
+
+
+def counts_by_buffer(dst_flat, count):
+    merged = {}
+    for b, c in zip(dst_flat, count):
+        k = id(b)
+        merged[k] = merged.get(k, 0) + c
+    return merged
+
+
+@pytest.mark.parametrize("seed", range(200))
+@pytest.mark.parametrize("fanout", [True, False])
+def test_interpreted_plan_matches_golden_tiny(seed, fanout):
+    wl = synth.tiny_case(seed)
+    plan, dst_flat, count = run_interpreted(wl, fanout=fanout)
+    for c in counts_by_buffer(dst_flat, count).values():
+        assert c.max(initial=0) <= 1
+
+
+@pytest.mark.parametrize("seed", range(0, 200, 9))
+@pytest.mark.parametrize("dtype", ["u8", "bf16"])
+def test_interpreted_plan_narrow_dtypes(seed, dtype):
+    run_interpreted(synth.tiny_case(seed, dtype=dtype))
+
+
+@pytest.mark.parametrize("seed", range(0, 500, 11))
+def test_interpreted_plan_uneven_and_back(seed):
+    wl = synth.uneven_case(seed, shapes=[[100, 300], [7, 51, 25]])
+    run_interpreted(wl)
+    run_interpreted(synth.reverse(wl))
+
+
+@pytest.mark.parametrize("kw", [{}, {"unit_bytes": 4096}, {"fanout": False},
+                                {"tiny_bytes": 0, "thin_bytes": 1}])
+def test_interpreted_plan_fused_dense(kw):
+    wl = synth.dense_ffn(hidden=48, inter=200, src_tp=4, dst_tp=2, dst_dp=2)
+    plan, dst_flat, count = run_interpreted(wl, **kw)
+    merged = counts_by_buffer(dst_flat, count)
+    for c in merged.values():
+        assert c.min() == 1 and c.max() == 1     # fused buffers are fully covered, once
+
+
+@pytest.mark.parametrize("quant", [None, "mxfp8"])
+@pytest.mark.parametrize("shape", [(8, 64, 96, 4, 2, 2), (6, 40, 64, 3, 2, 3), (4, 96, 32, 2, 1, 2)])
+def test_interpreted_plan_moe(quant, shape):
+    E, H, I, sep, dep, dtp = shape
+    wl = synth.moe_experts(E, H, I, sep, dep, dtp, seed=7, quant=quant)
+    plan, dst_flat, count = run_interpreted(wl)
+    for c in counts_by_buffer(dst_flat, count).values():
+        assert c.max() <= 1
+
+
+def test_region_counts_at_full_sizes():
+    """Region counts (before fan-out splits) on the layer-sized layouts."""
+    p = lh.plan_workload(synth.dense_ffn())
+    assert p.info()["n_regions"] == 12          # 24 (box, destination) pairs, 2 DP replicas each
+    p = lh.plan_workload(synth.dense_ffn(), fanout=False)
+    assert p.info()["n_regions"] == 24
+    p = lh.plan_workload(synth.moe_128e())
+    assert p.info()["n_regions"] == 96
+    p = lh.plan_workload(synth.moe_dsv3())
+    assert p.info()["n_regions"] == 384
+    p = lh.plan_workload(synth.moe_dsv3(quant="mxfp8"))
+    assert p.info()["n_regions"] == 384
+
+
+def test_algorithmic_bytes():
+    i = lh.plan_workload(synth.dense_ffn()).info()
+    assert (i["bytes_read"], i["bytes_written"]) == (352_321_536, 704_643_072)
+    assert i["bytes_read_no_fanout"] == 704_643_072
+    i = lh.plan_workload(synth.moe_128e()).info()
+    assert (i["bytes_read"], i["bytes_written"]) == (4_831_838_208, 4_831_838_208)
+    i = lh.plan_workload(synth.moe_dsv3()).info()
+    assert (i["bytes_read"], i["bytes_written"]) == (22_548_578_304, 22_548_578_304)
+    i = lh.plan_workload(synth.moe_dsv3(quant="mxfp8")).info()
+    assert i["bytes_read"] == 22_548_578_304
+    assert i["bytes_written"] == 11_274_289_152 + 352_321_536
+
+
+def test_plan_is_deterministic():
+    wl = synth.moe_dsv3()
+    a = lh.plan_workload(wl).regions()
+    b = lh.plan_workload(wl).regions()
+    assert a == b
+
+
+def test_dsv3_regions_are_long_contiguous_runs():
+    regs = lh.plan_workload(synth.moe_dsv3()).regions()
+    for r in regs:
+        assert r["bucket"] == "bulk"
+        if r["tensor"] < 2:   # gate / up: 16 experts x 256 rows x 7168 bf16, contiguous per expert
+            assert r["inner"] == 65536 and r["ext"][:2] == [56, 16]
+        else:                 # down: 114,688 rows of 512 bytes
+            assert r["inner"] == 512 and r["ext"][0] == 114_688
+
+
+def test_every_violation_is_reported():
+    bad_src = {"shape": [4, 4], "dtype": "f32", "mesh": [2, 0], "placements": [5, 0]}
+    bad_dst = {"shape": [4, 5], "dtype": "f32", "mesh": [2], "placements": [0]}
+    with pytest.raises(binding.ReshardError) as e:
+        binding.reshard_plan([bad_src], [bad_dst])
+    msg = str(e.value)
+    assert "mesh_shape[1]" in msg and "placements[0]" in msg
+    src = {"shape": [4, 4], "dtype": "f32", "mesh": [2], "placements": [0]}
+    dst = {"shape": [4, 5], "dtype": "bf16", "mesh": [2], "placements": [0]}
+    with pytest.raises(binding.ReshardError) as e:
+        binding.reshard_plan([src], [dst])
+    assert e.value.status == 2
+    msg = str(e.value)
+    assert "global_shape[1]" in msg and "dtype" in msg
+
+
+def test_mxfp8_block_spanning_sources_is_unsupported():
+    src = {"shape": [4, 100], "dtype": "bf16", "mesh": [2], "placements": [1]}
+    dst = {"shape": [4, 100], "dtype": "u8", "mesh": [1], "placements": [-1], "quant": "mxfp8"}
+    with pytest.raises(binding.ReshardError) as e:
+        binding.reshard_plan([src], [dst])
+    assert e.value.status == 3 and "span" in str(e.value)
+
+
+def test_execute_rejects_null_pointer_before_launch():
+    wl = synth.worked_example()
+    plan = lh.plan_workload(wl)
+    with pytest.raises(binding.ReshardError) as e:
+        binding.reshard_execute(plan, [0x1000, 0], [0x2000, 0x3000, 0x4000, 0x5000])
+    assert e.value.status == 1 and "src_ptrs[1]" in str(e.value)
+
+
+def test_empty_tensor_plans_nothing():
+    src = {"shape": [0, 5], "dtype": "f32", "mesh": [2], "placements": [0]}
+    dst = {"shape": [0, 5], "dtype": "f32", "mesh": [3], "placements": [1]}
+    plan = binding.reshard_plan([src], [dst])
+    assert plan.info()["n_regions"] == 0 and plan.info()["n_launches"] == 0
+    binding.reshard_execute(plan, [0, 0], [0, 0, 0])   # nothing to launch, nothing read
+
+
+def test_plan_time_is_reported():
+    plan = lh.plan_workload(synth.moe_dsv3())
+    assert 0 < plan.info()["plan_ns"] < 1e9
