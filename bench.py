@@ -140,7 +140,7 @@ def copy_ceiling(torch, nbytes, stream):
 
 def cpu_baseline():
     """The oracle (as it stands) on a bounded sample of the same workload: the
-    same layer shape and meshes with 8 experts instead of 256 (1/32 of the
+    same layer shape and meshes with 16 experts instead of 256 (1/16 of the
     bytes), bf16 relayout plus MXFP8 install, on the host."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from oracle import golden as ogolden
@@ -150,7 +150,7 @@ def cpu_baseline():
     total_bytes = 0
     elapsed = 0.0
     for quant in (None, "mxfp8"):
-        wl = synth.moe_experts(8, 7168, 2048, 8, 8, 8, seed=5, quant=quant)
+        wl = synth.moe_experts(16, 7168, 2048, 16, 8, 8, seed=5, quant=quant)
         for t in wl["tensors"]:
             G = synth.host_values(t)
             src = helpers.source_buffers(t, G)
@@ -167,7 +167,7 @@ def cpu_baseline():
             del src, per
     return {"value": round(total_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": "same layer shape with 8 of 256 experts (1/32 of the bytes), EP8 -> EP8xTP8, "
+            "sample": "same layer shape and meshes with 16 of 256 experts (1/16 of the bytes), "
                       "bf16 relayout + MXFP8 install, numpy on the host, %.1f s" % elapsed}
 
 

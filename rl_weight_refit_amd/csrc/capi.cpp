@@ -169,8 +169,8 @@ rs_status reshard_plan_info(const rs_plan* plan, rs_plan_info* info) {
 rs_status reshard_plan_region(const rs_plan* plan, uint64_t index, rs_region* out) {
   g_error.clear();
   if (!plan || !out) return fail(RS_ERR_INVALID, "plan or out is NULL\n");
-  if (index >= plan->d.regions.size()) return fail(RS_ERR_INVALID, "region index out of range\n");
-  *out = plan->d.regions[index];
+  if (rs::region_info(plan->d, index, out) != RS_OK)
+    return fail(RS_ERR_INVALID, "region index out of range\n");
   return RS_OK;
 }
 

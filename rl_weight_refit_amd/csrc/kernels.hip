@@ -49,11 +49,79 @@ __device__ __forceinline__ uint64_t row_off(uint32_t r, uint32_t e0, uint32_t e1
   return uint64_t(i0) * s0 + uint64_t(i1) * s1 + uint64_t(i2) * s2;
 }
 
+// Tuning knobs (compile-time).  Streaming data is touched once, so loads
+// and stores are non-temporal by default.
+#ifndef RS_NT_LOAD
+#define RS_NT_LOAD 1
+#endif
+#ifndef RS_NT_STORE
+#define RS_NT_STORE 1
+#endif
+#ifndef RS_UNROLL
+#define RS_UNROLL 4   // 16-byte vectors in flight per lane in the bulk kernel
+#endif
+#ifndef RS_PIPE
+#define RS_PIPE 0     // 1: software-pipeline the long-row copy loop
+#endif
+#ifndef RS_BULK_MIN_WAVES
+#define RS_BULK_MIN_WAVES 1  // occupancy floor (waves per SIMD) for the bulk kernel
+#endif
+
 __device__ __forceinline__ u32x4 ld16(const void* p) {
+#if RS_NT_LOAD
   return __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+#else
+  return *static_cast<const u32x4*>(p);
+#endif
 }
 __device__ __forceinline__ void st16(void* p, u32x4 v) {
+#if RS_NT_STORE
   __builtin_nontemporal_store(v, static_cast<u32x4*>(p));
+#else
+  *static_cast<u32x4*>(p) = v;
+#endif
+}
+
+#ifndef RS_XCD_MAP
+#define RS_XCD_MAP 1     // bulk kernel: 1 = map workgroups so each XCD walks its own units
+#endif
+#ifndef RS_XCD_CHUNK
+#define RS_XCD_CHUNK 0   // units per XCD turn (0: one contiguous eighth per XCD)
+#endif
+#ifndef RS_MX_XCD_MAP
+#define RS_MX_XCD_MAP 0  // MXFP8 kernel: same choice
+#endif
+
+// Work unit of workgroup b out of n.  Workgroups are dispatched round-robin
+// over the 8 XCDs (b -> XCD b % 8), each with its own L2.  Remapped, XCD x
+// takes runs of `chunk` consecutive units in turn (or, with chunk 0, one
+// contiguous eighth of all units), so neighbouring units stay on one XCD.
+template <bool kMap>
+__device__ __forceinline__ uint32_t unit_of_block(uint32_t b, uint32_t n, uint32_t chunk) {
+  if (!kMap) return b;
+  const uint32_t x = b & 7u, i = b >> 3;
+  if (chunk == 0) {
+    const uint32_t per = n >> 3, rem = n & 7u;
+    return x * per + min(x, rem) + i;
+  }
+  const uint32_t full = n / (8u * chunk) * (8u * chunk);
+  if (b >= full) return b;
+  return ((i / chunk) * 8u + x) * chunk + i % chunk;
+}
+
+// Region of a work unit: the chunk table brackets it, a short binary search
+// over the regions' first units finds it (all loads are uniform).
+template <class Reg>
+__device__ __forceinline__ const Reg* find_region(const LaunchArgs& a, uint32_t unit) {
+  const Reg* regs = static_cast<const Reg*>(a.regions);
+  const uint32_t c = unit >> kChunkShift;
+  uint32_t lo = __builtin_amdgcn_readfirstlane(a.unit_region[c]);
+  uint32_t hi = __builtin_amdgcn_readfirstlane(a.unit_region[c + 1]) + 1;
+  while (hi - lo > 1) {
+    const uint32_t mid = (lo + hi) >> 1;
+    if (regs[mid].unit_begin <= unit) lo = mid; else hi = mid;
+  }
+  return regs + lo;
 }
 
 // Copies one granule of g bytes (g in {1,2,4,8,16}; both addresses g-aligned).
@@ -129,6 +197,51 @@ __device__ __forceinline__ void block_copy_bytes(char* d, const char* s, uint32_
 // bulk
 // ---------------------------------------------------------------------------
 
+// Short aligned rows: lane groups of L lanes per row; each lane holds M
+// vectors of each of U rows before storing them.
+template <bool kFan1, int M>
+__device__ __forceinline__ void bulk_short_rows(const LaunchArgs& a, const CopyRegion* R,
+                                                const char* sp, char* dp0, uint64_t dst_off,
+                                                uint32_t r0, uint32_t r1, uint32_t vpr, uint32_t L,
+                                                uint32_t e0, uint32_t e1, uint32_t nouter,
+                                                uint64_t s0, uint64_t s1, uint64_t s2,
+                                                uint64_t d0, uint64_t d1, uint64_t d2, uint32_t nd) {
+  constexpr int U = RS_UNROLL / M > 0 ? RS_UNROLL / M : 1;
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = tid & 63u, wave = tid >> 6;
+  const uint32_t sub = lane & (L - 1u);
+  const uint32_t G = 64u / L;
+  const uint32_t step = 4u * G;
+  for (uint32_t rb = r0 + wave * G + lane / L; rb < r1; rb += U * step) {
+    u32x4 x[U][M];
+    uint64_t dofs[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t r = rb + u * step;
+      const bool rv = r < r1;
+      const uint64_t so = rv ? row_off(r, e0, e1, nouter, s0, s1, s2) : 0;
+      dofs[u] = rv ? row_off(r, e0, e1, nouter, d0, d1, d2) : 0;
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const uint32_t v = sub + m * L;
+        if (rv && v < vpr) x[u][m] = ld16(sp + so + 16ull * v);
+      }
+    }
+    for (uint32_t j = 0; j < nd; ++j) {
+      char* d = kFan1 ? dp0 : static_cast<char*>(a.ptr[R->dst_ptr[j]]) + dst_off;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t r = rb + u * step;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          const uint32_t v = sub + m * L;
+          if (r < r1 && v < vpr) st16(d + dofs[u] + 16ull * v, x[u][m]);
+        }
+      }
+    }
+  }
+}
+
 template <bool kFan1>
 __device__ __forceinline__ void bulk_body(const LaunchArgs& a, const CopyRegion* R, uint32_t unit) {
   const uint32_t tid = threadIdx.x;
@@ -157,54 +270,56 @@ __device__ __forceinline__ void bulk_body(const LaunchArgs& a, const CopyRegion*
       const uint64_t so = row_off(r, e0, e1, nouter, s0, s1, s2);
       const uint64_t dof = row_off(r, e0, e1, nouter, d0, d1, d2);
       const char* s = sp + so;
-      for (uint32_t v = tid; v < vpr; v += 4 * kThreads) {
-        const bool b1 = v + kThreads < vpr, b2 = v + 2 * kThreads < vpr, b3 = v + 3 * kThreads < vpr;
-        u32x4 x0 = ld16(s + 16ull * v), x1{}, x2{}, x3{};
-        if (b1) x1 = ld16(s + 16ull * (v + kThreads));
-        if (b2) x2 = ld16(s + 16ull * (v + 2 * kThreads));
-        if (b3) x3 = ld16(s + 16ull * (v + 3 * kThreads));
+#if RS_PIPE
+      // Software pipelined: the next batch of loads is issued before the
+      // current batch is stored.
+      u32x4 x[RS_UNROLL], y[RS_UNROLL];
+      uint32_t v = tid;
+#pragma unroll
+      for (int k = 0; k < RS_UNROLL; ++k)
+        if (v + k * kThreads < vpr) x[k] = ld16(s + 16ull * (v + k * kThreads));
+      for (; v < vpr; v += RS_UNROLL * kThreads) {
+        const uint32_t vn = v + RS_UNROLL * kThreads;
+#pragma unroll
+        for (int k = 0; k < RS_UNROLL; ++k)
+          if (vn + k * kThreads < vpr) y[k] = ld16(s + 16ull * (vn + k * kThreads));
         for (uint32_t j = 0; j < nd; ++j) {
           char* d = (kFan1 ? dp0 : static_cast<char*>(a.ptr[R->dst_ptr[j]]) + dst_off) + dof;
-          st16(d + 16ull * v, x0);
-          if (b1) st16(d + 16ull * (v + kThreads), x1);
-          if (b2) st16(d + 16ull * (v + 2 * kThreads), x2);
-          if (b3) st16(d + 16ull * (v + 3 * kThreads), x3);
+#pragma unroll
+          for (int k = 0; k < RS_UNROLL; ++k)
+            if (v + k * kThreads < vpr) st16(d + 16ull * (v + k * kThreads), x[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < RS_UNROLL; ++k) x[k] = y[k];
+      }
+#else
+      for (uint32_t v = tid; v < vpr; v += RS_UNROLL * kThreads) {
+        u32x4 x[RS_UNROLL];
+#pragma unroll
+        for (int k = 0; k < RS_UNROLL; ++k)
+          if (v + k * kThreads < vpr) x[k] = ld16(s + 16ull * (v + k * kThreads));
+        for (uint32_t j = 0; j < nd; ++j) {
+          char* d = (kFan1 ? dp0 : static_cast<char*>(a.ptr[R->dst_ptr[j]]) + dst_off) + dof;
+#pragma unroll
+          for (int k = 0; k < RS_UNROLL; ++k)
+            if (v + k * kThreads < vpr) st16(d + 16ull * (v + k * kThreads), x[k]);
         }
       }
+#endif
     }
   } else if (al == 0) {
     // Short rows: L lanes per row (a power of two >= the row's vectors, at
-    // most 64), 64 / L rows per wave step; each lane moves <= 2 vectors of a
-    // row and two rows per iteration.
+    // most 64), 64 / L rows per wave step; each lane moves one or two
+    // vectors of each of several rows per iteration.
     const uint32_t vpr = inner >> 4;
     uint32_t L = 1;
     while (L < vpr && L < 64u) L <<= 1;
-    const uint32_t lane = tid & 63u, wave = tid >> 6;
-    const uint32_t sub = lane & (L - 1u);
-    const uint32_t G = 64u / L;
-    const uint32_t step = 4u * G;
-    for (uint32_t rb = r0 + wave * G + lane / L; rb < r1; rb += 2u * step) {
-      const uint32_t ra = rb, rc = rb + step;
-      const bool hc = rc < r1;
-      const uint64_t soa = row_off(ra, e0, e1, nouter, s0, s1, s2);
-      const uint64_t doa = row_off(ra, e0, e1, nouter, d0, d1, d2);
-      const uint64_t soc = hc ? row_off(rc, e0, e1, nouter, s0, s1, s2) : 0;
-      const uint64_t doc = hc ? row_off(rc, e0, e1, nouter, d0, d1, d2) : 0;
-      const uint32_t v0 = sub, v1 = sub + L;
-      const bool a0 = v0 < vpr, a1 = v1 < vpr;
-      u32x4 xa0{}, xa1{}, xc0{}, xc1{};
-      if (a0) xa0 = ld16(sp + soa + 16ull * v0);
-      if (a1) xa1 = ld16(sp + soa + 16ull * v1);
-      if (hc && a0) xc0 = ld16(sp + soc + 16ull * v0);
-      if (hc && a1) xc1 = ld16(sp + soc + 16ull * v1);
-      for (uint32_t j = 0; j < nd; ++j) {
-        char* d = kFan1 ? dp0 : static_cast<char*>(a.ptr[R->dst_ptr[j]]) + dst_off;
-        if (a0) st16(d + doa + 16ull * v0, xa0);
-        if (a1) st16(d + doa + 16ull * v1, xa1);
-        if (hc && a0) st16(d + doc + 16ull * v0, xc0);
-        if (hc && a1) st16(d + doc + 16ull * v1, xc1);
-      }
-    }
+    if (vpr > L)
+      bulk_short_rows<kFan1, 2>(a, R, sp, dp0, dst_off, r0, r1, vpr, L, e0, e1, nouter,
+                                s0, s1, s2, d0, d1, d2, nd);
+    else
+      bulk_short_rows<kFan1, 1>(a, R, sp, dp0, dst_off, r0, r1, vpr, L, e0, e1, nouter,
+                                s0, s1, s2, d0, d1, d2, nd);
   } else {
     // Misaligned: one row per wave at the co-alignment granule.
     const uint32_t lane = tid & 63u, wave = tid >> 6;
@@ -219,14 +334,17 @@ __device__ __forceinline__ void bulk_body(const LaunchArgs& a, const CopyRegion*
   }
 }
 
-__global__ __launch_bounds__(kThreads) void rs_bulk_kernel(LaunchArgs a) {
-  const uint32_t unit = blockIdx.x;
-  const uint32_t ri = __builtin_amdgcn_readfirstlane(a.unit_region[unit]);
-  const CopyRegion* R = static_cast<const CopyRegion*>(a.regions) + ri;
-  if (R->n_dst == 1)
-    bulk_body<true>(a, R, unit);
-  else
-    bulk_body<false>(a, R, unit);
+__global__ __launch_bounds__(kThreads, RS_BULK_MIN_WAVES) void rs_bulk_kernel(LaunchArgs a) {
+  // gridDim.x may be smaller than the number of units (a persistent grid):
+  // each workgroup then takes units blockIdx.x, blockIdx.x + gridDim.x, ...
+  for (uint32_t ub = blockIdx.x; ub < a.n_units; ub += gridDim.x) {
+    const uint32_t unit = gridDim.x == a.n_units ? unit_of_block<RS_XCD_MAP != 0>(ub, a.n_units, RS_XCD_CHUNK) : ub;
+    const CopyRegion* R = find_region<CopyRegion>(a, unit);
+    if (R->n_dst == 1)
+      bulk_body<true>(a, R, unit);
+    else
+      bulk_body<false>(a, R, unit);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -237,8 +355,7 @@ __global__ __launch_bounds__(kThreads) void rs_thin_kernel(LaunchArgs a) {
   __shared__ __attribute__((aligned(16))) char tile[kThinTile + 16];
   const uint32_t tid = threadIdx.x;
   const uint32_t unit = blockIdx.x;
-  const uint32_t ri = __builtin_amdgcn_readfirstlane(a.unit_region[unit]);
-  const CopyRegion* R = static_cast<const CopyRegion*>(a.regions) + ri;
+  const CopyRegion* R = find_region<CopyRegion>(a, unit);
   const uint64_t src_off = R->src_off, dst_off = R->dst_off;
   const uint64_t s0 = R->sstr[0], s1 = R->sstr[1], s2 = R->sstr[2];
   const uint64_t d0 = R->dstr[0], d1 = R->dstr[1], d2 = R->dstr[2];
@@ -382,42 +499,108 @@ __device__ __forceinline__ int shared_exp(uint32_t amax_bits) {
   return X < -127 ? -127 : (X > 127 ? 127 : X);
 }
 
-// E4M3 code of v * 2^-X for a bf16 bit pattern b: round to nearest even,
-// saturating at 448, sign of zero kept.  |v| = M * 2^k with an 8-bit integer
-// M; the result's binade exponent is ee = max(floor(log2|q|), -6) and its grid
-// step 2^(ee-3), so the code is (ee + 6) * 8 + RNE(M * 2^(k - X - ee + 3)).
-__device__ __forceinline__ uint32_t e4m3(uint32_t b, int X) {
-  const uint32_t sign = (b >> 8) & 0x80u;
-  const uint32_t E = (b >> 7) & 0xFFu;
-  const uint32_t M = E ? (0x80u | (b & 0x7Fu)) : (b & 0x7Fu);
-  if (M == 0) return sign;
-  const int k = E ? int(E) - 134 : -133;
-  const int msb = 31 - __builtin_clz(M);
-  const int fl = msb + k - X;
-  if (fl >= 9) return sign | 0x7Eu;
-  const int ee = fl < -6 ? -6 : fl;
-  const int sh = ee - 3 - (k - X);
-  uint32_t n;
-  if (sh <= 0) {
-    n = M << (-sh);
-  } else if (sh > 30) {
-    n = 0;
-  } else {
-    n = M >> sh;
-    const uint32_t rem = M & ((1u << sh) - 1u);
-    const uint32_t half = 1u << (sh - 1);
-    n += (rem > half || (rem == half && (n & 1u))) ? 1u : 0u;
-  }
-  uint32_t code = uint32_t((ee + 6) * 8) + n;
-  if (code > 0x7Eu) code = 0x7Eu;
-  return sign | code;
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
+}
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
 }
 
-__global__ __launch_bounds__(kThreads) void rs_mx_kernel(LaunchArgs a) {
+// Four E4M3 codes (one 32-bit word, element i in byte i) of two words of
+// packed bf16 (w0, w1) with magnitudes (m0, m1) = w & 0x7FFF7FFF.  The
+// magnitude is first clamped to T = 448 * 2^X (bf16 magnitudes order like
+// their bit patterns, and T is a bf16 value), so the conversion saturates;
+// v_cvt_scalef32_pk_fp8_bf16 then gives round-to-nearest-even of v / 2^X,
+// exactly, for every finite bf16 (subnormals included).
+__device__ __forceinline__ uint32_t e4m3x4(uint32_t w0, uint32_t w1, uint32_t m0, uint32_t m1,
+                                           uint32_t T2, float scale) {
+  const uint32_t c0 = (w0 & 0x80008000u) | pk_min_u16(m0, T2);
+  const uint32_t c1 = (w1 & 0x80008000u) | pk_min_u16(m1, T2);
+  s16x2 r = s16x2{0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2, c0), scale, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2, c1), scale, true);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+struct MxRow {
+  const char* src;   // bf16 row start
+  uint64_t dst_off;  // element-row offset from each destination pointer
+  uint64_t sc_off;   // scale-row offset from each scale pointer
+};
+
+#ifndef RS_MX_MIN_WAVES
+#define RS_MX_MIN_WAVES 1  // occupancy floor (waves per SIMD) the register allocator must keep
+#endif
+
+// Loads one lane's 8-element group g of a row (zeros past the row end).
+__device__ __forceinline__ int mx_load(const MxRow& row, uint32_t g, uint32_t inner, u32x4& x) {
+  const uint32_t col = g * 8u;
+  const int nvalid = int(min(inner, col + 8u)) - int(min(inner, col));
+  const uint16_t* s = reinterpret_cast<const uint16_t*>(row.src) + col;
+  x = u32x4{0u, 0u, 0u, 0u};
+  if (nvalid == 8 && (reinterpret_cast<uintptr_t>(s) & 15u) == 0) {
+    x = ld16(s);
+  } else if (nvalid > 0) {
+    uint32_t w[4] = {0, 0, 0, 0};
+    for (int i = 0; i < 8; ++i)
+      if (i < nvalid) w[i >> 1] |= uint32_t(s[i]) << (16 * (i & 1));
+    x = u32x4{w[0], w[1], w[2], w[3]};
+  }
+  return nvalid;
+}
+
+// Quantises and stores one lane's group (4 consecutive lanes = one block).
+// All four lanes of a block must call this together: the block's amax is
+// reduced across them.  Lanes past the row end pass nvalid <= 0.
+__device__ __forceinline__ void mx_finish(const LaunchArgs& a, const MxRegion* R, const MxRow& row,
+                                          uint32_t g, u32x4 x, int nvalid, uint32_t sc_inner,
+                                          uint32_t nd) {
+  const uint32_t w0 = x.x, w1 = x.y, w2 = x.z, w3 = x.w;
+  const uint32_t m0 = w0 & 0x7FFF7FFFu, m1 = w1 & 0x7FFF7FFFu;
+  const uint32_t m2 = w2 & 0x7FFF7FFFu, m3 = w3 & 0x7FFF7FFFu;
+  const uint32_t mm = pk_max_u16(pk_max_u16(m0, m1), pk_max_u16(m2, m3));
+  uint32_t amax = max(mm & 0xFFFFu, mm >> 16);
+  // Block amax across the quad: DPP quad_perm [1,0,3,2] then [2,3,0,1].
+  amax = max(amax, uint32_t(__builtin_amdgcn_update_dpp(0, int(amax), 0xB1, 0xF, 0xF, true)));
+  amax = max(amax, uint32_t(__builtin_amdgcn_update_dpp(0, int(amax), 0x4E, 0xF, 0xF, true)));
+  if (nvalid <= 0) return;
+  const bool bad = amax >= 0x7F80u;
+  const int X = shared_exp(amax);
+  const uint32_t T = (uint32_t(X + 135) << 7) | 0x60u;   // bf16 bits of 448 * 2^X
+  const uint32_t T2 = T | (T << 16);
+  const float sc = __builtin_amdgcn_ldexpf(1.0f, X);
+  uint32_t lo = e4m3x4(w0, w1, m0, m1, T2, sc);
+  uint32_t hi = e4m3x4(w2, w3, m2, m3, T2, sc);
+  if (bad) lo = hi = 0x7F7F7F7Fu;
+  const uint8_t scale = bad ? uint8_t(0xFF) : uint8_t(X + 127);
+  const uint32_t col = g * 8u;
+  const bool lead = (g & 3u) == 0;
+  const uint64_t sco = row.sc_off + uint64_t(g >> 2) * sc_inner;
+  for (uint32_t j = 0; j < nd; ++j) {
+    char* d = static_cast<char*>(a.ptr[R->dst_ptr[j]]) + row.dst_off + col;
+    if (nvalid == 8 && (reinterpret_cast<uintptr_t>(d) & 7u) == 0) {
+      u32x2 v;
+      v.x = lo;
+      v.y = hi;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(d));
+    } else {
+      for (int i = 0; i < 8; ++i)
+        if (i < nvalid) d[i] = char(((i < 4 ? lo : hi) >> (8 * (i & 3))) & 0xFFu);
+    }
+    if (lead) *(static_cast<char*>(a.ptr[R->sc_ptr[j]]) + sco) = char(scale);
+  }
+}
+
+__global__ __launch_bounds__(kThreads, RS_MX_MIN_WAVES) void rs_mx_kernel(LaunchArgs a) {
   const uint32_t tid = threadIdx.x;
-  const uint32_t unit = blockIdx.x;
-  const uint32_t ri = __builtin_amdgcn_readfirstlane(a.unit_region[unit]);
-  const MxRegion* R = static_cast<const MxRegion*>(a.regions) + ri;
+  const uint32_t unit = unit_of_block<RS_MX_XCD_MAP != 0>(blockIdx.x, gridDim.x, RS_XCD_CHUNK);
+  const MxRegion* R = find_region<MxRegion>(a, unit);
   const uint64_t src_off = R->src_off, dst_off = R->dst_off, sc_off = R->sc_off;
   const uint64_t s0 = R->sstr[0], s1 = R->sstr[1], s2 = R->sstr[2];
   const uint64_t d0 = R->dstr[0], d1 = R->dstr[1], d2 = R->dstr[2];
@@ -431,61 +614,57 @@ __global__ __launch_bounds__(kThreads) void rs_mx_kernel(LaunchArgs a) {
 
   const uint32_t r0 = (unit - ub) * rpu;
   const uint32_t r1 = min(r0 + rpu, rows);
-  const uint32_t nb = (inner + 31u) >> 5;
-  const uint32_t total = (r1 - r0) * nb;
-  const uint32_t quad = tid >> 2, sub = tid & 3u;
+  const uint32_t ng = (inner + 7u) >> 3;     // 8-element groups per row
+  const uint32_t ngp = (ng + 3u) & ~3u;      // padded to whole blocks
+  constexpr int U = kMxUnroll;
 
-  for (uint32_t fb = quad; fb < total; fb += kThreads / 4) {
-    const uint32_t rr = fb / nb;
-    const uint32_t b = fb - rr * nb;
-    const uint32_t row = r0 + rr;
-    const uint64_t so = row_off(row, e0, e1, nouter, s0, s1, s2);
-    const uint64_t dof = row_off(row, e0, e1, nouter, d0, d1, d2);
-    const uint64_t sco = row_off(row, e0, e1, nouter, c0, c1, c2);
-    const uint32_t col = b * 32u + sub * 8u;
-    const int nvalid = int(min(inner, col + 8u)) - int(min(inner, col));
-    const uint16_t* s = reinterpret_cast<const uint16_t*>(sp + so) + col;
-    uint32_t w[4] = {0, 0, 0, 0};
-    if (nvalid == 8 && (reinterpret_cast<uintptr_t>(s) & 15u) == 0) {
-      const u32x4 x = ld16(s);
-      w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
-    } else {
-      for (int i = 0; i < 8; ++i)
-        if (i < nvalid) w[i >> 1] |= uint32_t(s[i]) << (16 * (i & 1));
-    }
-    uint32_t amax = 0;
-    for (int i = 0; i < 4; ++i) {
-      amax = max(amax, w[i] & 0x7FFFu);
-      amax = max(amax, (w[i] >> 16) & 0x7FFFu);
-    }
-    amax = max(amax, uint32_t(__shfl_xor(int(amax), 1, 64)));
-    amax = max(amax, uint32_t(__shfl_xor(int(amax), 2, 64)));
-    const bool bad = amax >= 0x7F80u;
-    const int X = shared_exp(amax);
-    uint32_t lo = 0, hi = 0;
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t c = bad ? 0x7Fu : e4m3(w[i >> 1] >> (16 * (i & 1)) & 0xFFFFu, X);
-      lo |= c << (8 * i);
-    }
-    for (int i = 4; i < 8; ++i) {
-      const uint32_t c = bad ? 0x7Fu : e4m3(w[i >> 1] >> (16 * (i & 1)) & 0xFFFFu, X);
-      hi |= c << (8 * (i - 4));
-    }
-    const uint8_t scale = bad ? uint8_t(0xFF) : uint8_t(X + 127);
-    for (uint32_t j = 0; j < nd; ++j) {
-      char* d = static_cast<char*>(a.ptr[R->dst_ptr[j]]) + dst_off + dof + col;
-      if (nvalid == 8 && (reinterpret_cast<uintptr_t>(d) & 7u) == 0) {
-        u32x2 v;
-        v.x = lo;
-        v.y = hi;
-        __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(d));
-      } else {
-        for (int i = 0; i < 8; ++i)
-          if (i < nvalid) d[i] = char(((i < 4 ? lo : hi) >> (8 * (i & 3))) & 0xFFu);
+  if (ng >= kThreads) {
+    // Long rows: the workgroup walks rows (uniform row addresses); each lane
+    // loads U groups of the row before quantising them.
+    for (uint32_t r = r0; r < r1; ++r) {
+      MxRow row;
+      row.src = sp + row_off(r, e0, e1, nouter, s0, s1, s2);
+      row.dst_off = dst_off + row_off(r, e0, e1, nouter, d0, d1, d2);
+      row.sc_off = sc_off + row_off(r, e0, e1, nouter, c0, c1, c2);
+      for (uint32_t g0 = tid; g0 < ngp; g0 += U * kThreads) {
+        u32x4 x[U];
+        int nv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) nv[u] = mx_load(row, g0 + u * kThreads, inner, x[u]);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (g0 + u * kThreads < ngp) mx_finish(a, R, row, g0 + u * kThreads, x[u], nv[u], sc_inner, nd);
       }
-      if (sub == 0) {
-        char* sc = static_cast<char*>(a.ptr[R->sc_ptr[j]]) + sc_off + sco + uint64_t(b) * sc_inner;
-        *sc = char(scale);
+    }
+  } else {
+    // Short rows: L lanes per row (a power of two, at least one block); each
+    // lane loads its group of U rows before quantising them.
+    uint32_t L = 4;
+    while (L < ng && L < 64u) L <<= 1;
+    const uint32_t lane = tid & 63u, wave = tid >> 6;
+    const uint32_t G = 64u / L;
+    const uint32_t sub = lane & (L - 1u);
+    const uint32_t step = 4u * G;
+    for (uint32_t rb = r0 + wave * G + lane / L; rb < r1; rb += U * step) {
+      for (uint32_t g = sub; g < ngp; g += L) {
+        MxRow row[U];
+        u32x4 x[U];
+        int nv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const uint32_t r = rb + u * step;
+          nv[u] = 0;
+          x[u] = u32x4{0u, 0u, 0u, 0u};
+          if (r < r1) {
+            row[u].src = sp + row_off(r, e0, e1, nouter, s0, s1, s2);
+            row[u].dst_off = dst_off + row_off(r, e0, e1, nouter, d0, d1, d2);
+            row[u].sc_off = sc_off + row_off(r, e0, e1, nouter, c0, c1, c2);
+            nv[u] = mx_load(row[u], g, inner, x[u]);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (rb + u * step < r1) mx_finish(a, R, row[u], g, x[u], nv[u], sc_inner, nd);
       }
     }
   }
@@ -493,10 +672,28 @@ __global__ __launch_bounds__(kThreads) void rs_mx_kernel(LaunchArgs a) {
 
 }  // namespace
 
+#ifndef RS_BULK_WG_PER_CU
+#define RS_BULK_WG_PER_CU 0   // 0: one workgroup per unit; n > 0: persistent grid of n per CU
+#endif
+
 hipError_t launch(uint32_t bucket, uint32_t grid, const LaunchArgs& args, hipStream_t stream) {
   if (grid == 0) return hipSuccess;
   switch (bucket) {
-    case kBulk: hipLaunchKernelGGL(rs_bulk_kernel, dim3(grid), dim3(kThreads), 0, stream, args); break;
+    case kBulk: {
+      uint32_t g = grid;
+#if RS_BULK_WG_PER_CU > 0
+      static int cus = 0;
+      if (!cus) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+          cus = 256;
+      }
+      g = min(grid, uint32_t(cus) * RS_BULK_WG_PER_CU);
+#endif
+      hipLaunchKernelGGL(rs_bulk_kernel, dim3(g), dim3(kThreads), 0, stream, args);
+      break;
+    }
     case kThin: hipLaunchKernelGGL(rs_thin_kernel, dim3(grid), dim3(kThreads), 0, stream, args); break;
     case kTiny: hipLaunchKernelGGL(rs_tiny_kernel, dim3(grid), dim3(kThreads), 0, stream, args); break;
     case kMx: hipLaunchKernelGGL(rs_mx_kernel, dim3(grid), dim3(kThreads), 0, stream, args); break;

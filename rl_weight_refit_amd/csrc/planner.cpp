@@ -30,7 +30,6 @@
 #include <algorithm>
 #include <chrono>
 #include <cstring>
-#include <map>
 #include <sstream>
 #include <utility>
 
@@ -312,30 +311,43 @@ struct Dim {
   uint64_t ext, ss, ds, sc;  // extent; byte strides on src, dst, scale sides
 };
 
+// Outer dims, outermost first (fixed capacity: tensor rank + one split).
+struct Dims {
+  Dim d[RS_MAX_DIMS + 1];
+  int n = 0;
+  void push_back(const Dim& x) { d[n++] = x; }
+  void pop_back() { --n; }
+  Dim& back() { return d[n - 1]; }
+  Dim& front() { return d[0]; }
+  bool empty() const { return n == 0; }
+  size_t size() const { return size_t(n); }
+  const Dim* begin() const { return d; }
+  const Dim* end() const { return d + n; }
+};
+
 struct Raw {
   uint32_t tensor;
   bool mx;
   uint32_t src_index;
-  std::vector<uint32_t> dst_index, sc_index;
+  uint32_t n_dst;
+  uint32_t dst_index[kMaxFan], sc_index[kMaxFan];
   uint64_t src_off, dst_off, sc_off;
   uint64_t inner;                 // bytes (copy) or elements (mx)
   uint64_t sc_inner;
-  std::vector<Dim> outer;         // outermost first
+  Dims outer;
 };
 
-uint64_t rows_of(const std::vector<Dim>& o) {
+uint64_t rows_of(const Dims& o) {
   uint64_t r = 1;
   for (const Dim& d : o) r *= d.ext;
   return r;
 }
 
 // Merge mergeable adjacent outer dims; drop extent-1 dims.
-void merge_outer(std::vector<Dim>& o, bool with_scale) {
-  std::vector<Dim> v;
-  for (const Dim& d : o)
-    if (d.ext != 1) v.push_back(d);
-  std::vector<Dim> m;
-  for (const Dim& d : v) {
+void merge_outer(Dims& o, bool with_scale) {
+  Dims m;
+  for (const Dim& d : o) {
+    if (d.ext == 1) continue;
     if (!m.empty()) {
       Dim& p = m.back();  // p outer, d inner
       if (p.ss == d.ext * d.ss && p.ds == d.ext * d.ds && (!with_scale || p.sc == d.ext * d.sc)) {
@@ -348,19 +360,36 @@ void merge_outer(std::vector<Dim>& o, bool with_scale) {
     }
     m.push_back(d);
   }
-  o.swap(m);
+  o = m;
 }
 
 struct Opts {
   bool fanout = true;
-  uint64_t unit = 65536;
+  uint64_t unit = 16384;
   uint64_t tiny = 1024;
   uint64_t thin = 128;
 };
 
 // Splits a raw region until the kernels can take it: at most 3 outer dims,
 // rows < 2^31, every extent < 2^32, and (copy) inner <= unit bytes.
-void finalize(Raw r, const Opts& o, std::vector<Raw>& out) {
+void finalize(Raw r, const Opts& o, std::vector<Raw>& out) {  // r by value: it is modified
+  if (r.mx && r.inner > kMxBatchElems) {
+    // Split long MXFP8 rows into block-aligned segments of one batch each.
+    const uint64_t C = kMxBatchElems;
+    const uint64_t q = r.inner / C, rem = r.inner % C;
+    const uint64_t sc_step = (C / kMxBlock) * r.sc_inner;
+    if (rem) {
+      Raw tail = r;
+      tail.inner = rem;
+      tail.src_off += q * C * 2;
+      tail.dst_off += q * C;
+      tail.sc_off += q * sc_step;
+      finalize(tail, o, out);
+    }
+    r.inner = C;
+    r.outer.push_back({q, 2 * C, C, sc_step});
+    merge_outer(r.outer, true);
+  }
   if (!r.mx && r.inner > o.unit) {
     const uint64_t q = r.inner / o.unit, rem = r.inner % o.unit;
     if (rem) {
@@ -381,8 +410,9 @@ void finalize(Raw r, const Opts& o, std::vector<Raw>& out) {
   if (r.outer.size() > 3 || rows > kMaxRows || ext_big) {
     // Peel the outermost dim: either one index at a time (too many dims) or
     // in halves (too many rows).
-    Dim top = r.outer.front();
-    std::vector<Dim> rest(r.outer.begin() + 1, r.outer.end());
+    const Dim top = r.outer.front();
+    Dims rest;
+    for (int i = 1; i < r.outer.n; ++i) rest.push_back(r.outer.d[i]);
     if (r.outer.size() > 3) {
       for (uint64_t i = 0; i < top.ext; ++i) {
         Raw s = r;
@@ -396,10 +426,11 @@ void finalize(Raw r, const Opts& o, std::vector<Raw>& out) {
       const uint64_t h = top.ext / 2;
       for (int part = 0; part < 2; ++part) {
         Raw s = r;
-        s.outer = rest;
         const uint64_t n = part ? top.ext - h : h;
         const uint64_t first = part ? h : 0;
-        s.outer.insert(s.outer.begin(), Dim{n, top.ss, top.ds, top.sc});
+        s.outer.n = 0;
+        s.outer.push_back(Dim{n, top.ss, top.ds, top.sc});
+        for (const Dim& x : rest) s.outer.push_back(x);
         s.src_off += first * top.ss;
         s.dst_off += first * top.ds;
         s.sc_off += first * top.sc;
@@ -412,7 +443,7 @@ void finalize(Raw r, const Opts& o, std::vector<Raw>& out) {
 }
 
 struct Final {
-  Raw raw;
+  const Raw* rp;
   uint32_t bucket;
   uint32_t flags;
   uint64_t rows;
@@ -421,7 +452,7 @@ struct Final {
 };
 
 // Fills the fields shared by the public and device views.
-void outer_fields(const std::vector<Dim>& o, uint64_t ext[3], uint64_t ss[3], uint64_t ds[3],
+void outer_fields(const Dims& o, uint64_t ext[3], uint64_t ss[3], uint64_t ds[3],
                   uint64_t sc[3]) {
   // Device convention: index 0 is the innermost outer dim.
   for (int k = 0; k < 3; ++k) {
@@ -430,7 +461,7 @@ void outer_fields(const std::vector<Dim>& o, uint64_t ext[3], uint64_t ss[3], ui
   }
   const int n = int(o.size());
   for (int k = 0; k < n; ++k) {
-    const Dim& d = o[n - 1 - k];
+    const Dim& d = o.d[n - 1 - k];
     ext[k] = d.ext;
     ss[k] = d.ss;
     ds[k] = d.ds;
@@ -545,7 +576,23 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
   out.dst_span.assign(n_dst_ptrs, 0);
 
   // ---- steps 2 and 3: overlap boxes -> byte regions -------------------------
-  std::vector<Raw> raws;
+  // Scratch reused across calls on this thread (plans are often rebuilt
+  // for the same layouts; keeping capacity avoids fresh allocations).
+  struct Target {
+    int64_t dslot, sslot;
+  };
+  struct Scratch {
+    std::vector<Target> targets;
+    std::vector<uint8_t> done;
+    std::vector<size_t> grp;
+    std::vector<Raw> raws, split;
+  };
+  thread_local Scratch scratch;
+  std::vector<Target>& targets = scratch.targets;
+  std::vector<uint8_t>& done = scratch.done;
+  std::vector<size_t>& grp = scratch.grp;
+  std::vector<Raw>& raws = scratch.raws;
+  raws.clear();
   for (int t = 0; t < n; ++t) {
     const Layout& A = S[t];
     const Layout& B = D[t];
@@ -573,10 +620,7 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
       }
       const int64_t cls = class_ordinal(B, di);
       // Destination slots of this class, each with its source replica.
-      struct Target {
-        int64_t dslot, sslot;
-      };
-      std::vector<Target> targets;
+      targets.clear();
       for (int64_t rep = 0; rep < B.nrep; ++rep) {
         const int64_t dlin = compose_coord(B, di, rep);
         const int64_t dslot = B.coord_to_slot[dlin];
@@ -586,11 +630,12 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
       }
       // Group destination replicas that read the same source through the same
       // views; each group becomes one region (one read, n_dst writes).
-      std::vector<bool> done(targets.size(), false);
+      done.assign(targets.size(), 0);
       for (size_t a = 0; a < targets.size(); ++a) {
         if (done[a]) continue;
-        std::vector<size_t> grp{a};
-        done[a] = true;
+        grp.clear();
+        grp.push_back(a);
+        done[a] = 1;
         if (o.fanout) {
           for (size_t b = a + 1; b < targets.size() && grp.size() < size_t(kMaxFan); ++b) {
             if (done[b] || targets[b].sslot != targets[a].sslot) continue;
@@ -599,7 +644,7 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
                                  B.scale_views[targets[a].dslot], nd))
               continue;
             grp.push_back(b);
-            done[b] = true;
+            done[b] = 1;
           }
         }
         const int64_t ss = targets[a].sslot, ds0 = targets[a].dslot;
@@ -611,9 +656,11 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
         r.tensor = t;
         r.mx = mx;
         r.src_index = uint32_t(src_base[t] + ss);
+        r.n_dst = 0;
         for (size_t g : grp) {
-          r.dst_index.push_back(uint32_t(dst_base[t] + targets[g].dslot));
-          if (mx) r.sc_index.push_back(uint32_t(sc_base[t] + targets[g].dslot));
+          r.dst_index[r.n_dst] = uint32_t(dst_base[t] + targets[g].dslot);
+          r.sc_index[r.n_dst] = mx ? uint32_t(sc_base[t] + targets[g].dslot) : 0;
+          ++r.n_dst;
         }
         int64_t so = sv.base, dof = dv.base, sco = 0;
         for (int dd = 0; dd < nd; ++dd) {
@@ -628,13 +675,11 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
           r.sc_inner = 0;
           // Element size folds into the innermost run; runs grow while both
           // sides stay contiguous.
-          std::vector<Dim> dims;
+          Dims keep;
           for (int dd = 0; dd < nd; ++dd)
-            dims.push_back({uint64_t(len[dd]), uint64_t(sv.strides[dd]) * es,
-                            uint64_t(dv.strides[dd]) * es, 0});
-          std::vector<Dim> keep;
-          for (const Dim& x : dims)
-            if (x.ext != 1) keep.push_back(x);
+            if (len[dd] != 1)
+              keep.push_back({uint64_t(len[dd]), uint64_t(sv.strides[dd]) * es,
+                              uint64_t(dv.strides[dd]) * es, 0});
           uint64_t run = es;
           while (!keep.empty() && keep.back().ss == run && keep.back().ds == run) {
             run *= keep.back().ext;
@@ -683,25 +728,37 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
   }
 
   // ---- step 4: split, bucket, size work units ------------------------------
-  std::vector<Raw> split;
-  for (Raw& r : raws) finalize(std::move(r), o, split);
+  std::vector<Raw>& split = scratch.split;
+  split.clear();
+  for (Raw& r : raws) finalize(r, o, split);
   raws.clear();
 
-  std::vector<Final> fin;
+  thread_local std::vector<Final> fin;
+  fin.clear();
   fin.reserve(split.size());
   uint64_t bytes_read = 0, bytes_written = 0, bytes_nofan = 0;
-  for (Raw& r : split) {
+  for (const Raw& r : split) {
     Final f;
+    f.rp = &r;
     f.rows = rows_of(r.outer);
     const int nouter = int(r.outer.size());
     uint64_t ext[3], ss[3], ds[3], sc[3];
     outer_fields(r.outer, ext, ss, ds, sc);
     f.flags = uint32_t(nouter);
-    const uint64_t nd = r.dst_index.size();
+    const uint64_t nd = r.n_dst;
     if (r.mx) {
       f.bucket = kMx;
       const uint64_t row_bytes = r.inner * 2;
-      const uint64_t rpu = std::max<uint64_t>(1, o.unit / row_bytes);
+      // One load batch per work unit: rows of at least kThreads groups take
+      // the whole workgroup; shorter rows are spread over lane groups of L
+      // lanes (as in the kernel), kMxUnroll rows per lane.
+      const uint64_t ng = (r.inner + 7) / 8;
+      uint64_t rpu = 1;
+      if (ng < uint64_t(kThreads)) {
+        uint64_t L = 4;
+        while (L < ng && L < 64) L <<= 1;
+        rpu = uint64_t(kThreads) * kMxUnroll / L;
+      }
       f.rows_per_unit = uint32_t(std::min<uint64_t>(rpu, f.rows));
       const uint64_t nb = (r.inner + kMxBlock - 1) / kMxBlock;
       bytes_read += f.rows * row_bytes;
@@ -743,24 +800,29 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
       span_c += r.mx ? ((r.inner + kMxBlock - 1) / kMxBlock - 1) * r.sc_inner + 1 : 0;
       out.src_used[r.src_index] = 1;
       out.src_span[r.src_index] = std::max(out.src_span[r.src_index], span_s);
-      for (uint32_t di : r.dst_index) {
+      for (uint32_t j = 0; j < r.n_dst; ++j) {
+        const uint32_t di = r.dst_index[j];
         out.dst_used[di] = 1;
         out.dst_span[di] = std::max(out.dst_span[di], span_d);
-      }
-      for (uint32_t ci : r.sc_index) {
-        out.dst_used[ci] = 1;
-        out.dst_span[ci] = std::max(out.dst_span[ci], span_c);
+        if (r.mx) {
+          const uint32_t ci = r.sc_index[j];
+          out.dst_used[ci] = 1;
+          out.dst_span[ci] = std::max(out.dst_span[ci], span_c);
+        }
       }
     }
-    f.raw = std::move(r);
-    fin.push_back(std::move(f));
+    fin.push_back(f);
   }
 
   // ---- device image: per bucket, launch groups bounded by the pointer pool --
   out.image.clear();
   out.launches.clear();
-  out.regions.clear();
+  out.region_tensor.clear();
+  out.region_tensor.reserve(fin.size());
+  out.image.reserve(fin.size() * sizeof(MxRegion) + 8 * 256 + 4 * (fin.size() + 8) +
+                    4 * ((bytes_read / o.unit) >> kChunkShift) + 4096);
   uint64_t nreg_bucket[kBuckets] = {}, nunit_bucket[kBuckets] = {};
+  std::vector<int32_t> pool_src(n_src_ptrs, -1), pool_dst(n_dst_ptrs, -1);
   for (uint32_t bucket = 0; bucket < kBuckets; ++bucket) {
     std::vector<const Final*> list;
     for (const Final& f : fin)
@@ -768,42 +830,59 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
     size_t i = 0;
     while (i < list.size()) {
       // Greedy group: regions in order while their pointers fit the pool.
-      std::map<uint32_t, uint16_t> pool;
-      std::vector<const Final*> grp;
+      std::vector<uint32_t> members;    // pool slot -> caller pointer index (| kDstBit)
+      std::vector<const Final*> batch;
       uint64_t units = 0;
       while (i < list.size()) {
         const Final* f = list[i];
-        std::vector<uint32_t> need{f->raw.src_index};
-        for (uint32_t di : f->raw.dst_index) need.push_back(di | kDstBit);
-        for (uint32_t ci : f->raw.sc_index) need.push_back(ci | kDstBit);
+        uint32_t need[1 + 2 * kMaxFan];
+        int nneed = 0;
+        need[nneed++] = f->rp->src_index;
+        for (uint32_t j = 0; j < f->rp->n_dst; ++j) {
+          need[nneed++] = f->rp->dst_index[j] | kDstBit;
+          if (f->rp->mx) need[nneed++] = f->rp->sc_index[j] | kDstBit;
+        }
         size_t add = 0;
-        for (uint32_t k : need) add += pool.count(k) ? 0 : 1;
-        if (!grp.empty() && (pool.size() + add > size_t(kPool) ||
+        for (int q = 0; q < nneed; ++q) {
+          const uint32_t k = need[q];
+          const int32_t at = (k & kDstBit) ? pool_dst[k & ~kDstBit] : pool_src[k];
+          if (at < 0) {
+            bool dup = false;
+            for (int q2 = 0; q2 < q; ++q2) dup |= need[q2] == k;
+            add += dup ? 0 : 1;
+          }
+        }
+        if (!batch.empty() && (members.size() + add > size_t(kPool) ||
                              units + f->units > kMaxUnitsPerLaunch))
           break;
-        for (uint32_t k : need)
-          if (!pool.count(k)) {
-            const uint16_t idx = uint16_t(pool.size());
-            pool[k] = idx;
+        for (int q = 0; q < nneed; ++q) {
+          const uint32_t k = need[q];
+          int32_t& at = (k & kDstBit) ? pool_dst[k & ~kDstBit] : pool_src[k];
+          if (at < 0) {
+            at = int32_t(members.size());
+            members.push_back(k);
           }
-        grp.push_back(f);
+        }
+        batch.push_back(f);
         units += f->units;
         ++i;
       }
+      auto pool = [&](uint32_t k) -> uint16_t {
+        return uint16_t((k & kDstBit) ? pool_dst[k & ~kDstBit] : pool_src[k]);
+      };
       Launch L;
       L.bucket = bucket;
-      L.n_regions = uint32_t(grp.size());
-      L.pool.resize(pool.size());
-      for (auto& kv : pool) L.pool[kv.second] = kv.first;
+      L.n_regions = uint32_t(batch.size());
+      L.pool = members;
       align_up(out.image, 256);
       L.regions_off = out.image.size();
       const size_t rsz = bucket == kMx ? sizeof(MxRegion) : sizeof(CopyRegion);
-      out.image.resize(out.image.size() + rsz * grp.size(), 0);
+      out.image.resize(out.image.size() + rsz * batch.size(), 0);
       uint32_t ub = 0;
       std::vector<uint32_t> unit_region;
-      for (size_t k = 0; k < grp.size(); ++k) {
-        const Final& f = *grp[k];
-        const Raw& r = f.raw;
+      for (size_t k = 0; k < batch.size(); ++k) {
+        const Final& f = *batch[k];
+        const Raw& r = *f.rp;
         uint64_t ext[3], ss[3], ds[3], sc[3];
         outer_fields(r.outer, ext, ss, ds, sc);
         uint8_t* dstp = out.image.data() + L.regions_off + rsz * k;
@@ -826,11 +905,11 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
           m.unit_begin = ub;
           m.flags = f.flags;
           m.sc_inner = uint32_t(r.sc_inner);
-          m.src_ptr = pool[r.src_index];
-          m.n_dst = uint16_t(r.dst_index.size());
-          for (size_t j = 0; j < r.dst_index.size(); ++j) {
-            m.dst_ptr[j] = pool[r.dst_index[j] | kDstBit];
-            m.sc_ptr[j] = pool[r.sc_index[j] | kDstBit];
+          m.src_ptr = pool(r.src_index);
+          m.n_dst = uint16_t(r.n_dst);
+          for (uint32_t j = 0; j < r.n_dst; ++j) {
+            m.dst_ptr[j] = pool(r.dst_index[j] | kDstBit);
+            m.sc_ptr[j] = pool(r.sc_index[j] | kDstBit);
           }
           std::memcpy(dstp, &m, sizeof(m));
         } else {
@@ -851,49 +930,34 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
           c.rows_per_unit = f.rows_per_unit;
           c.unit_begin = ub;
           c.flags = f.flags | (uint32_t(al & 15) << 8);
-          c.src_ptr = pool[r.src_index];
-          c.n_dst = uint16_t(r.dst_index.size());
-          for (size_t j = 0; j < r.dst_index.size(); ++j) c.dst_ptr[j] = pool[r.dst_index[j] | kDstBit];
+          c.src_ptr = pool(r.src_index);
+          c.n_dst = uint16_t(r.n_dst);
+          for (uint32_t j = 0; j < r.n_dst; ++j) c.dst_ptr[j] = pool(r.dst_index[j] | kDstBit);
           std::memcpy(dstp, &c, sizeof(c));
         }
-        if (bucket != kTiny)
-          for (uint32_t u = 0; u < f.units; ++u) unit_region.push_back(uint32_t(k));
+        if (bucket != kTiny) {
+          // Chunk table: the region of every (1 << kChunkShift)-th unit.
+          const uint64_t first = (uint64_t(ub) + (1u << kChunkShift) - 1) >> kChunkShift;
+          for (uint64_t c = first; (c << kChunkShift) < uint64_t(ub) + f.units; ++c)
+            unit_region.push_back(uint32_t(k));
+        }
         ub += f.units;
 
-        rs_region pub;
-        std::memset(&pub, 0, sizeof(pub));
-        pub.tensor = r.tensor;
-        pub.bucket = bucket;
-        pub.src_index = r.src_index;
-        pub.n_dst = uint32_t(r.dst_index.size());
-        for (size_t j = 0; j < r.dst_index.size(); ++j) {
-          pub.dst_index[j] = r.dst_index[j];
-          if (r.mx) pub.scale_index[j] = r.sc_index[j];
-        }
-        pub.src_off = r.src_off;
-        pub.dst_off = r.dst_off;
-        pub.scale_off = r.sc_off;
-        pub.inner = r.inner;
-        for (int q = 0; q < 3; ++q) {
-          pub.ext[q] = ext[q];
-          pub.src_stride[q] = ss[q];
-          pub.dst_stride[q] = ds[q];
-          pub.scale_stride[q] = sc[q];
-        }
-        pub.scale_inner_stride = r.sc_inner;
-        out.regions.push_back(pub);
+        out.region_tensor.push_back(r.tensor);
       }
       if (bucket == kTiny) {
-        L.n_units = uint32_t((grp.size() + kThreads - 1) / kThreads);
+        L.n_units = uint32_t((batch.size() + kThreads - 1) / kThreads);
         L.units_off = 0;
       } else {
         L.n_units = ub;
+        unit_region.push_back(uint32_t(batch.size() - 1));  // entry for unit n_units - 1
         align_up(out.image, 256);
         L.units_off = out.image.size();
         out.image.resize(out.image.size() + 4 * unit_region.size());
         std::memcpy(out.image.data() + L.units_off, unit_region.data(), 4 * unit_region.size());
       }
-      nreg_bucket[bucket] += grp.size();
+      for (uint32_t k : members) ((k & kDstBit) ? pool_dst[k & ~kDstBit] : pool_src[k]) = -1;
+      nreg_bucket[bucket] += batch.size();
       nunit_bucket[bucket] += L.n_units;
       out.launches.push_back(std::move(L));
     }
@@ -905,8 +969,8 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
   I.n_tensors = uint64_t(n);
   I.n_src_ptrs = n_src_ptrs;
   I.n_dst_ptrs = n_dst_ptrs;
-  I.n_regions = out.regions.size();
-  for (int b = 0; b < kBuckets; ++b) {
+  I.n_regions = out.region_tensor.size();
+  for (uint32_t b = 0; b < kBuckets; ++b) {
     I.n_regions_bucket[b] = nreg_bucket[b];
     I.n_units_bucket[b] = nunit_bucket[b];
   }
@@ -918,6 +982,65 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
                            std::chrono::steady_clock::now() - t0)
                            .count());
   return RS_OK;
+}
+
+rs_status region_info(const PlanData& d, uint64_t index, rs_region* out) {
+  if (index >= d.region_tensor.size()) return RS_ERR_INVALID;
+  uint64_t base = 0;
+  for (const Launch& L : d.launches) {
+    if (index >= base + L.n_regions) {
+      base += L.n_regions;
+      continue;
+    }
+    const uint64_t k = index - base;
+    std::memset(out, 0, sizeof(*out));
+    out->tensor = d.region_tensor[index];
+    out->bucket = L.bucket;
+    auto user = [&](uint16_t slot) { return L.pool[slot] & ~kDstBit; };
+    if (L.bucket == kMx) {
+      MxRegion m;
+      std::memcpy(&m, d.image.data() + L.regions_off + k * sizeof(MxRegion), sizeof(m));
+      out->src_index = user(m.src_ptr);
+      out->n_dst = m.n_dst;
+      for (uint32_t j = 0; j < m.n_dst; ++j) {
+        out->dst_index[j] = user(m.dst_ptr[j]);
+        out->scale_index[j] = user(m.sc_ptr[j]);
+      }
+      out->src_off = m.src_off;
+      out->dst_off = m.dst_off;
+      out->scale_off = m.sc_off;
+      out->inner = m.inner;
+      const uint32_t nouter = m.flags & kFlagOuterMask;
+      const uint64_t e2 = (nouter >= 3) ? uint64_t(m.rows) / (uint64_t(m.e0) * m.e1) : 1;
+      const uint64_t ext[3] = {nouter >= 1 ? m.e0 : 1u, nouter >= 2 ? m.e1 : 1u, e2};
+      for (int q = 0; q < 3; ++q) {
+        out->ext[q] = ext[q];
+        out->src_stride[q] = m.sstr[q];
+        out->dst_stride[q] = m.dstr[q];
+        out->scale_stride[q] = m.scstr[q];
+      }
+      out->scale_inner_stride = m.sc_inner;
+    } else {
+      CopyRegion c;
+      std::memcpy(&c, d.image.data() + L.regions_off + k * sizeof(CopyRegion), sizeof(c));
+      out->src_index = user(c.src_ptr);
+      out->n_dst = c.n_dst;
+      for (uint32_t j = 0; j < c.n_dst; ++j) out->dst_index[j] = user(c.dst_ptr[j]);
+      out->src_off = c.src_off;
+      out->dst_off = c.dst_off;
+      out->inner = c.inner;
+      const uint32_t nouter = c.flags & kFlagOuterMask;
+      const uint64_t e2 = (nouter >= 3) ? uint64_t(c.rows) / (uint64_t(c.e0) * c.e1) : 1;
+      const uint64_t ext[3] = {nouter >= 1 ? c.e0 : 1u, nouter >= 2 ? c.e1 : 1u, e2};
+      for (int q = 0; q < 3; ++q) {
+        out->ext[q] = ext[q];
+        out->src_stride[q] = c.sstr[q];
+        out->dst_stride[q] = c.dstr[q];
+      }
+    }
+    return RS_OK;
+  }
+  return RS_ERR_INVALID;
 }
 
 }  // namespace rs

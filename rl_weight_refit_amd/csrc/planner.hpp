@@ -23,7 +23,7 @@ struct Launch {
 };
 
 struct PlanData {
-  std::vector<rs_region> regions;  // public view, in image order
+  std::vector<uint32_t> region_tensor;  // tensor of each region, in image order
   std::vector<uint8_t> image;      // device tables, uploaded once per device
   std::vector<Launch> launches;
   std::vector<uint8_t> src_used;   // pointer index -> referenced by some region
@@ -38,6 +38,9 @@ struct PlanData {
 // line per violation to `err`.
 rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32_t n,
                      const rs_plan_opts* opts, PlanData& out, std::string& err);
+
+// Public view of region `index` (image order), rebuilt from the device image.
+rs_status region_info(const PlanData& d, uint64_t index, rs_region* out);
 
 // Global box of one slot of a layout.
 rs_status shard_box(const rs_tensor_desc* d, int64_t slot, int64_t* off, int64_t* len,

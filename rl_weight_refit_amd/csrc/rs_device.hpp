@@ -8,10 +8,15 @@
 namespace rs {
 
 constexpr int kThreads = 256;         // threads per workgroup (4 wave64s)
-constexpr int kPool = 240;            // device pointers passed per launch (kernel arguments)
+constexpr int kPool = 320;            // device pointers passed per launch (kernel arguments)
 constexpr int kMaxFan = 16;           // destination replicas per region
 constexpr uint32_t kThinTile = 16384; // LDS tile of the thin bucket, bytes
 constexpr uint32_t kLongRow = 2048;   // bulk rows at least this long are walked row by row
+constexpr uint32_t kChunkShift = 8;   // the unit table holds the region of every 256th unit
+constexpr int kMxUnroll = 2;          // 8-element groups each lane of the MXFP8 kernel loads at once
+// Elements one MXFP8 workgroup loads in one batch; longer rows are split
+// (at block boundaries) so that each work unit is a single batch.
+constexpr uint32_t kMxBatchElems = uint32_t(kThreads) * kMxUnroll * 8;
 
 enum Bucket : uint32_t { kBulk = 0, kThin = 1, kTiny = 2, kMx = 3, kBuckets = 4 };
 
@@ -71,7 +76,9 @@ static_assert(sizeof(MxRegion) == 208, "MxRegion must stay 208 bytes");
 // Kernel arguments of one launch.
 struct LaunchArgs {
   const void* regions;          // CopyRegion[] or MxRegion[]
-  const uint32_t* unit_region;  // work unit -> region index (bulk, thin, mx)
+  // Region of unit min(c << kChunkShift, n_units - 1), for c = 0 ..
+  // ceil(n_units >> kChunkShift) inclusive (bulk, thin, mx; NULL for tiny).
+  const uint32_t* unit_region;
   uint32_t n_regions;
   uint32_t n_units;
   void* ptr[kPool];

@@ -115,6 +115,8 @@ MOE_SMALL = [
     (12, 200, 100, 3, 2, 4),     # ragged: 100 / 4 per TP shard, 200 hidden
     (32, 256, 64, 16, 8, 8),     # the DSV3 meshes at a small size
     (6, 96, 40, 3, 2, 3),        # uneven intermediate split
+    (4, 5000, 64, 2, 2, 2),      # MXFP8 rows split into 4096 + 904 elements (short last block)
+    (2, 8200, 24, 1, 2, 1),      # two full 4096-element segments and an 8-element tail
 ]
 
 
@@ -148,3 +150,34 @@ def test_mxfp8_extreme_values():
         b[rng.random(shape) < 0.001] = 0xFF80
         globals_.append(b)
     gh.check_against_oracle(wl, globals_=globals_)
+
+
+def _all_bf16_orders():
+    """Eight arrangements of all 65536 bf16 bit patterns: in order (blocks of
+    nearby values, including the NaN/Inf range), three seeded shuffles (blocks
+    mixing far-apart binades), and four exponent-windowed shuffles (blocks
+    within about a dozen binades, so small elements land on E4M3 subnormals
+    and zero)."""
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    out = [allb.copy()]
+    rng = np.random.default_rng(12)
+    for _ in range(3):
+        out.append(rng.permutation(allb))
+    order = np.argsort(((allb >> 7) & 0xFF).astype(np.int64) * 65536 + rng.integers(0, 65536, 65536),
+                       kind="stable")
+    by_exp = allb[order]
+    for w in (1024, 2048, 4096, 8192):
+        x = by_exp.copy()
+        for i in range(0, x.size, w):
+            x[i:i + w] = rng.permutation(x[i:i + w])
+        out.append(x)
+    return np.stack(out)
+
+
+def test_mxfp8_every_bf16_pattern():
+    G = _all_bf16_orders().reshape(8, 64, 1024)
+    t = {"name": "allbf16", "shape": [8, 64, 1024], "dtype": "bf16",
+         "src": synth.side([2], [0]), "dst": synth.side([2, 2], [0, 1], quant="mxfp8"),
+         "values": {"kind": "index"}}
+    wl = {"name": "mxfp8_all_bf16", "buffers": {}, "tensors": [t]}
+    gh.check_against_oracle(wl, globals_=[G])
