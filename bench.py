@@ -49,6 +49,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--variant", choices=["both", "copy", "mxfp8"], default="both")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--plan-reps", type=int, default=1000)
     ap.add_argument("--ceiling-bytes", type=int, default=8 << 30)
     return ap.parse_args()
@@ -112,7 +113,18 @@ def device_destinations(torch, binding, wl):
     ptrs = []
     for t in wl["tensors"]:
         d = t["dst"]
-        ptrs += [named[e["buf"]].data_ptr() for e in d["slots"]]
+        if d["slots"] is None:
+            # Dense per-slot buffers, sized by the library's own shard boxes.
+            sp = spec(t, "dst")
+            es = synth.ELEM_BYTES[sp["dtype"]]
+            for k in range(int(np.prod(d["mesh"]))):
+                _, ln = binding.reshard_shard_box(sp, k)
+                key = "%s/%d" % (t["name"], k)
+                named[key] = torch.empty(max(1, int(np.prod(ln)) * es), dtype=torch.uint8,
+                                         device="cuda")
+                ptrs.append(named[key].data_ptr())
+        else:
+            ptrs += [named[e["buf"]].data_ptr() for e in d["slots"]]
         if d.get("quant") == "mxfp8":
             ptrs += [named[e["buf"]].data_ptr() for e in d["scale_slots"]]
     return named, ptrs
@@ -136,6 +148,71 @@ def copy_ceiling(torch, nbytes, stream):
             best = max(best, 2 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
     del a, b
     return best
+
+
+def time_plan(torch, binding, plan, src_ptrs, dst_ptrs, stream, reps=10):
+    """Median event-timed execute of a plan on `stream` (ms)."""
+    for _ in range(2):
+        binding.reshard_execute(plan, src_ptrs, dst_ptrs, stream.cuda_stream)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        a.record(stream)
+        binding.reshard_execute(plan, src_ptrs, dst_ptrs, stream.cuda_stream)
+        b.record(stream)
+    stream.synchronize()
+    return statistics.median(a.elapsed_time(b) for a, b in evs)
+
+
+def secondary(torch, binding, stream):
+    """Other layer-sized layouts and the kernels' special paths, measured
+    after the timed region (not part of `value`)."""
+    from rl_weight_refit_amd import synth
+    out = {}
+    for name, wl in (("dense_ffn_4096x14336_tp4_to_tp2xdp2", synth.dense_ffn()),
+                     ("moe_128e_4096x1536_ep8_to_ep4xtp4", synth.moe_128e())):
+        src = device_sources(torch, binding, wl)
+        sp = [x.data_ptr() for t in src for x in t]
+        named, dp = device_destinations(torch, binding, wl)
+        plan = plan_of(binding, wl)
+        info = plan.info()
+        ms = time_plan(torch, binding, plan, sp, dp, stream)
+        nb = info["bytes_read"] + info["bytes_written"]
+        out[name] = {"ms": round(ms, 4), "GBps": round(nb / ms / 1e6, 1), "bytes": nb,
+                     "bytes_no_fanout": info["bytes_read_no_fanout"] + info["bytes_written"],
+                     "regions": info["n_regions"]}
+        del src, named
+    # Tall-thin column slabs (the worked example's shape at scale): [1048576, 8]
+    # int32, rows split over 2 sources, columns over 4 destinations; each
+    # region is 524,288 rows x 8 bytes.  LDS-staged thin kernel vs the bulk
+    # kernel's direct path (thin bucket disabled).
+    wl = {"name": "slabs", "buffers": {}, "tensors": [
+        {"name": "w", "shape": [1 << 20, 8], "dtype": "i32", "src": synth.side([2], [0]),
+         "dst": synth.side([4], [1]), "values": {"kind": "uniform", "seed": 1}}]}
+    t = wl["tensors"][0]
+    srcs = [torch.empty((1 << 19) * 8 * 4, dtype=torch.uint8, device="cuda").fill_(7) for _ in range(2)]
+    dsts = [torch.empty((1 << 20) * 2 * 4, dtype=torch.uint8, device="cuda") for _ in range(4)]
+    sp = [x.data_ptr() for x in srcs]
+    dp = [x.data_ptr() for x in dsts]
+    slab = {}
+    for label, kw in (("lds_thin_kernel", {}), ("bulk_direct", {"thin_bytes": 1})):
+        plan = binding.reshard_plan([spec(t, "src")], [spec(t, "dst")], **kw)
+        info = plan.info()
+        ms = time_plan(torch, binding, plan, sp, dp, stream)
+        nb = info["bytes_read"] + info["bytes_written"]
+        slab[label] = {"ms": round(ms, 4), "GBps": round(nb / ms / 1e6, 1),
+                       "regions": info["regions"]}
+    out["column_slabs_1Mx8_i32_2row_to_4col"] = slab
+    # Plan time over the 500 uneven layouts (CPU).
+    ns = []
+    for seed in range(500):
+        u = synth.uneven_case(seed)["tensors"][0]
+        p = binding.reshard_plan([spec(u, "src")], [spec(u, "dst")])
+        ns.append(p.info()["plan_ns"])
+        p.destroy()
+    ns.sort()
+    out["uneven_500_plan_us"] = {"p50": ns[250] / 1e3, "p99": ns[494] / 1e3, "max": ns[-1] / 1e3}
+    return out
 
 
 def cpu_baseline():
@@ -308,6 +385,10 @@ def main():
     }
     del src, d_copy, d_mx
     torch.cuda.empty_cache()
+    if not args.no_secondary:
+        print("secondary workloads ...", file=sys.stderr, flush=True)
+        out["secondary"] = secondary(torch, binding, stream)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("cpu baseline ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline()

@@ -28,9 +28,14 @@ def _cuda():
     yield
 
 
-def test_worked_example():
-    gh.log("worked 8x8")
-    gh.check_against_oracle(synth.worked_example())
+@pytest.mark.parametrize("kw,bucket", [({}, "tiny"), ({"tiny_bytes": 0}, "thin"),
+                                       ({"tiny_bytes": 0, "thin_bytes": 1}, "bulk")])
+def test_worked_example(kw, bucket):
+    """The 8x8 example through each kernel: the wave-prefix-sum tiny kernel,
+    the LDS-staged thin kernel (8-byte column slabs) and the bulk kernel."""
+    gh.log("worked 8x8 via %s" % bucket)
+    plan = gh.check_against_oracle(synth.worked_example(), **kw)
+    assert plan.info()["regions"][bucket] == 8
 
 
 @pytest.mark.parametrize("seed", range(200))

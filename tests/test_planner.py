@@ -62,6 +62,14 @@ def test_worked_example_regions():
     assert seen == {(k, s) for k in range(4) for s in range(2)}
 
 
+@pytest.mark.parametrize("kw,bucket", [({}, "tiny"), ({"tiny_bytes": 0}, "thin"),
+                                       ({"tiny_bytes": 0, "thin_bytes": 1}, "bulk")])
+def test_worked_example_bucket(kw, bucket):
+    """The 8x8 example's 4 x 8-byte regions land in the bucket the options ask for."""
+    plan = lh.plan_workload(synth.worked_example(), **kw)
+    assert plan.info()["regions"][bucket] == 8
+
+
 def run_interpreted(wl, **kw):
     G, sources, named, per = helpers.golden_workload(wl, poison=0xA5)
     _, per2 = None, None
