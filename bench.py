@@ -65,7 +65,8 @@ def spec(tensor, side_name):
             "views": None if s["slots"] is None else [e["view"] for e in s["slots"]],
             "quant": s.get("quant") if side_name == "dst" else None,
             "scale_views": None if s.get("scale_slots") is None
-            else [e["view"] for e in s["scale_slots"]]}
+            else [e["view"] for e in s["scale_slots"]],
+            "split0": s.get("split0", False)}
 
 
 def plan_of(binding, wl):
@@ -99,7 +100,11 @@ def device_sources(torch, binding, wl):
         for k in range(nslots):
             off, ln = binding.reshard_shard_box(sp, k)
             sl = tuple(slice(o, o + n) for o, n in zip(off, ln))
-            shards.append(G[sl].contiguous())
+            if t["src"].get("split0"):
+                part = G[sl]
+                shards += [part[i].contiguous() for i in range(ln[0])]   # one buffer per expert
+            else:
+                shards.append(G[sl].contiguous())
         del G
         out.append(shards)
     torch.cuda.synchronize()
@@ -182,6 +187,41 @@ def secondary(torch, binding, stream):
                      "bytes_no_fanout": info["bytes_read_no_fanout"] + info["bytes_written"],
                      "regions": info["n_regions"]}
         del src, named
+    # The DSV3 layer with every source expert in a buffer of its own (no
+    # stacking copy on the training side): 768 source pointers.
+    wl = synth.moe_dsv3(src_split=True)
+    src = device_sources(torch, binding, wl)
+    sp = [x.data_ptr() for t in src for x in t]
+    named, dp = device_destinations(torch, binding, wl)
+    plan = plan_of(binding, wl)
+    info = plan.info()
+    ms = time_plan(torch, binding, plan, sp, dp, stream)
+    nb = info["bytes_read"] + info["bytes_written"]
+    out["moe_dsv3_per_expert_sources"] = {"ms": round(ms, 4), "GBps": round(nb / ms / 1e6, 1),
+                                          "bytes": nb, "regions": info["n_regions"],
+                                          "launches": info["n_launches"],
+                                          "plan_us": info["plan_ns"] / 1e3}
+    del src, named
+    torch.cuda.empty_cache()
+    # Misc-path packing: 61 layers of small tensors into one buffer, and back.
+    wl = synth.misc_pack()
+    for label, w in (("misc_pack_61layers", wl), ("misc_unpack_61layers", synth.reverse(wl))):
+        if label.startswith("misc_pack"):
+            src = device_sources(torch, binding, w)
+            sp = [x.data_ptr() for t in src for x in t]
+            named, dp = device_destinations(torch, binding, w)
+        else:
+            pack = named["pack"]
+            sp = [pack.data_ptr()] * len(w["tensors"])
+            named2, dp = device_destinations(torch, binding, w)
+        plan = plan_of(binding, w)
+        info = plan.info()
+        ms = time_plan(torch, binding, plan, sp, dp, stream)
+        nb = info["bytes_read"] + info["bytes_written"]
+        out[label] = {"ms": round(ms, 4), "GBps": round(nb / ms / 1e6, 1), "bytes": nb,
+                      "tensors": info["n_tensors"], "regions": info["regions"],
+                      "launches": info["n_launches"], "plan_us": info["plan_ns"] / 1e3}
+    del src, named, named2
     # Tall-thin column slabs (the worked example's shape at scale): [1048576, 8]
     # int32, rows split over 2 sources, columns over 4 destinations; each
     # region is 524,288 rows x 8 bytes.  LDS-staged thin kernel vs the bulk

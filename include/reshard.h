@@ -116,6 +116,15 @@ typedef struct rs_tensor_desc {
   /* MXFP8 destinations: per-slot views of the scale buffers, over the local
    * shape with the last extent replaced by ceil(last / 32).  NULL = dense. */
   const rs_view* scale_views;
+  /* 0: each slot is one buffer.  1: each slot's shard is held as separate
+   * buffers, one per local index along tensor dim 0 (for example one buffer
+   * per expert of a grouped [E, ...] weight, as a training side holds them
+   * before stacking; "NCCL Reshard Refit (Experimental)", "Execution Flow:
+   * Setup Time", the grouped-expert pre hook).  The slot then takes one
+   * pointer per local dim-0 index, in order, in the pointer array, and its
+   * view describes each part (strides[0] is ignored; base applies to every
+   * part).  An MXFP8 destination splits its scale buffers the same way. */
+  int32_t split_dim0;
 } rs_tensor_desc;
 
 /* Planning options.  Pass NULL for the defaults. */
@@ -183,11 +192,13 @@ rs_status reshard_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int
 
 /* Run a plan on `stream` (a hipStream_t; NULL = the default stream).
  * src_ptrs: device pointers of the source buffers, tensor by tensor, slot by
- *   slot (tensor 0 slots 0..M0-1, then tensor 1, ...).
+ *   slot (tensor 0 slots 0..M0-1, then tensor 1, ...); a split_dim0 side has
+ *   one pointer per local dim-0 index of each slot instead (slot by slot).
  * dst_ptrs: device pointers of the destination buffers, tensor by tensor:
- *   N_t element buffers in slot order, and for MXFP8 tensors N_t scale
- *   buffers right after them.  Fused destinations pass the same pointer for
- *   several tensors (their views differ).
+ *   the element buffers in slot order (per part for split_dim0), and for
+ *   MXFP8 tensors as many scale buffers right after them.  Fused
+ *   destinations pass the same pointer for several tensors (their views
+ *   differ).  rs_plan_info gives the expected counts.
  * Both arrays are host arrays, read before the call returns; the buffers
  * are owned by the caller and must stay alive until the work on `stream`
  * completes.  Sources and destinations must not overlap.

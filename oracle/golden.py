@@ -11,6 +11,9 @@ there) must give the same destination bytes.
 Buffers are host byte images (numpy uint8).  A shard lives in its buffer
 through a view: (base, strides), both in elements of the tensor's dtype;
 None means a dense row-major array of the shard's local shape at offset 0.
+A shard may instead be held as "parts", one buffer per index of its first
+dimension (per expert, say); the view then describes every part, with the
+first stride unused.
 The copy is bitwise: elements are handled as unsigned integers of the same
 width, so NaN payloads and signed zeros survive.
 
@@ -65,6 +68,34 @@ def view_array(buf, esize, view, lengths, writeable=False):
                       writeable=writeable)
 
 
+def _part_view(view):
+    """View of one part of a shard held as one buffer per dim-0 index: the
+    same base, the strides of dims 1.. (None stays dense)."""
+    if view is None:
+        return None
+    return view[0], list(view[1])[1:]
+
+
+def read_shard(entry, esize, lengths, buf_key="buf", parts_key="parts", view_key="view"):
+    """The local array of a shard from its buffer (or from its parts)."""
+    if parts_key in entry:
+        out = np.zeros(lengths, dtype=UINT[esize])
+        for i0, part in enumerate(entry[parts_key]):
+            out[i0] = view_array(part, esize, _part_view(entry.get(view_key)), lengths[1:])
+        return out
+    return view_array(entry[buf_key], esize, entry.get(view_key), lengths)
+
+
+def write_shard(entry, esize, lengths, V, buf_key="buf", parts_key="parts", view_key="view"):
+    """Write the local array V of a shard through its view (or into its parts)."""
+    if parts_key in entry:
+        for i0, part in enumerate(entry[parts_key]):
+            view_array(part, esize, _part_view(entry.get(view_key)), lengths[1:],
+                       writeable=True)[...] = V[i0]
+        return
+    view_array(entry[buf_key], esize, entry.get(view_key), lengths, writeable=True)[...] = V
+
+
 def box_slices(box):
     off, ln = box
     return tuple(slice(o, o + n) for o, n in zip(off, ln))
@@ -83,7 +114,7 @@ def assemble(src_desc, esize, src_bufs):
     for s, box in enumerate(layout.slot_boxes(src_desc)):
         if layout.box_volume(box) == 0:
             continue
-        part = view_array(src_bufs[s]["buf"], esize, src_bufs[s].get("view"), box[1])
+        part = read_shard(src_bufs[s], esize, box[1])
         sl = box_slices(box)
         prev = seen[sl]
         if prev.any() and not np.array_equal(G[sl][prev], part[prev]):
@@ -116,20 +147,15 @@ def reshard(src_desc, dst_desc, src_bufs, dst_bufs):
         if quant is None:
             if ELEM_BYTES[dst_desc["dtype"]] != esize:
                 raise ValueError("element sizes differ")
-            out = view_array(dst_bufs[k]["buf"], esize, dst_bufs[k].get("view"), ln,
-                             writeable=True)
-            out[...] = V
+            write_shard(dst_bufs[k], esize, ln, V)
         elif quant == "mxfp8":
             if src_desc["dtype"] != "bf16":
                 raise ValueError("mxfp8 install needs a bf16 source")
             codes, scales = mxfp8.quantize(V)
-            out = view_array(dst_bufs[k]["buf"], 1, dst_bufs[k].get("view"), ln,
-                             writeable=True)
-            out[...] = codes
+            write_shard(dst_bufs[k], 1, ln, codes)
             sln = list(ln[:-1]) + [-(-ln[-1] // mxfp8.BLOCK)]
-            so = view_array(dst_bufs[k]["scale_buf"], 1, dst_bufs[k].get("scale_view"),
-                            sln, writeable=True)
-            so[...] = scales
+            write_shard(dst_bufs[k], 1, sln, scales, buf_key="scale_buf",
+                        parts_key="scale_parts", view_key="scale_view")
         else:
             raise ValueError("unknown quant mode %r" % (quant,))
 

@@ -10,7 +10,7 @@ A side description is a dict:
   shape, dtype ("u8", "bf16", "f32", ...), mesh, placements (d >= 0 Shard(d),
   -1 Replicate), and optionally slot_of_coord, views (per slot (base,
   strides) in elements, or None for all-dense), quant ("mxfp8" on a
-  destination) and scale_views.
+  destination), scale_views and split0 (one buffer per local dim-0 index).
 """
 
 import ctypes
@@ -42,7 +42,8 @@ class TensorDesc(ctypes.Structure):
                 ("mesh_ndim", c_i32), ("placements", c_i32 * RS_MAX_MESH),
                 ("mesh_shape", c_i64 * RS_MAX_MESH),
                 ("slot_of_coord", ctypes.POINTER(c_i32)), ("views", ctypes.POINTER(View)),
-                ("quant", c_i32), ("scale_views", ctypes.POINTER(View))]
+                ("quant", c_i32), ("scale_views", ctypes.POINTER(View)),
+                ("split_dim0", c_i32)]
 
 
 class PlanOpts(ctypes.Structure):
@@ -145,6 +146,7 @@ def make_desc(spec):
         keep.append(v)
         d.views = ctypes.cast(v, ctypes.POINTER(View))
     d.quant = QUANT[spec.get("quant")]
+    d.split_dim0 = 1 if spec.get("split0") else 0
     sv = _views(spec.get("scale_views"), d.ndim)
     if sv is not None:
         keep.append(sv)

@@ -86,6 +86,9 @@ struct Layout {
   std::vector<Interval> iv[RS_MAX_DIMS];    // interval index -> interval
   std::vector<int> rep_md;                  // Replicate mesh dims, in order
   int64_t nrep = 1;
+  bool split = false;                       // one buffer per local dim-0 index
+  std::vector<int64_t> ptr_base;            // slot -> first pointer index of the side
+  int64_t nptrs = 0;                        // pointers the side takes
   std::vector<rs_view> views;               // resolved per slot
   std::vector<rs_view> scale_views;         // MXFP8 destinations
   std::vector<Interval> box;                // slot * ndim + d
@@ -215,6 +218,18 @@ bool parse_layout(const rs_tensor_desc* d, const char* side, int t, bool is_dst,
     }
   }
 
+  if (d->split_dim0 != 0 && d->split_dim0 != 1)
+    E.add(&E.invalid, "tensor ", t, " ", side, ": split_dim0 = ", d->split_dim0, " is not 0 or 1");
+  L.split = d->split_dim0 == 1;
+  if (L.split && L.quant == RS_Q_MXFP8_E4M3 && L.ndim < 2)
+    E.add(&E.unsupported, "tensor ", t, " ", side,
+          ": a split MXFP8 destination needs at least 2 dims (blocks run along the last dim)");
+  L.ptr_base.resize(L.nslots);
+  L.nptrs = 0;
+  for (int64_t s = 0; s < L.nslots; ++s) {
+    L.ptr_base[s] = L.nptrs;
+    L.nptrs += L.split ? L.slot_box(s)[0].len : 1;
+  }
   L.views.resize(L.nslots);
   for (int64_t s = 0; s < L.nslots; ++s) {
     if (d->views) {
@@ -558,11 +573,11 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
   }
   for (int t = 0; t < n; ++t) {
     src_base[t] = n_src_ptrs;
-    n_src_ptrs += S[t].nslots;
+    n_src_ptrs += S[t].nptrs;
     dst_base[t] = n_dst_ptrs;
-    n_dst_ptrs += D[t].nslots;
+    n_dst_ptrs += D[t].nptrs;
     sc_base[t] = n_dst_ptrs;
-    if (D[t].quant == RS_Q_MXFP8_E4M3) n_dst_ptrs += D[t].nslots;
+    if (D[t].quant == RS_Q_MXFP8_E4M3) n_dst_ptrs += D[t].nptrs;
   }
   if (E.status() != RS_OK) {
     err = E.text.str();
@@ -606,7 +621,7 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
     }
     if (empty) continue;
     if (mx) {
-      for (int64_t s = 0; s < A.nslots; ++s) out.src_align[src_base[t] + s] = 2;
+      for (int64_t s = 0; s < A.nptrs; ++s) out.src_align[src_base[t] + s] = 2;
     }
     size_t odo[RS_MAX_DIMS] = {};
     while (true) {
@@ -652,70 +667,86 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
         const Interval* db = B.slot_box(ds0);
         const rs_view& sv = A.views[ss];
         const rs_view& dv = B.views[ds0];
-        Raw r;
-        r.tensor = t;
-        r.mx = mx;
-        r.src_index = uint32_t(src_base[t] + ss);
-        r.n_dst = 0;
-        for (size_t g : grp) {
-          r.dst_index[r.n_dst] = uint32_t(dst_base[t] + targets[g].dslot);
-          r.sc_index[r.n_dst] = mx ? uint32_t(sc_base[t] + targets[g].dslot) : 0;
-          ++r.n_dst;
-        }
-        int64_t so = sv.base, dof = dv.base, sco = 0;
-        for (int dd = 0; dd < nd; ++dd) {
-          so += (start[dd] - sb[dd].start) * sv.strides[dd];
-          dof += (start[dd] - db[dd].start) * dv.strides[dd];
-        }
-        if (!mx) {
-          const uint64_t es = A.esize;
-          r.src_off = uint64_t(so) * es;
-          r.dst_off = uint64_t(dof) * es;
-          r.sc_off = 0;
-          r.sc_inner = 0;
-          // Element size folds into the innermost run; runs grow while both
-          // sides stay contiguous.
-          Dims keep;
-          for (int dd = 0; dd < nd; ++dd)
-            if (len[dd] != 1)
-              keep.push_back({uint64_t(len[dd]), uint64_t(sv.strides[dd]) * es,
-                              uint64_t(dv.strides[dd]) * es, 0});
-          uint64_t run = es;
-          while (!keep.empty() && keep.back().ss == run && keep.back().ds == run) {
-            run *= keep.back().ext;
-            keep.pop_back();
+        // A side held as one buffer per dim-0 index takes one region per
+        // index of the box along dim 0 (the dim-0 offset picks the buffer).
+        const bool split = A.split || B.split;
+        const int64_t nparts = split ? len[0] : 1;
+        for (int64_t p0 = 0; p0 < nparts; ++p0) {
+          int64_t st[RS_MAX_DIMS], ln[RS_MAX_DIMS];
+          for (int dd = 0; dd < nd; ++dd) {
+            st[dd] = start[dd];
+            ln[dd] = len[dd];
           }
-          r.inner = run;
-          r.outer = keep;
-          merge_outer(r.outer, false);
-        } else {
-          const rs_view& cv = B.scale_views[ds0];
-          const int last = nd - 1;
-          const int64_t c0 = start[last] - db[last].start;
-          const int64_t kloc = db[last].len;
-          const int64_t c1 = c0 + len[last];
-          if (c0 % kMxBlock != 0 || (c1 % kMxBlock != 0 && c1 != kloc)) {
-            E.add(&E.unsupported, "tensor ", t, ": an MXFP8 block of destination slot ", ds0,
-                  " would span two source shards (columns ", c0, "..", c1,
-                  " of its last dim); block-aligned source splits are required");
+          if (split) {
+            st[0] = start[0] + p0;
+            ln[0] = 1;
           }
-          if ((sv.strides[last] != 1 && len[last] > 1) || (dv.strides[last] != 1 && len[last] > 1))
-            E.add(&E.unsupported, "tensor ", t,
-                  ": MXFP8 install needs a contiguous last dim on both sides");
-          for (int dd = 0; dd < last; ++dd)
-            sco += (start[dd] - db[dd].start) * cv.strides[dd];
-          sco += cv.base + (c0 / kMxBlock) * cv.strides[last];
-          r.src_off = uint64_t(so) * 2;
-          r.dst_off = uint64_t(dof);
-          r.sc_off = uint64_t(sco);
-          r.inner = uint64_t(len[last]);
-          r.sc_inner = uint64_t(cv.strides[last]);
-          for (int dd = 0; dd < last; ++dd)
-            r.outer.push_back({uint64_t(len[dd]), uint64_t(sv.strides[dd]) * 2,
-                               uint64_t(dv.strides[dd]), uint64_t(cv.strides[dd])});
-          merge_outer(r.outer, true);
+          const int64_t s0 = st[0] - sb[0].start, d0 = st[0] - db[0].start;
+          Raw r;
+          r.tensor = t;
+          r.mx = mx;
+          r.src_index = uint32_t(src_base[t] + (A.split ? A.ptr_base[ss] + s0 : ss));
+          r.n_dst = 0;
+          for (size_t g : grp) {
+            const int64_t dk = targets[g].dslot;
+            const int64_t part = B.split ? B.ptr_base[dk] + d0 : dk;
+            r.dst_index[r.n_dst] = uint32_t(dst_base[t] + part);
+            r.sc_index[r.n_dst] = mx ? uint32_t(sc_base[t] + part) : 0;
+            ++r.n_dst;
+          }
+          int64_t so = sv.base, dof = dv.base, sco = 0;
+          for (int dd = A.split ? 1 : 0; dd < nd; ++dd) so += (st[dd] - sb[dd].start) * sv.strides[dd];
+          for (int dd = B.split ? 1 : 0; dd < nd; ++dd) dof += (st[dd] - db[dd].start) * dv.strides[dd];
+          if (!mx) {
+            const uint64_t es = A.esize;
+            r.src_off = uint64_t(so) * es;
+            r.dst_off = uint64_t(dof) * es;
+            r.sc_off = 0;
+            r.sc_inner = 0;
+            // Element size folds into the innermost run; runs grow while both
+            // sides stay contiguous.
+            Dims keep;
+            for (int dd = 0; dd < nd; ++dd)
+              if (ln[dd] != 1)
+                keep.push_back({uint64_t(ln[dd]), uint64_t(sv.strides[dd]) * es,
+                                uint64_t(dv.strides[dd]) * es, 0});
+            uint64_t run = es;
+            while (!keep.empty() && keep.back().ss == run && keep.back().ds == run) {
+              run *= keep.back().ext;
+              keep.pop_back();
+            }
+            r.inner = run;
+            r.outer = keep;
+            merge_outer(r.outer, false);
+          } else {
+            const rs_view& cv = B.scale_views[ds0];
+            const int last = nd - 1;
+            const int64_t c0 = st[last] - db[last].start;
+            const int64_t kloc = db[last].len;
+            const int64_t c1 = c0 + ln[last];
+            if (c0 % kMxBlock != 0 || (c1 % kMxBlock != 0 && c1 != kloc)) {
+              E.add(&E.unsupported, "tensor ", t, ": an MXFP8 block of destination slot ", ds0,
+                    " would span two source shards or parts (columns ", c0, "..", c1,
+                    " of its last dim); block-aligned splits are required");
+            }
+            if ((sv.strides[last] != 1 && ln[last] > 1) || (dv.strides[last] != 1 && ln[last] > 1))
+              E.add(&E.unsupported, "tensor ", t,
+                    ": MXFP8 install needs a contiguous last dim on both sides");
+            for (int dd = B.split ? 1 : 0; dd < last; ++dd)
+              sco += (st[dd] - db[dd].start) * cv.strides[dd];
+            sco += cv.base + (c0 / kMxBlock) * cv.strides[last];
+            r.src_off = uint64_t(so) * 2;
+            r.dst_off = uint64_t(dof);
+            r.sc_off = uint64_t(sco);
+            r.inner = uint64_t(ln[last]);
+            r.sc_inner = uint64_t(cv.strides[last]);
+            for (int dd = 0; dd < last; ++dd)
+              r.outer.push_back({uint64_t(ln[dd]), uint64_t(sv.strides[dd]) * 2,
+                                 uint64_t(dv.strides[dd]), uint64_t(cv.strides[dd])});
+            merge_outer(r.outer, true);
+          }
+          raws.push_back(std::move(r));
         }
-        raws.push_back(std::move(r));
       }
       int dd = nd - 1;
       while (dd >= 0 && ++odo[dd] == pieces[dd].size()) odo[dd--] = 0;

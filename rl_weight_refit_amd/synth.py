@@ -39,10 +39,11 @@ ELEM_BYTES = {"u8": 1, "u16": 2, "bf16": 2, "f16": 2, "i16": 2,
               "i32": 4, "u32": 4, "f32": 4, "i64": 8, "u64": 8, "f64": 8}
 
 
-def side(mesh, placements, slots=None, slot_of_coord=None, quant=None, scale_slots=None):
+def side(mesh, placements, slots=None, slot_of_coord=None, quant=None, scale_slots=None,
+         split0=False):
     return {"mesh": list(mesh), "placements": list(placements),
             "slot_of_coord": slot_of_coord, "slots": slots,
-            "quant": quant, "scale_slots": scale_slots}
+            "quant": quant, "scale_slots": scale_slots, "split0": split0}
 
 
 def _row_major(shape):
@@ -168,7 +169,8 @@ def dense_ffn(hidden=4096, inter=14336, src_tp=4, dst_tp=2, dst_dp=2, seed=1):
             ]}
 
 
-def moe_experts(experts, hidden, inter, src_ep, dst_ep, dst_tp, seed, quant=None):
+def moe_experts(experts, hidden, inter, src_ep, dst_ep, dst_tp, seed, quant=None,
+                src_split=False):
     """Grouped MoE experts: gate/up [E,I,H], down [E,H,I]; source EP Shard(0)
     on the expert dim; destination mesh [EP, TP] with experts Shard(0) and the
     intermediate dim sharded on TP.  Per destination slot, gate and up share
@@ -176,7 +178,10 @@ def moe_experts(experts, hidden, inter, src_ep, dst_ep, dst_tp, seed, quant=None
     w2 buffer [ceil(E/EP), H, ceil(I/TP)].
 
     quant="mxfp8": destinations hold E4M3 bytes, plus u8 scale buffers
-    [.., ceil(K/32)] along each destination's last dim."""
+    [.., ceil(K/32)] along each destination's last dim.
+
+    src_split=True: every source expert is a buffer of its own (the training
+    side's per-expert weights, before any stacking)."""
     el = -(-experts // dst_ep)
     ip = -(-inter // dst_tp)
     ndst = dst_ep * dst_tp
@@ -204,20 +209,21 @@ def moe_experts(experts, hidden, inter, src_ep, dst_ep, dst_tp, seed, quant=None
         sd = [{"buf": "s2/%d" % k, "view": (0, s2)} for k in range(ndst)]
     vals = lambda i: {"kind": "normal", "std": 0.02, "seed": seed * 1000 + i}
     mesh = [dst_ep, dst_tp]
-    name = "moe_e%d_h%d_i%d_ep%d_to_ep%dxtp%d%s" % (experts, hidden, inter, src_ep, dst_ep,
-                                                      dst_tp, "_mxfp8" if quant else "")
+    name = "moe_e%d_h%d_i%d_ep%d_to_ep%dxtp%d%s%s" % (experts, hidden, inter, src_ep, dst_ep,
+                                                        dst_tp, "_mxfp8" if quant else "",
+                                                        "_per_expert_src" if src_split else "")
     return {"name": name, "buffers": bufs,
             "tensors": [
                 {"name": "gate", "shape": [experts, inter, hidden], "dtype": "bf16",
-                 "src": side([src_ep], [0]),
+                 "src": side([src_ep], [0], split0=src_split),
                  "dst": side(mesh, [0, 1], gate, quant=quant, scale_slots=sg),
                  "values": vals(0)},
                 {"name": "up", "shape": [experts, inter, hidden], "dtype": "bf16",
-                 "src": side([src_ep], [0]),
+                 "src": side([src_ep], [0], split0=src_split),
                  "dst": side(mesh, [0, 1], up, quant=quant, scale_slots=su),
                  "values": vals(1)},
                 {"name": "down", "shape": [experts, hidden, inter], "dtype": "bf16",
-                 "src": side([src_ep], [0]),
+                 "src": side([src_ep], [0], split0=src_split),
                  "dst": side(mesh, [0, 2], down, quant=quant, scale_slots=sd),
                  "values": vals(2)},
             ]}
@@ -228,11 +234,49 @@ def moe_128e(quant=None):
     return moe_experts(128, 4096, 1536, 8, 4, 4, seed=2, quant=quant)
 
 
-def moe_dsv3(quant=None):
+def moe_dsv3(quant=None, src_split=False):
     """DeepSeek-V3-shaped MoE layer: 256 experts, hidden 7168, expert
     intermediate 2048 (gate + up + down = 22,548,578,304 bytes of bf16):
     EP16 -> EP8 x TP8."""
-    return moe_experts(256, 7168, 2048, 16, 8, 8, seed=5, quant=quant)
+    return moe_experts(256, 7168, 2048, 16, 8, 8, seed=5, quant=quant, src_split=src_split)
+
+
+# ---------------------------------------------------------------------------
+# Misc-path packing: many small tensors into one contiguous buffer.
+# ---------------------------------------------------------------------------
+
+def misc_pack(layers=61, hidden=7168, q_rank=1536, kv_rank=512, experts=256, src_tp=4, seed=7,
+              align=16):
+    """The small per-layer tensors of a DeepSeek-V3-shaped model packed into
+    one buffer, each at a running offset (aligned to `align` bytes): two
+    RMSNorm weights [hidden], the q / kv low-rank norms [q_rank], [kv_rank]
+    (bf16, replicated over the source TP ranks), the MoE router
+    [experts, hidden] (bf16, row-sharded over TP) and its correction bias
+    [experts] (f32, replicated).  The destination of every tensor is the one
+    slot of mesh [1], viewed into the shared "pack" buffer."""
+    specs = []
+    for l in range(layers):
+        specs += [("l%d.input_norm" % l, [hidden], "bf16", R),
+                  ("l%d.post_attn_norm" % l, [hidden], "bf16", R),
+                  ("l%d.q_a_norm" % l, [q_rank], "bf16", R),
+                  ("l%d.kv_a_norm" % l, [kv_rank], "bf16", R),
+                  ("l%d.router" % l, [experts, hidden], "bf16", 0),
+                  ("l%d.router_bias" % l, [experts], "f32", R)]
+    tensors, off = [], 0
+    for i, (name, shape, dt, pl) in enumerate(specs):
+        es = ELEM_BYTES[dt]
+        off = -(-off // align) * align
+        view = (off // es, _row_major(shape))
+        kind = {"kind": "normal", "std": 0.02, "seed": seed * 100000 + i} if dt == "bf16" else \
+            {"kind": "uniform", "seed": seed * 100000 + i}
+        tensors.append({"name": name, "shape": shape, "dtype": dt,
+                        "src": side([src_tp], [pl]),
+                        "dst": side([1], [R], [{"buf": "pack", "view": view}]),
+                        "values": kind})
+        off += _prod(shape) * es
+    return {"name": "misc_pack_%dlayers" % layers,
+            "buffers": {"pack": {"dtype": "u8", "elems": -(-off // align) * align}},
+            "tensors": tensors}
 
 
 # ---------------------------------------------------------------------------

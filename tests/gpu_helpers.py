@@ -62,8 +62,15 @@ def device_run(workload, sources, per_tensor_dst_host, poison=0xA5, src_shift=0,
     images, execute the HIP path, return the device buffers in pointer order.
     """
     src_dev = []
+    src_seen = {}
     for t_src in sources:
-        src_dev.append([DevBuf(e["buf"].size, data=e["buf"], shift=src_shift) for e in t_src])
+        row = []
+        for e in t_src:
+            for hb in (e["parts"] if "parts" in e else [e["buf"]]):
+                if id(hb) not in src_seen:   # shared (packed) source buffers upload once
+                    src_seen[id(hb)] = DevBuf(hb.size, data=hb, shift=src_shift)
+                row.append(src_seen[id(hb)])
+        src_dev.append(row)
     # Shared (fused) buffers are the same numpy object in the host images.
     seen = {}
     dst_ptrs = []
@@ -109,6 +116,7 @@ def check_against_oracle(workload, poison=0xA5, src_shift=0, dst_shift=0, global
                                     host_img[bad[0]]))
         assert dev.guard_ok(), "%s: guard bytes overwritten" % workload["name"]
     for t_src, t_dev in zip(sources, src_dev):
-        for e, d in zip(t_src, t_dev):
-            assert np.array_equal(d.host(), e["buf"]), "source modified"
+        host = [hb for e in t_src for hb in (e["parts"] if "parts" in e else [e["buf"]])]
+        for hb, d in zip(host, t_dev):
+            assert np.array_equal(d.host(), hb), "source modified"
     return plan

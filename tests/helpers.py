@@ -35,14 +35,39 @@ def dense_bytes(arr):
     return np.ascontiguousarray(arr).view(np.uint8).reshape(-1)
 
 
-def source_buffers(tensor, G):
-    """Per source slot: dense byte image of the slot's shard (oracle boxes)."""
+def source_buffers(tensor, G, named_src=None):
+    """Per source slot: the byte image holding the slot's shard (oracle
+    boxes).  Dense slots get a buffer of their own; slots with views are
+    written through the view into the shared buffer named_src[key]."""
     desc = src_desc_for(tensor)
+    s = tensor["src"]
     out = []
-    for box in olayout.slot_boxes(desc):
+    for k, box in enumerate(olayout.slot_boxes(desc)):
         part = G[ogolden.box_slices(box)]
-        out.append({"buf": dense_bytes(part).copy(), "view": None})
+        if s.get("split0"):
+            out.append({"parts": [dense_bytes(part[i]).copy() for i in range(part.shape[0])],
+                        "view": None})
+        elif s["slots"] is None:
+            out.append({"buf": dense_bytes(part).copy(), "view": None})
+        else:
+            e = s["slots"][k]
+            buf = named_src[e["buf"]]
+            if part.size:
+                ogolden.view_array(buf, synth.ELEM_BYTES[tensor["dtype"]], e["view"], list(part.shape),
+                                   writeable=True)[...] = part
+            out.append({"buf": buf, "view": e["view"]})
     return out
+
+
+def alloc_sources(workload):
+    """Zeroed images of every named buffer some tensor reads through a view."""
+    keys = set()
+    for t in workload["tensors"]:
+        if t["src"]["slots"] is not None:
+            keys |= {e["buf"] for e in t["src"]["slots"]}
+    return {k: np.zeros(workload["buffers"][k]["elems"] *
+                        synth.ELEM_BYTES[workload["buffers"][k]["dtype"]], dtype=np.uint8)
+            for k in sorted(keys)}
 
 
 def alloc_destinations(workload, poison=0xA5):
@@ -91,7 +116,8 @@ def golden_workload(workload, poison=0xA5, globals_=None):
     """
     if globals_ is None:
         globals_ = [synth.host_values(t) for t in workload["tensors"]]
-    sources = [source_buffers(t, G) for t, G in zip(workload["tensors"], globals_)]
+    named_src = alloc_sources(workload)
+    sources = [source_buffers(t, G, named_src) for t, G in zip(workload["tensors"], globals_)]
     named, per_tensor = alloc_destinations(workload, poison)
     for t, src, dst in zip(workload["tensors"], sources, per_tensor):
         ogolden.reshard(src_desc_for(t), odesc(t, "dst"), src, dst)

@@ -23,7 +23,7 @@ def spec(tensor, side_name):
     return {"shape": tensor["shape"], "dtype": dtype, "mesh": s["mesh"],
             "placements": s["placements"], "slot_of_coord": s.get("slot_of_coord"),
             "views": views, "quant": s.get("quant") if side_name == "dst" else None,
-            "scale_views": sviews}
+            "scale_views": sviews, "split0": s.get("split0", False)}
 
 
 def plan_workload(workload, **kw):
@@ -37,10 +37,13 @@ def flat_lists(workload, sources, per_tensor_dst):
     tensor (element buffers, then scale buffers for MXFP8 tensors)."""
     src_flat, dst_flat = [], []
     for t, src, dst in zip(workload["tensors"], sources, per_tensor_dst):
-        src_flat += [e["buf"] for e in src]
-        dst_flat += [e["buf"] for e in dst]
+        for e in src:
+            src_flat += e["parts"] if "parts" in e else [e["buf"]]
+        for e in dst:
+            dst_flat += e["parts"] if "parts" in e else [e["buf"]]
         if t["dst"].get("quant") == "mxfp8":
-            dst_flat += [e["scale_buf"] for e in dst]
+            for e in dst:
+                dst_flat += e["scale_parts"] if "scale_parts" in e else [e["scale_buf"]]
     return src_flat, dst_flat
 
 

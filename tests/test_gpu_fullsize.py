@@ -44,7 +44,8 @@ def dense_strides(lengths):
 
 def build(wl):
     """Device sources (cut from seeded device-generated globals with the
-    oracle's boxes) and poisoned destinations."""
+    oracle's boxes; one buffer per expert for split sources) and poisoned
+    destinations."""
     dev = torch.device("cuda")
     src = []
     for t in wl["tensors"]:
@@ -52,7 +53,10 @@ def build(wl):
         shards = []
         for off, ln in olayout.slot_boxes(helpers.src_desc_for(t)):
             sl = tuple(slice(o, o + n) for o, n in zip(off, ln))
-            shards.append(G[sl].contiguous())
+            if t["src"].get("split0"):
+                shards.append([G[o0].contiguous() for o0 in range(off[0], off[0] + ln[0])])
+            else:
+                shards.append(G[sl].contiguous())
         del G
         src.append(shards)
     torch.cuda.synchronize()
@@ -84,7 +88,8 @@ def build(wl):
 def run(wl):
     src, named, dst_bufs, dst_ptrs = build(wl)
     plan = lh.plan_workload(wl)
-    src_ptrs = [s.data_ptr() for shards in src for s in shards]
+    src_ptrs = [p.data_ptr() for shards in src for s in shards
+                for p in (s if isinstance(s, list) else [s])]
     binding.reshard_execute(plan, src_ptrs, dst_ptrs, torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     return plan, src, named, dst_bufs
@@ -121,8 +126,13 @@ def sampled_copy_check(wl, src, named, nsamp, rng):
             k = int(rng.integers(len(dboxes)))
             ln = dboxes[k][1]
             l = [int(rng.integers(n)) for n in ln]
-            (s, off), = ogolden.expected_sources(sdesc, [None] * len(src[ti]), ddesc, k, [l])
-            want = int(src[ti][s].view(-1)[off]) & 0xFFFF
+            if t["src"].get("split0"):
+                g = [a + b for a, b in zip(dboxes[k][0], l)]
+                s, loc = ogolden.source_location(sdesc, g)
+                want = int(src[ti][s][loc[0]][tuple(loc[1:])]) & 0xFFFF
+            else:
+                (s, off), = ogolden.expected_sources(sdesc, [None] * len(src[ti]), ddesc, k, [l])
+                want = int(src[ti][s].view(-1)[off]) & 0xFFFF
             view = slots[k]["view"] if slots else None
             buf = named[slots[k]["buf"]] if slots else None
             doff = ogolden.element_offset(view, ln, l)
@@ -158,14 +168,16 @@ def sampled_mx_check(wl, src, named, nblocks, rng):
             assert int(sbuf[so]) == int(scales[0, 0]), (t["name"], k, row, b)
 
 
-@pytest.mark.parametrize("which", ["moe_128e", "moe_dsv3"])
+@pytest.mark.parametrize("which", ["moe_128e", "moe_dsv3", "moe_dsv3_per_expert_src"])
 def test_full_size_copy(which):
-    wl = getattr(synth, which)()
+    wl = synth.moe_dsv3(src_split=True) if which == "moe_dsv3_per_expert_src" else \
+        getattr(synth, which)()
     gh.log("full size %s" % wl["name"])
     plan, src, named, dst_bufs = run(wl)
     for key, buf in named.items():
         assert no_poison(buf, wl["buffers"][key]["dtype"]), key
-    src_sum = sum(chunked_sum16(s) for shards in src for s in shards)
+    src_sum = sum(chunked_sum16(p) for shards in src for s in shards
+                  for p in (s if isinstance(s, list) else [s]))
     dst_sum = sum(chunked_sum16(b) for b in named.values())
     assert src_sum == dst_sum
     sampled_copy_check(wl, src, named, 3000, np.random.default_rng(1))

@@ -130,6 +130,14 @@ def test_moe_experts_small(shape):
     gh.check_against_oracle(synth.moe_experts(*shape, seed=9))
 
 
+@pytest.mark.parametrize("quant", [None, "mxfp8"])
+@pytest.mark.parametrize("shape", MOE_SMALL[:4])
+def test_moe_experts_per_expert_sources(shape, quant):
+    """Sources held as one buffer per expert: one region per expert, many
+    pointers (several launch groups at the larger expert counts)."""
+    gh.check_against_oracle(synth.moe_experts(*shape, seed=9, quant=quant, src_split=True))
+
+
 @pytest.mark.parametrize("shape", MOE_SMALL)
 def test_moe_experts_small_mxfp8(shape):
     gh.check_against_oracle(synth.moe_experts(*shape, seed=9, quant="mxfp8"))
@@ -186,3 +194,16 @@ def test_mxfp8_every_bf16_pattern():
          "values": {"kind": "index"}}
     wl = {"name": "mxfp8_all_bf16", "buffers": {}, "tensors": [t]}
     gh.check_against_oracle(wl, globals_=[G])
+
+
+@pytest.mark.parametrize("reverse", [False, True], ids=["pack", "unpack"])
+def test_misc_pack_full_size(reverse):
+    """61 layers of small tensors (norms, router, bias) packed into one
+    buffer, and unpacked again: many regions of mixed sizes in one plan, the
+    tiny bucket included."""
+    wl = synth.misc_pack()
+    if reverse:
+        wl = synth.reverse(wl)
+    gh.log(wl["name"])
+    plan = gh.check_against_oracle(wl)
+    assert plan.info()["regions"]["tiny"] > 0

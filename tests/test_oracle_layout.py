@@ -259,3 +259,27 @@ def test_replica_disagreement_detected():
     with pytest.raises(AssertionError):
         golden.reshard(src, dst, [{"buf": a.view(np.uint8)}, {"buf": b.view(np.uint8)}],
                        [{"buf": np.zeros(16, np.uint8)}])
+
+
+def test_parts_equal_stacked_buffer():
+    """A shard given as one buffer per dim-0 index reads and writes like the
+    same shard in one dense buffer."""
+    rng = np.random.default_rng(3)
+    src = {"shape": [6, 5, 4], "dtype": "i32", "mesh": [3], "placements": [0]}
+    dst = {"shape": [6, 5, 4], "dtype": "i32", "mesh": [2, 2], "placements": [0, 2]}
+    G = rng.integers(0, 1 << 30, size=(6, 5, 4)).astype(np.uint32)
+    stacked = [{"buf": G[2 * s:2 * s + 2].copy().view(np.uint8).reshape(-1)} for s in range(3)]
+    parts = [{"parts": [G[2 * s + i].copy().view(np.uint8).reshape(-1) for i in range(2)]}
+             for s in range(3)]
+    outs = []
+    for sb in (stacked, parts):
+        db = [{"parts": [np.zeros(5 * 2 * 4, np.uint8) for _ in range(3)]} for _ in range(4)]
+        golden.reshard(src, dst, sb, db)
+        outs.append([np.concatenate(d["parts"]) for d in db])
+    for a, b in zip(*outs):
+        np.testing.assert_array_equal(a, b)
+    # destination k = (e, t): experts 3e..3e+2, last-dim half t
+    for k in range(4):
+        e, t = divmod(k, 2)
+        want = G[3 * e:3 * e + 3, :, 2 * t:2 * t + 2]
+        np.testing.assert_array_equal(outs[0][k].view(np.uint32).reshape(3, 5, 2), want)

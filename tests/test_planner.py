@@ -141,6 +141,48 @@ def test_interpreted_plan_moe(quant, shape):
         assert c.max() <= 1
 
 
+@pytest.mark.parametrize("reverse", [False, True], ids=["pack", "unpack"])
+def test_interpreted_misc_pack(reverse):
+    """Small per-layer tensors packed into one buffer at running offsets (and
+    unpacked again): norms replicated over the source TP ranks, the router
+    row-sharded, an f32 bias."""
+    wl = synth.misc_pack(layers=3, hidden=256, q_rank=96, kv_rank=32, experts=16)
+    if reverse:
+        wl = synth.reverse(wl)
+    plan, dst_flat, count = run_interpreted(wl)
+    assert plan.info()["n_tensors"] == 18
+    for c in counts_by_buffer(dst_flat, count).values():
+        assert c.max(initial=0) <= 1
+
+
+@pytest.mark.parametrize("quant", [None, "mxfp8"])
+@pytest.mark.parametrize("shape", [(8, 64, 96, 4, 2, 2), (6, 40, 64, 3, 2, 3), (2, 5000, 40, 2, 1, 2)])
+def test_interpreted_plan_per_expert_sources(quant, shape):
+    """Sources held as one buffer per expert (no stacking copy on the training side)."""
+    E, H, I, sep, dep, dtp = shape
+    wl = synth.moe_experts(E, H, I, sep, dep, dtp, seed=7, quant=quant, src_split=True)
+    plan, dst_flat, count = run_interpreted(wl)
+    assert plan.info()["n_src_ptrs"] == 3 * E
+    for c in counts_by_buffer(dst_flat, count).values():
+        assert c.max() <= 1
+
+
+def test_per_expert_sources_dsv3_plan():
+    p = lh.plan_workload(synth.moe_dsv3(src_split=True))
+    i = p.info()
+    assert i["n_src_ptrs"] == 768 and i["n_regions"] == 384 * 16
+    assert (i["bytes_read"], i["bytes_written"]) == (22_548_578_304, 22_548_578_304)
+
+
+def test_split_mxfp8_destination_needs_two_dims():
+    src = {"shape": [64], "dtype": "bf16", "mesh": [1], "placements": [-1]}
+    dst = {"shape": [64], "dtype": "u8", "mesh": [1], "placements": [-1], "quant": "mxfp8",
+           "split0": True}
+    with pytest.raises(binding.ReshardError) as e:
+        binding.reshard_plan([src], [dst])
+    assert e.value.status == 3
+
+
 def test_region_counts_at_full_sizes():
     """Region counts (before fan-out splits) on the layer-sized layouts."""
     p = lh.plan_workload(synth.dense_ffn())
