@@ -66,7 +66,9 @@ def spec(tensor, side_name):
             "quant": s.get("quant") if side_name == "dst" else None,
             "scale_views": None if s.get("scale_slots") is None
             else [e["view"] for e in s["scale_slots"]],
-            "split0": s.get("split0", False)}
+            "split0": s.get("split0", False),
+            "scale_of": tensor.get("scale_of") if side_name == "src" else None,
+            "scale_block": tensor.get("scale_block")}
 
 
 def plan_of(binding, wl):
@@ -201,6 +203,22 @@ def secondary(torch, binding, stream):
                                           "bytes": nb, "regions": info["n_regions"],
                                           "launches": info["n_launches"],
                                           "plan_us": info["plan_ns"] / 1e3}
+    del src, named
+    torch.cuda.empty_cache()
+    # The DSV3 layer as blockwise-FP8 weights (E4M3 bytes) with their float32
+    # 128 x 128 block scales, gate/up fused with their scales: 6 tensors.
+    wl = synth.fp8_moe_experts(256, 7168, 2048, 16, 8, 8, seed=6)
+    src = device_sources(torch, binding, wl)
+    sp = [x.data_ptr() for t in src for x in t]
+    named, dp = device_destinations(torch, binding, wl)
+    plan = plan_of(binding, wl)
+    info = plan.info()
+    ms = time_plan(torch, binding, plan, sp, dp, stream)
+    nb = info["bytes_read"] + info["bytes_written"]
+    out["fp8_blockwise_dsv3_with_scales"] = {"ms": round(ms, 4), "GBps": round(nb / ms / 1e6, 1),
+                                             "bytes": nb, "regions": info["regions"],
+                                             "launches": info["n_launches"],
+                                             "plan_us": info["plan_ns"] / 1e3}
     del src, named
     torch.cuda.empty_cache()
     # Misc-path packing: 61 layers of small tensors into one buffer, and back.

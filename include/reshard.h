@@ -125,6 +125,19 @@ typedef struct rs_tensor_desc {
    * view describes each part (strides[0] is ignored; base applies to every
    * part).  An MXFP8 destination splits its scale buffers the same way. */
   int32_t split_dim0;
+  /* Blockwise-scaled weights (read from the source description; the
+   * destination's must be 0 or equal).  0: an ordinary tensor.  w + 1: this
+   * tensor holds the scales of tensor w of the same plan, one per block of
+   * scale_block[d] weight elements along each dim d (1 = unblocked), so its
+   * global shape is ceil(weight shape / block) and it uses the weight's
+   * meshes and placements.  Blockwise-FP8 weights move as bytes next to
+   * their scale siblings ("NCCL Reshard Refit (Experimental)", "Enabling It"
+   * and "Design Overview": FP8 weights with their _scale_inv tensors); the
+   * planner checks that every shard boundary of both sides falls on a block
+   * boundary, so each destination receives exactly the scales of its weight
+   * blocks, and reports RS_ERR_UNSUPPORTED naming the slot otherwise. */
+  int32_t scale_of;
+  int32_t scale_block[RS_MAX_DIMS];
 } rs_tensor_desc;
 
 /* Planning options.  Pass NULL for the defaults. */

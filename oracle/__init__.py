@@ -18,6 +18,7 @@ Modules:
   golden  -- gather-then-slice reshard, writing through destination views
   brute   -- per-element ownership brute force (tiny cases only)
   mxfp8   -- BF16 -> MXFP8 (E4M3 elements, E8M0 block scale) rule
+  fp8block -- blockwise-FP8 weights and their scale tensors
 """
 
-from . import layout, golden, brute, mxfp8  # noqa: F401
+from . import layout, golden, brute, mxfp8, fp8block  # noqa: F401

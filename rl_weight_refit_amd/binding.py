@@ -10,7 +10,9 @@ A side description is a dict:
   shape, dtype ("u8", "bf16", "f32", ...), mesh, placements (d >= 0 Shard(d),
   -1 Replicate), and optionally slot_of_coord, views (per slot (base,
   strides) in elements, or None for all-dense), quant ("mxfp8" on a
-  destination), scale_views and split0 (one buffer per local dim-0 index).
+  destination), scale_views, split0 (one buffer per local dim-0 index), and
+  scale_of / scale_block (this tensor holds the block scales of tensor
+  scale_of of the same plan).
 """
 
 import ctypes
@@ -43,7 +45,7 @@ class TensorDesc(ctypes.Structure):
                 ("mesh_shape", c_i64 * RS_MAX_MESH),
                 ("slot_of_coord", ctypes.POINTER(c_i32)), ("views", ctypes.POINTER(View)),
                 ("quant", c_i32), ("scale_views", ctypes.POINTER(View)),
-                ("split_dim0", c_i32)]
+                ("split_dim0", c_i32), ("scale_of", c_i32), ("scale_block", c_i32 * RS_MAX_DIMS)]
 
 
 class PlanOpts(ctypes.Structure):
@@ -147,6 +149,11 @@ def make_desc(spec):
         d.views = ctypes.cast(v, ctypes.POINTER(View))
     d.quant = QUANT[spec.get("quant")]
     d.split_dim0 = 1 if spec.get("split0") else 0
+    so = spec.get("scale_of")
+    if so is not None:
+        d.scale_of = int(so) + 1
+        for i, b in enumerate(spec["scale_block"]):
+            d.scale_block[i] = int(b)
     sv = _views(spec.get("scale_views"), d.ndim)
     if sv is not None:
         keep.append(sv)

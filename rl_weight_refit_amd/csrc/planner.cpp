@@ -579,6 +579,68 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
     sc_base[t] = n_dst_ptrs;
     if (D[t].quant == RS_Q_MXFP8_E4M3) n_dst_ptrs += D[t].nptrs;
   }
+  // Blockwise-scaled weights: the scale tensor must follow the weight's
+  // layouts block for block.
+  for (int t = 0; t < n && E.status() == RS_OK; ++t) {
+    const int32_t so = src[t].scale_of;
+    if (dst[t].scale_of != 0 && dst[t].scale_of != so)
+      E.add(&E.invalid, "tensor ", t, ": dst scale_of ", dst[t].scale_of, " differs from src ", so);
+    if (so == 0) continue;
+    const int w = so - 1;
+    if (w < 0 || w >= n || w == t || src[w].scale_of != 0) {
+      E.add(&E.invalid, "tensor ", t, ": scale_of ", so, " does not name another, unscaled tensor");
+      continue;
+    }
+    const int nd = S[t].ndim;
+    if (S[w].ndim != nd) {
+      E.add(&E.mismatch, "tensor ", t, ": scales have ", nd, " dims, weight tensor ", w, " has ",
+            S[w].ndim);
+      continue;
+    }
+    int64_t blk[RS_MAX_DIMS];
+    bool ok = true;
+    for (int d = 0; d < nd; ++d) {
+      blk[d] = src[t].scale_block[d];
+      if (blk[d] < 1) {
+        E.add(&E.invalid, "tensor ", t, ": scale_block[", d, "] = ", blk[d], " < 1");
+        ok = false;
+      } else if (S[t].shape[d] != (S[w].shape[d] + blk[d] - 1) / blk[d]) {
+        E.add(&E.mismatch, "tensor ", t, ": scale extent ", S[t].shape[d], " along dim ", d,
+              " is not ceil(", S[w].shape[d], " / ", blk[d], ")");
+        ok = false;
+      }
+    }
+    if (!ok) continue;
+    const Layout* pairs[2][2] = {{&S[w], &S[t]}, {&D[w], &D[t]}};
+    const char* names[2] = {"src", "dst"};
+    for (int sd = 0; sd < 2; ++sd) {
+      const Layout& W = *pairs[sd][0];
+      const Layout& C = *pairs[sd][1];
+      bool same = W.mesh_ndim == C.mesh_ndim;
+      for (int i = 0; same && i < W.mesh_ndim; ++i)
+        same = W.mesh[i] == C.mesh[i] && W.pl[i] == C.pl[i];
+      if (!same) {
+        E.add(&E.mismatch, "tensor ", t, ": ", names[sd], " mesh/placements differ from weight tensor ", w);
+        continue;
+      }
+      for (int64_t sl = 0; sl < W.nslots; ++sl) {
+        const Interval* wb = W.slot_box(sl);
+        const Interval* cb = C.slot_box(sl);
+        for (int d = 0; d < nd; ++d) {
+          const int64_t ws = wb[d].start, we = ws + wb[d].len;
+          const int64_t cs = cb[d].start, ce = cs + cb[d].len;
+          const bool match = wb[d].len == 0 ? cb[d].len == 0
+                                            : (ws == cs * blk[d] && we == std::min(ce * blk[d], W.shape[d]));
+          if (!match) {
+            E.add(&E.unsupported, "tensor ", t, ": ", names[sd], " slot ", sl, " holds weight [", ws,
+                  ", ", we, ") but scales [", cs, ", ", ce, ") along dim ", d, " (block ", blk[d],
+                  "): a shard boundary falls inside a scale block");
+            break;
+          }
+        }
+      }
+    }
+  }
   if (E.status() != RS_OK) {
     err = E.text.str();
     return E.status();

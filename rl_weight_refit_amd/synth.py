@@ -241,6 +241,58 @@ def moe_dsv3(quant=None, src_split=False):
     return moe_experts(256, 7168, 2048, 16, 8, 8, seed=5, quant=quant, src_split=src_split)
 
 
+def fp8_moe_experts(experts, hidden, inter, src_ep, dst_ep, dst_tp, seed, block=128,
+                    src_split=False):
+    """Blockwise-FP8 grouped MoE experts with their scale tensors: E4M3
+    weight bytes gate/up [E,I,H], down [E,H,I] and float32 scales [E,
+    ceil(I/block), ceil(H/block)] / [E, ceil(H/block), ceil(I/block)], each
+    scale tensor on its weight's meshes and placements (source EP Shard(0) ->
+    destination [EP, TP]).  Destinations: gate and up weights fused in w13
+    (gate first), their scales fused in s13 the same way; down in w2 / s2."""
+    el = -(-experts // dst_ep)
+    ip = -(-inter // dst_tp)
+    cb = lambda n: -(-n // block)
+    ndst = dst_ep * dst_tp
+    bufs = {}
+    w13_st = _row_major([el, 2 * ip, hidden])
+    w2_st = _row_major([el, hidden, ip])
+    s13_st = _row_major([el, 2 * cb(ip), cb(hidden)])
+    s2_st = _row_major([el, cb(hidden), cb(ip)])
+    for k in range(ndst):
+        bufs["w13/%d" % k] = {"dtype": "u8", "elems": el * 2 * ip * hidden}
+        bufs["w2/%d" % k] = {"dtype": "u8", "elems": el * hidden * ip}
+        bufs["s13/%d" % k] = {"dtype": "f32", "elems": el * 2 * cb(ip) * cb(hidden)}
+        bufs["s2/%d" % k] = {"dtype": "f32", "elems": el * cb(hidden) * cb(ip)}
+    mesh = [dst_ep, dst_tp]
+
+    def w(name, shape, pl, slots, i):
+        return {"name": name, "shape": shape, "dtype": "u8",
+                "src": side([src_ep], [0], split0=src_split), "dst": side(mesh, pl, slots),
+                "values": {"kind": "e4m3", "seed": seed * 1000 + i}}
+
+    def sc(name, shape, pl, slots, of, i):
+        t = {"name": name, "shape": shape, "dtype": "f32",
+             "src": side([src_ep], [0]), "dst": side(mesh, pl, slots),
+             "values": {"kind": "scale", "seed": seed * 1000 + i},
+             "scale_of": of, "scale_block": [1, block, block]}
+        return t
+
+    slots = lambda key, base, st: [{"buf": "%s/%d" % (key, k), "view": (base, st)}
+                                   for k in range(ndst)]
+    tensors = [
+        w("gate", [experts, inter, hidden], [0, 1], slots("w13", 0, w13_st), 0),
+        w("up", [experts, inter, hidden], [0, 1], slots("w13", ip * hidden, w13_st), 1),
+        w("down", [experts, hidden, inter], [0, 2], slots("w2", 0, w2_st), 2),
+        sc("gate_scale_inv", [experts, cb(inter), cb(hidden)], [0, 1], slots("s13", 0, s13_st), 0, 3),
+        sc("up_scale_inv", [experts, cb(inter), cb(hidden)], [0, 1],
+           slots("s13", cb(ip) * cb(hidden), s13_st), 1, 4),
+        sc("down_scale_inv", [experts, cb(hidden), cb(inter)], [0, 2], slots("s2", 0, s2_st), 2, 5),
+    ]
+    name = "fp8_moe_e%d_h%d_i%d_ep%d_to_ep%dxtp%d_b%d" % (experts, hidden, inter, src_ep, dst_ep,
+                                                          dst_tp, block)
+    return {"name": name, "buffers": bufs, "tensors": tensors}
+
+
 # ---------------------------------------------------------------------------
 # Misc-path packing: many small tensors into one contiguous buffer.
 # ---------------------------------------------------------------------------
@@ -303,6 +355,15 @@ def host_values(tensor):
         return (np.arange(n, dtype=np.uint64) & np.uint64((1 << (8 * es)) - 1)) \
             .astype(uint).reshape(shape)
     rng = np.random.Generator(np.random.PCG64(v["seed"]))
+    if v["kind"] == "e4m3":
+        # random E4M3 bytes, the two NaN codes replaced by zero
+        b = rng.integers(0, 256, size=shape, dtype=np.uint8)
+        b[(b & 0x7F) == 0x7F] = 0
+        return b
+    if v["kind"] == "scale":
+        # positive float32 block scales spread over a few binades
+        x = np.exp2(rng.uniform(-12.0, -4.0, size=shape)).astype(np.float32)
+        return x.view(np.uint32)
     if v["kind"] == "uniform":
         x = rng.uniform(-1.0, 1.0, size=shape).astype(np.float32)
     elif v["kind"] == "normal":
@@ -326,9 +387,16 @@ def device_values(tensor, device):
     """
     import torch
     v = tensor["values"]
-    dt = {"bf16": torch.bfloat16, "f32": torch.float32}[tensor["dtype"]]
     g = torch.Generator(device=device)
     g.manual_seed(v["seed"])
+    if v["kind"] == "e4m3":
+        b = torch.randint(0, 256, tensor["shape"], generator=g, device=device, dtype=torch.int32)
+        b = torch.where((b & 0x7F) == 0x7F, torch.zeros_like(b), b)
+        return b.to(torch.uint8)
+    if v["kind"] == "scale":
+        x = torch.rand(tensor["shape"], generator=g, device=device, dtype=torch.float32)
+        return torch.exp2(x * 8.0 - 12.0)
+    dt = {"bf16": torch.bfloat16, "f32": torch.float32}[tensor["dtype"]]
     if v["kind"] == "normal":
         x = torch.randn(tensor["shape"], generator=g, device=device, dtype=torch.float32)
         x.mul_(v["std"])

@@ -23,7 +23,9 @@ def spec(tensor, side_name):
     return {"shape": tensor["shape"], "dtype": dtype, "mesh": s["mesh"],
             "placements": s["placements"], "slot_of_coord": s.get("slot_of_coord"),
             "views": views, "quant": s.get("quant") if side_name == "dst" else None,
-            "scale_views": sviews, "split0": s.get("split0", False)}
+            "scale_views": sviews, "split0": s.get("split0", False),
+            "scale_of": tensor.get("scale_of") if side_name == "src" else None,
+            "scale_block": tensor.get("scale_block")}
 
 
 def plan_workload(workload, **kw):

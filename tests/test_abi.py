@@ -38,7 +38,8 @@ STRUCTS = {
     "rs_view": (binding.View, ["base", "strides"]),
     "rs_tensor_desc": (binding.TensorDesc, ["ndim", "dtype", "global_shape", "mesh_ndim",
                                             "placements", "mesh_shape", "slot_of_coord", "views",
-                                            "quant", "scale_views", "split_dim0"]),
+                                            "quant", "scale_views", "split_dim0", "scale_of",
+                                            "scale_block"]),
     "rs_plan_opts": (binding.PlanOpts, ["struct_size", "fanout", "unit_bytes", "tiny_bytes",
                                         "thin_bytes", "reserved"]),
     "rs_plan_info": (binding.PlanInfo, [f[0] for f in binding.PlanInfo._fields_]),

@@ -207,3 +207,17 @@ def test_misc_pack_full_size(reverse):
     gh.log(wl["name"])
     plan = gh.check_against_oracle(wl)
     assert plan.info()["regions"]["tiny"] > 0
+
+
+@pytest.mark.parametrize("kw", [{}, {"src_split": True}])
+def test_fp8_blockwise_layer_small(kw):
+    """Blockwise-FP8 weight bytes and their float32 block scales in one plan,
+    gate/up fused (weights in w13, scales in s13)."""
+    gh.check_against_oracle(synth.fp8_moe_experts(8, 256, 512, 4, 2, 2, seed=3, **kw))
+
+
+def test_fp8_blockwise_dsv3_shape_32_experts():
+    """32 experts of the DeepSeek-V3 FP8 layer (hidden 7168, intermediate
+    2048, 128 x 128 blocks), EP16 -> EP8 x TP8."""
+    gh.log("fp8 dsv3 32 experts")
+    gh.check_against_oracle(synth.fp8_moe_experts(32, 7168, 2048, 16, 8, 8, seed=4))
