@@ -261,6 +261,27 @@ def secondary(torch, binding, stream):
         slab[label] = {"ms": round(ms, 4), "GBps": round(nb / ms / 1e6, 1),
                        "regions": info["regions"]}
     out["column_slabs_1Mx8_i32_2row_to_4col"] = slab
+    # Execution time of the uneven layouts (fp32 / bf16 [1000,3000] and
+    # [7,513,257], meshes [3] / [2,3] -> [7] / [4,2]); small, cache-resident.
+    ex = []
+    for seed in range(0, 500, 10):
+        w = synth.uneven_case(seed)
+        u = w["tensors"][0]
+        plan = plan_of(binding, w)
+        info = plan.info()
+        ssp, dsp = spec(u, "src"), spec(u, "dst")
+        es = synth.ELEM_BYTES[u["dtype"]]
+        sbufs = [torch.empty(max(1, int(np.prod(binding.reshard_shard_box(ssp, k)[1])) * es),
+                             dtype=torch.uint8, device="cuda") for k in range(int(np.prod(u["src"]["mesh"])))]
+        dbufs = [torch.empty(max(1, int(np.prod(binding.reshard_shard_box(dsp, k)[1])) * es),
+                             dtype=torch.uint8, device="cuda") for k in range(int(np.prod(u["dst"]["mesh"])))]
+        ms = time_plan(torch, binding, plan, [b.data_ptr() for b in sbufs],
+                       [b.data_ptr() for b in dbufs], stream)
+        ex.append((ms * 1e3, info["bytes_read"] + info["bytes_written"], info["n_launches"]))
+    us = sorted(e[0] for e in ex)
+    out["uneven_50_layouts_exec_us"] = {"p50": round(us[len(us) // 2], 2), "max": round(us[-1], 2),
+                                        "bytes_p50": sorted(e[1] for e in ex)[len(ex) // 2],
+                                        "launches_max": max(e[2] for e in ex)}
     # Plan time over the 500 uneven layouts (CPU).
     ns = []
     for seed in range(500):

@@ -120,8 +120,8 @@ MOE_SMALL = [
     (12, 200, 100, 3, 2, 4),     # ragged: 100 / 4 per TP shard, 200 hidden
     (32, 256, 64, 16, 8, 8),     # the DSV3 meshes at a small size
     (6, 96, 40, 3, 2, 3),        # uneven intermediate split
-    (4, 5000, 64, 2, 2, 2),      # MXFP8 rows split into 4096 + 904 elements (short last block)
-    (2, 8200, 24, 1, 2, 1),      # two full 4096-element segments and an 8-element tail
+    (4, 9000, 64, 2, 2, 2),      # MXFP8 rows split into 2 x 4096 + 808 elements (short last block)
+    (2, 17000, 24, 1, 2, 1),     # four full 4096-element segments and a 616-element tail
 ]
 
 

@@ -132,7 +132,8 @@ def test_interpreted_plan_fused_dense(kw):
 
 @pytest.mark.parametrize("quant", [None, "mxfp8"])
 @pytest.mark.parametrize("shape", [(8, 64, 96, 4, 2, 2), (6, 40, 64, 3, 2, 3), (4, 96, 32, 2, 1, 2),
-                                   (2, 5000, 40, 2, 1, 2), (2, 8200, 24, 1, 2, 1)])
+                                   (2, 5000, 40, 2, 1, 2), (2, 8200, 24, 1, 2, 1),
+                                   (1, 17000, 8, 1, 1, 1)])
 def test_interpreted_plan_moe(quant, shape):
     E, H, I, sep, dep, dtp = shape
     wl = synth.moe_experts(E, H, I, sep, dep, dtp, seed=7, quant=quant)
@@ -271,3 +272,36 @@ def test_empty_tensor_plans_nothing():
 def test_plan_time_is_reported():
     plan = lh.plan_workload(synth.moe_dsv3())
     assert 0 < plan.info()["plan_ns"] < 1e9
+
+
+def test_debug_checks_reject_overlapping_buffers(monkeypatch):
+    """With RESHARD_DEBUG_CHECKS=1, a destination that overlaps a source is
+    rejected before anything is launched (no GPU needed: the check runs
+    first)."""
+    wl = synth.worked_example()
+    plan = lh.plan_workload(wl)
+    src = [0x100000, 0x200000]
+    dst = [0x300000, 0x400000, 0x100010, 0x500000]   # dst 2 lands inside src 0
+    monkeypatch.setenv("RESHARD_DEBUG_CHECKS", "1")
+    with pytest.raises(binding.ReshardError) as e:
+        binding.reshard_execute(plan, src, dst)
+    assert e.value.status == 1 and "overlap" in str(e.value)
+
+
+def test_execute_reports_every_bad_pointer():
+    wl = synth.worked_example()
+    plan = lh.plan_workload(wl)
+    with pytest.raises(binding.ReshardError) as e:
+        binding.reshard_execute(plan, [0, 0], [0x1000, 0, 0x3000, 0])
+    msg = str(e.value)
+    for name in ("src_ptrs[0]", "src_ptrs[1]", "dst_ptrs[1]", "dst_ptrs[3]"):
+        assert name in msg
+
+
+def test_mxfp8_source_must_be_two_byte_aligned():
+    wl = synth.moe_experts(2, 64, 32, 1, 1, 1, seed=1, quant="mxfp8")
+    plan = lh.plan_workload(wl)
+    n_src, n_dst = plan.info()["n_src_ptrs"], plan.info()["n_dst_ptrs"]
+    with pytest.raises(binding.ReshardError) as e:
+        binding.reshard_execute(plan, [0x1001] * n_src, [0x100000 + 0x1000 * i for i in range(n_dst)])
+    assert "aligned" in str(e.value)
