@@ -528,146 +528,159 @@ __device__ __forceinline__ uint32_t e4m3x4(uint32_t w0, uint32_t w1, uint32_t m0
   return __builtin_bit_cast(uint32_t, r);
 }
 
-struct MxRow {
-  const char* src;   // bf16 row start
-  uint64_t dst_off;  // element-row offset from each destination pointer
-  uint64_t sc_off;   // scale-row offset from each scale pointer
-};
-
 #ifndef RS_MX_MIN_WAVES
 #define RS_MX_MIN_WAVES 1  // occupancy floor (waves per SIMD) the register allocator must keep
 #endif
+#ifndef RS_MX_LDS_AUX
+#define RS_MX_LDS_AUX 2    // cache policy of the direct-to-LDS loads (2: non-temporal)
+#endif
+#ifndef RS_MX_SC_STAGE
+#define RS_MX_SC_STAGE 1   // 1: block scales gathered in LDS, stored by consecutive lanes at the end
+#endif
 
-// Loads one lane's 8-element group g of a row (zeros past the row end).
-__device__ __forceinline__ int mx_load(const MxRow& row, uint32_t g, uint32_t inner, u32x4& x) {
-  const uint32_t col = g * 8u;
-  const int nvalid = int(min(inner, col + 8u)) - int(min(inner, col));
-  const uint16_t* s = reinterpret_cast<const uint16_t*>(row.src) + col;
-  x = u32x4{0u, 0u, 0u, 0u};
-  if (nvalid == 8 && (reinterpret_cast<uintptr_t>(s) & 15u) == 0) {
-    x = ld16(s);
-  } else if (nvalid > 0) {
-    uint32_t w[4] = {0, 0, 0, 0};
-    for (int i = 0; i < 8; ++i)
-      if (i < nvalid) w[i >> 1] |= uint32_t(s[i]) << (16 * (i & 1));
-    x = u32x4{w[0], w[1], w[2], w[3]};
-  }
-  return nvalid;
-}
+typedef __attribute__((address_space(3))) void lds_void;
 
-// Quantises and stores one lane's group (4 consecutive lanes = one block).
-// All four lanes of a block must call this together: the block's amax is
-// reduced across them.  Lanes past the row end pass nvalid <= 0.
-__device__ __forceinline__ void mx_finish(const LaunchArgs& a, const MxRegion* R, const MxRow& row,
-                                          uint32_t g, u32x4 x, int nvalid, uint32_t sc_inner,
-                                          uint32_t nd) {
+// Block codes of one lane's 8-element group x (bf16 pairs; zeros past the
+// row end).  The four consecutive lanes of a block call this together: the
+// block's amax is reduced across them with DPP quad permutes.
+struct MxCodes {
+  uint32_t lo, hi;   // E4M3 codes of elements 0-3 and 4-7
+  uint8_t scale;     // E8M0 block scale
+};
+
+__device__ __forceinline__ MxCodes mx_encode(u32x4 x) {
   const uint32_t w0 = x.x, w1 = x.y, w2 = x.z, w3 = x.w;
   const uint32_t m0 = w0 & 0x7FFF7FFFu, m1 = w1 & 0x7FFF7FFFu;
   const uint32_t m2 = w2 & 0x7FFF7FFFu, m3 = w3 & 0x7FFF7FFFu;
   const uint32_t mm = pk_max_u16(pk_max_u16(m0, m1), pk_max_u16(m2, m3));
   uint32_t amax = max(mm & 0xFFFFu, mm >> 16);
-  // Block amax across the quad: DPP quad_perm [1,0,3,2] then [2,3,0,1].
+  // quad_perm [1,0,3,2] then [2,3,0,1]
   amax = max(amax, uint32_t(__builtin_amdgcn_update_dpp(0, int(amax), 0xB1, 0xF, 0xF, true)));
   amax = max(amax, uint32_t(__builtin_amdgcn_update_dpp(0, int(amax), 0x4E, 0xF, 0xF, true)));
-  if (nvalid <= 0) return;
-  const bool bad = amax >= 0x7F80u;
+  const bool bad = amax >= 0x7F80u;   // a NaN or Inf in the block
   const int X = shared_exp(amax);
   const uint32_t T = (uint32_t(X + 135) << 7) | 0x60u;   // bf16 bits of 448 * 2^X
   const uint32_t T2 = T | (T << 16);
   const float sc = __builtin_amdgcn_ldexpf(1.0f, X);
-  uint32_t lo = e4m3x4(w0, w1, m0, m1, T2, sc);
-  uint32_t hi = e4m3x4(w2, w3, m2, m3, T2, sc);
-  if (bad) lo = hi = 0x7F7F7F7Fu;
-  const uint8_t scale = bad ? uint8_t(0xFF) : uint8_t(X + 127);
-  const uint32_t col = g * 8u;
-  const bool lead = (g & 3u) == 0;
-  const uint64_t sco = row.sc_off + uint64_t(g >> 2) * sc_inner;
-  for (uint32_t j = 0; j < nd; ++j) {
-    char* d = static_cast<char*>(a.ptr[R->dst_ptr[j]]) + row.dst_off + col;
-    if (nvalid == 8 && (reinterpret_cast<uintptr_t>(d) & 7u) == 0) {
-      u32x2 v;
-      v.x = lo;
-      v.y = hi;
-      __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(d));
-    } else {
-      for (int i = 0; i < 8; ++i)
-        if (i < nvalid) d[i] = char(((i < 4 ? lo : hi) >> (8 * (i & 3))) & 0xFFu);
-    }
-    if (lead) *(static_cast<char*>(a.ptr[R->sc_ptr[j]]) + sco) = char(scale);
-  }
+  MxCodes c;
+  c.lo = e4m3x4(w0, w1, m0, m1, T2, sc);
+  c.hi = e4m3x4(w2, w3, m2, m3, T2, sc);
+  if (bad) c.lo = c.hi = 0x7F7F7F7Fu;
+  c.scale = bad ? uint8_t(0xFF) : uint8_t(X + 127);
+  return c;
 }
 
-__global__ __launch_bounds__(kThreads, RS_MX_MIN_WAVES) void rs_mx_kernel(LaunchArgs a) {
+// One work unit of the MXFP8 kernel: nr rows (nr <= kMxSlots >> lg) of inner
+// elements, staged in LDS with row i at slot i << lg (one 16-byte slot per
+// 8-element group).  kOneRow: the unit is a single row, whose addresses are
+// uniform across the workgroup.
+template <bool kOneRow>
+__device__ __forceinline__ void mx_unit(const LaunchArgs& a, const MxRegion* R, uint32_t r0, uint32_t nr,
+                                        u32x4* stage, uint8_t* sc_stage) {
+  constexpr uint32_t K = kMxSlots / kThreads;
   const uint32_t tid = threadIdx.x;
-  const uint32_t unit = unit_of_block<RS_MX_XCD_MAP != 0>(blockIdx.x, gridDim.x, RS_XCD_CHUNK);
-  const MxRegion* R = find_region<MxRegion>(a, unit);
-  const uint64_t src_off = R->src_off, dst_off = R->dst_off, sc_off = R->sc_off;
   const uint64_t s0 = R->sstr[0], s1 = R->sstr[1], s2 = R->sstr[2];
   const uint64_t d0 = R->dstr[0], d1 = R->dstr[1], d2 = R->dstr[2];
   const uint64_t c0 = R->scstr[0], c1 = R->scstr[1], c2 = R->scstr[2];
-  const uint32_t e0 = R->e0, e1 = R->e1, rows = R->rows, inner = R->inner;
-  const uint32_t rpu = R->rows_per_unit, ub = R->unit_begin, flags = R->flags;
-  const uint32_t sc_inner = R->sc_inner;
-  const uint32_t nd = R->n_dst;
-  const uint32_t nouter = flags & kFlagOuterMask;
-  const char* sp = static_cast<const char*>(a.ptr[R->src_ptr]) + src_off;
+  const uint32_t e0 = R->e0, e1 = R->e1, inner = R->inner;
+  const uint32_t nouter = R->flags & kFlagOuterMask;
+  const uint32_t sc_inner = R->sc_inner, nd = R->n_dst;
+  const uint32_t lg = mx_slot_shift(inner), Lp = 1u << lg;
+  const uint32_t ng = (inner + 7u) >> 3;
+  const char* sp = static_cast<const char*>(a.ptr[R->src_ptr]) + R->src_off;
+  const uint64_t so1 = kOneRow ? row_off(r0, e0, e1, nouter, s0, s1, s2) : 0;
+  const uint64_t do1 = kOneRow ? row_off(r0, e0, e1, nouter, d0, d1, d2) : 0;
 
-  const uint32_t r0 = (unit - ub) * rpu;
-  const uint32_t r1 = min(r0 + rpu, rows);
-  const uint32_t ng = (inner + 7u) >> 3;     // 8-element groups per row
-  const uint32_t ngp = (ng + 3u) & ~3u;      // padded to whole blocks
-  constexpr int U = kMxUnroll;
-
-  if (ng >= kThreads) {
-    // Long rows: the workgroup walks rows (uniform row addresses); each lane
-    // loads U groups of the row before quantising them.
-    for (uint32_t r = r0; r < r1; ++r) {
-      MxRow row;
-      row.src = sp + row_off(r, e0, e1, nouter, s0, s1, s2);
-      row.dst_off = dst_off + row_off(r, e0, e1, nouter, d0, d1, d2);
-      row.sc_off = sc_off + row_off(r, e0, e1, nouter, c0, c1, c2);
-      for (uint32_t g0 = tid; g0 < ngp; g0 += U * kThreads) {
-        u32x4 x[U];
-        int nv[U];
+  // Phase 1: every group of the unit into its LDS slot.  Whole, 16-byte
+  // aligned groups load straight into LDS; a partial or misaligned group is
+  // gathered element by element (zero-filled) and written by its lane.
 #pragma unroll
-        for (int u = 0; u < U; ++u) nv[u] = mx_load(row, g0 + u * kThreads, inner, x[u]);
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-          if (g0 + u * kThreads < ngp) mx_finish(a, R, row, g0 + u * kThreads, x[u], nv[u], sc_inner, nd);
-      }
-    }
-  } else {
-    // Short rows: L lanes per row (a power of two, at least one block); each
-    // lane loads its group of U rows before quantising them.
-    uint32_t L = 4;
-    while (L < ng && L < 64u) L <<= 1;
-    const uint32_t lane = tid & 63u, wave = tid >> 6;
-    const uint32_t G = 64u / L;
-    const uint32_t sub = lane & (L - 1u);
-    const uint32_t step = 4u * G;
-    for (uint32_t rb = r0 + wave * G + lane / L; rb < r1; rb += U * step) {
-      for (uint32_t g = sub; g < ngp; g += L) {
-        MxRow row[U];
-        u32x4 x[U];
-        int nv[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const uint32_t r = rb + u * step;
-          nv[u] = 0;
-          x[u] = u32x4{0u, 0u, 0u, 0u};
-          if (r < r1) {
-            row[u].src = sp + row_off(r, e0, e1, nouter, s0, s1, s2);
-            row[u].dst_off = dst_off + row_off(r, e0, e1, nouter, d0, d1, d2);
-            row[u].sc_off = sc_off + row_off(r, e0, e1, nouter, c0, c1, c2);
-            nv[u] = mx_load(row[u], g, inner, x[u]);
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-          if (rb + u * step < r1) mx_finish(a, R, row[u], g, x[u], nv[u], sc_inner, nd);
+  for (uint32_t k = 0; k < K; ++k) {
+    const uint32_t s = k * kThreads + tid;
+    const uint32_t rl = s >> lg, g = s & (Lp - 1u);
+    if (rl < nr && g < ng) {
+      const char* p = sp + (kOneRow ? so1 : row_off(r0 + rl, e0, e1, nouter, s0, s1, s2)) +
+                      uint64_t(g) * 16u;
+      if (g * 8u + 8u <= inner && (reinterpret_cast<uintptr_t>(p) & 15u) == 0) {
+        __builtin_amdgcn_global_load_lds(p, (lds_void*)(stage + k * kThreads + (tid & ~63u)), 16, 0,
+                                         RS_MX_LDS_AUX);
+      } else {
+        const uint16_t* q = reinterpret_cast<const uint16_t*>(p);
+        const uint32_t n = min(inner - g * 8u, 8u);
+        uint32_t w[4] = {0, 0, 0, 0};
+        for (uint32_t i = 0; i < 8; ++i)
+          if (i < n) w[i >> 1] |= uint32_t(q[i]) << (16 * (i & 1));
+        stage[s] = u32x4{w[0], w[1], w[2], w[3]};
       }
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // Phase 2: quantise slot by slot (a quad of lanes per block) and store
+  // 8 code bytes per lane to every replica.
+#pragma unroll
+  for (uint32_t k = 0; k < K; ++k) {
+    const uint32_t s = k * kThreads + tid;
+    const uint32_t rl = s >> lg, g = s & (Lp - 1u);
+    const uint32_t col = g * 8u;
+    const int nvalid = rl < nr ? int(min(inner, col + 8u)) - int(min(inner, col)) : 0;
+    const u32x4 x = nvalid > 0 ? stage[s] : u32x4{0u, 0u, 0u, 0u};
+    const MxCodes c = mx_encode(x);
+    if (nvalid > 0) {
+      const uint64_t doff = R->dst_off + (kOneRow ? do1 : row_off(r0 + rl, e0, e1, nouter, d0, d1, d2)) + col;
+      for (uint32_t j = 0; j < nd; ++j) {
+        char* d = static_cast<char*>(a.ptr[R->dst_ptr[j]]) + doff;
+        if (nvalid == 8 && (reinterpret_cast<uintptr_t>(d) & 7u) == 0) {
+          u32x2 v;
+          v.x = c.lo;
+          v.y = c.hi;
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(d));
+        } else {
+          for (int i = 0; i < 8; ++i)
+            if (i < nvalid) d[i] = char(((i < 4 ? c.lo : c.hi) >> (8 * (i & 3))) & 0xFFu);
+        }
+      }
+      if ((g & 3u) == 0) {
+#if RS_MX_SC_STAGE
+        sc_stage[s >> 2] = c.scale;
+#else
+        const uint64_t so = R->sc_off + row_off(r0 + rl, e0, e1, nouter, c0, c1, c2) + uint64_t(g >> 2) * sc_inner;
+        for (uint32_t j = 0; j < nd; ++j) *(static_cast<char*>(a.ptr[R->sc_ptr[j]]) + so) = char(c.scale);
+#endif
+      }
+    }
+  }
+#if RS_MX_SC_STAGE
+  // Phase 3: the unit's block scales, block b of row i at LDS byte
+  // (i << lg) / 4 + b, written by consecutive lanes.
+  __syncthreads();
+  const uint32_t nb = (inner + 31u) >> 5;
+  for (uint32_t t = tid; t < kMxSlots / 4; t += kThreads) {
+    const uint32_t rl = t >> (lg - 2), b = t & ((Lp >> 2) - 1u);
+    if (rl < nr && b < nb) {
+      const uint64_t so = R->sc_off + row_off(r0 + rl, e0, e1, nouter, c0, c1, c2) + uint64_t(b) * sc_inner;
+      const char v = char(sc_stage[t]);
+      for (uint32_t j = 0; j < nd; ++j) *(static_cast<char*>(a.ptr[R->sc_ptr[j]]) + so) = v;
+    }
+  }
+#else
+  (void)sc_stage;
+  (void)c0; (void)c1; (void)c2; (void)sc_inner;
+#endif
+}
+
+__global__ __launch_bounds__(kThreads, RS_MX_MIN_WAVES) void rs_mx_kernel(LaunchArgs a) {
+  __shared__ u32x4 stage[kMxSlots];
+  __shared__ uint8_t sc_stage[kMxSlots / 4];
+  const uint32_t unit = unit_of_block<RS_MX_XCD_MAP != 0>(blockIdx.x, gridDim.x, RS_XCD_CHUNK);
+  const MxRegion* R = find_region<MxRegion>(a, unit);
+  const uint32_t r0 = (unit - R->unit_begin) * R->rows_per_unit;
+  const uint32_t nr = min(R->rows_per_unit, R->rows - r0);
+  if (nr == 1)
+    mx_unit<true>(a, R, r0, nr, stage, sc_stage);
+  else
+    mx_unit<false>(a, R, r0, nr, stage, sc_stage);
 }
 
 }  // namespace

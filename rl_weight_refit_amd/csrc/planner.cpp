@@ -842,16 +842,8 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
     if (r.mx) {
       f.bucket = kMx;
       const uint64_t row_bytes = r.inner * 2;
-      // One load batch per work unit: rows of at least kThreads groups take
-      // the whole workgroup; shorter rows are spread over lane groups of L
-      // lanes (as in the kernel), kMxUnroll rows per lane.
-      const uint64_t ng = (r.inner + 7) / 8;
-      uint64_t rpu = 1;
-      if (ng < uint64_t(kThreads)) {
-        uint64_t L = 4;
-        while (L < ng && L < 64) L <<= 1;
-        rpu = uint64_t(kThreads) * kMxUnroll / L;
-      }
+      // Whole rows per LDS-staged work unit (a long row is one segment).
+      const uint64_t rpu = kMxSlots >> mx_slot_shift(uint32_t(r.inner));
       f.rows_per_unit = uint32_t(std::min<uint64_t>(rpu, f.rows));
       const uint64_t nb = (r.inner + kMxBlock - 1) / kMxBlock;
       bytes_read += f.rows * row_bytes;

@@ -13,10 +13,23 @@ constexpr int kMaxFan = 16;           // destination replicas per region
 constexpr uint32_t kThinTile = 16384; // LDS tile of the thin bucket, bytes
 constexpr uint32_t kLongRow = 2048;   // bulk rows at least this long are walked row by row
 constexpr uint32_t kChunkShift = 8;   // the unit table holds the region of every 256th unit
-constexpr int kMxUnroll = 2;          // 8-element groups each lane of the MXFP8 kernel loads at once
-// Elements one MXFP8 workgroup loads in one batch; longer rows are split
-// (at block boundaries) so that each work unit is a single batch.
-constexpr uint32_t kMxBatchElems = uint32_t(kThreads) * kMxUnroll * 8;
+// MXFP8 work units are staged in LDS, kMxSlots 16-byte slots (8 bf16
+// elements each) per workgroup.  A row takes 2^mx_slot_shift(inner) slots
+// (the power of two at or above its 8-element groups, at least one 32-element
+// block), so a unit holds kMxSlots >> mx_slot_shift(inner) whole rows; rows
+// longer than kMxBatchElems are split at block boundaries first.
+#ifndef RS_MX_SLOTS
+#define RS_MX_SLOTS 1024
+#endif
+constexpr uint32_t kMxSlots = RS_MX_SLOTS;
+constexpr uint32_t kMxBatchElems = kMxSlots * 8;
+static_assert(kMxSlots >= uint32_t(kThreads) && kMxSlots % kThreads == 0, "whole slots per lane");
+
+constexpr uint32_t mx_slot_shift(uint32_t inner) {
+  uint32_t s = 2;
+  while ((1u << s) < (inner + 7) / 8) ++s;
+  return s;
+}
 
 enum Bucket : uint32_t { kBulk = 0, kThin = 1, kTiny = 2, kMx = 3, kBuckets = 4 };
 

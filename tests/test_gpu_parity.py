@@ -120,8 +120,8 @@ MOE_SMALL = [
     (12, 200, 100, 3, 2, 4),     # ragged: 100 / 4 per TP shard, 200 hidden
     (32, 256, 64, 16, 8, 8),     # the DSV3 meshes at a small size
     (6, 96, 40, 3, 2, 3),        # uneven intermediate split
-    (4, 9000, 64, 2, 2, 2),      # MXFP8 rows split into 2 x 4096 + 808 elements (short last block)
-    (2, 17000, 24, 1, 2, 1),     # four full 4096-element segments and a 616-element tail
+    (4, 9000, 64, 2, 2, 2),      # MXFP8 rows split into 8192 + 808 elements (short last block)
+    (2, 17000, 24, 1, 2, 1),     # two full 8192-element segments and a 616-element tail
 ]
 
 
@@ -141,6 +141,28 @@ def test_moe_experts_per_expert_sources(shape, quant):
 @pytest.mark.parametrize("shape", MOE_SMALL)
 def test_moe_experts_small_mxfp8(shape):
     gh.check_against_oracle(synth.moe_experts(*shape, seed=9, quant="mxfp8"))
+
+
+@pytest.mark.parametrize("shifts", [(2, 0), (0, 1), (6, 3), (8, 8)])
+@pytest.mark.parametrize("shape", [MOE_SMALL[0], MOE_SMALL[1], MOE_SMALL[4]])
+def test_moe_experts_mxfp8_misaligned(shape, shifts):
+    """Sources on 2-byte (not 16-byte) boundaries: groups are gathered into
+    LDS element by element instead of the direct 16-byte loads; odd
+    destination offsets take the byte stores."""
+    gh.check_against_oracle(synth.moe_experts(*shape, seed=9, quant="mxfp8"), src_shift=shifts[0],
+                            dst_shift=shifts[1])
+
+
+@pytest.mark.parametrize("shape,inner", [([6, 40, 64], 64), ([3, 30, 200], 200), ([2, 8, 8200], 8200),
+                                         ([5, 3, 33], 33), ([7, 11, 8], 8), ([4, 9, 1000], 1000)])
+@pytest.mark.parametrize("mesh,pl", [([2, 2], [0, -1]), ([4], [-1]), ([2, 3], [-1, 1])])
+def test_mxfp8_fanout_and_row_lengths(shape, inner, mesh, pl):
+    """Replicated MXFP8 destinations (one read, up to four replicas written)
+    over row lengths that pack 1..128 rows into a work unit, rows shorter
+    than a block, and a row just over one unit."""
+    t = {"name": "w", "shape": shape, "dtype": "bf16", "src": synth.side([2], [0]),
+         "dst": synth.side(mesh, pl, quant="mxfp8"), "values": {"kind": "normal", "std": 0.02, "seed": 21}}
+    gh.check_against_oracle({"name": "mx_fan", "buffers": {}, "tensors": [t]})
 
 
 def test_mxfp8_extreme_values():

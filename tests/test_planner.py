@@ -195,8 +195,8 @@ def test_region_counts_at_full_sizes():
     p = lh.plan_workload(synth.moe_dsv3())
     assert p.info()["n_regions"] == 384
     p = lh.plan_workload(synth.moe_dsv3(quant="mxfp8"))
-    # gate/up rows of 7168 elements are split into 4096 + 3072 element segments
-    assert p.info()["n_regions"] == 128 * 2 * 2 + 128
+    # gate/up rows of 7168 elements fit one 8192-element MXFP8 work unit
+    assert p.info()["n_regions"] == 128 * 2 + 128
 
 
 def test_algorithmic_bytes():
