@@ -18,9 +18,13 @@
 //  tiny  regions of at most a few hundred bytes: one lane per region, a
 //        wave-level prefix sum of their granule counts, then all 64 lanes
 //        share the wave's granules.
-//  mx    BF16 -> MXFP8 install: four lanes per 32-element block (8 bf16 = 16
-//        bytes each), integer amax, integer round-to-nearest-even E4M3
-//        encoding, 8 code bytes per lane and one scale byte per block.
+//  mx    BF16 -> MXFP8 install.  A work unit (whole rows or one row segment,
+//        at most 16 KB of bf16) is loaded straight into LDS with 16-byte
+//        direct-to-LDS loads, so the data takes no VGPRs and eight
+//        workgroups per CU keep their loads in flight.  Then two lanes per
+//        32-element block: integer amax, exact scaled E4M3 conversion, 16
+//        code bytes per lane; the block scales are gathered in LDS and
+//        written by consecutive lanes at the end.
 //
 // Fan-out: a region may name up to 16 destination replicas; the data is read
 // once and stored to each (the one-GPU analogue of serving every replica from
@@ -534,38 +538,39 @@ __device__ __forceinline__ uint32_t e4m3x4(uint32_t w0, uint32_t w1, uint32_t m0
 #ifndef RS_MX_LDS_AUX
 #define RS_MX_LDS_AUX 2    // cache policy of the direct-to-LDS loads (2: non-temporal)
 #endif
-#ifndef RS_MX_SC_STAGE
-#define RS_MX_SC_STAGE 1   // 1: block scales gathered in LDS, stored by consecutive lanes at the end
-#endif
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Block codes of one lane's 8-element group x (bf16 pairs; zeros past the
-// row end).  The four consecutive lanes of a block call this together: the
-// block's amax is reduced across them with DPP quad permutes.
+// Block codes of one lane's two adjacent 8-element groups xa, xb (bf16
+// pairs, 16 elements, half a block; zeros past the row end).  The two lanes
+// of a block call this together: the block's amax is exchanged between them
+// with a DPP quad permute.
 struct MxCodes {
-  uint32_t lo, hi;   // E4M3 codes of elements 0-3 and 4-7
+  u32x4 v;           // E4M3 codes of the 16 elements, element i in byte i
   uint8_t scale;     // E8M0 block scale
 };
 
-__device__ __forceinline__ MxCodes mx_encode(u32x4 x) {
-  const uint32_t w0 = x.x, w1 = x.y, w2 = x.z, w3 = x.w;
-  const uint32_t m0 = w0 & 0x7FFF7FFFu, m1 = w1 & 0x7FFF7FFFu;
-  const uint32_t m2 = w2 & 0x7FFF7FFFu, m3 = w3 & 0x7FFF7FFFu;
-  const uint32_t mm = pk_max_u16(pk_max_u16(m0, m1), pk_max_u16(m2, m3));
+__device__ __forceinline__ MxCodes mx_encode(u32x4 xa, u32x4 xb) {
+  const uint32_t a0 = xa.x & 0x7FFF7FFFu, a1 = xa.y & 0x7FFF7FFFu, a2 = xa.z & 0x7FFF7FFFu,
+                 a3 = xa.w & 0x7FFF7FFFu;
+  const uint32_t b0 = xb.x & 0x7FFF7FFFu, b1 = xb.y & 0x7FFF7FFFu, b2 = xb.z & 0x7FFF7FFFu,
+                 b3 = xb.w & 0x7FFF7FFFu;
+  const uint32_t mm = pk_max_u16(pk_max_u16(pk_max_u16(a0, a1), pk_max_u16(a2, a3)),
+                                 pk_max_u16(pk_max_u16(b0, b1), pk_max_u16(b2, b3)));
   uint32_t amax = max(mm & 0xFFFFu, mm >> 16);
-  // quad_perm [1,0,3,2] then [2,3,0,1]
+  // quad_perm [1,0,3,2]: the partner lane holds the other half of the block
   amax = max(amax, uint32_t(__builtin_amdgcn_update_dpp(0, int(amax), 0xB1, 0xF, 0xF, true)));
-  amax = max(amax, uint32_t(__builtin_amdgcn_update_dpp(0, int(amax), 0x4E, 0xF, 0xF, true)));
   const bool bad = amax >= 0x7F80u;   // a NaN or Inf in the block
   const int X = shared_exp(amax);
   const uint32_t T = (uint32_t(X + 135) << 7) | 0x60u;   // bf16 bits of 448 * 2^X
   const uint32_t T2 = T | (T << 16);
   const float sc = __builtin_amdgcn_ldexpf(1.0f, X);
   MxCodes c;
-  c.lo = e4m3x4(w0, w1, m0, m1, T2, sc);
-  c.hi = e4m3x4(w2, w3, m2, m3, T2, sc);
-  if (bad) c.lo = c.hi = 0x7F7F7F7Fu;
+  c.v.x = e4m3x4(xa.x, xa.y, a0, a1, T2, sc);
+  c.v.y = e4m3x4(xa.z, xa.w, a2, a3, T2, sc);
+  c.v.z = e4m3x4(xb.x, xb.y, b0, b1, T2, sc);
+  c.v.w = e4m3x4(xb.z, xb.w, b2, b3, T2, sc);
+  if (bad) c.v = u32x4{0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu};
   c.scale = bad ? uint8_t(0xFF) : uint8_t(X + 127);
   return c;
 }
@@ -617,41 +622,32 @@ __device__ __forceinline__ void mx_unit(const LaunchArgs& a, const MxRegion* R, 
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // Phase 2: quantise slot by slot (a quad of lanes per block) and store
-  // 8 code bytes per lane to every replica.
+  // Phase 2: each lane quantises two adjacent slots (a pair of lanes per
+  // block) and stores their 16 code bytes to every replica.
 #pragma unroll
-  for (uint32_t k = 0; k < K; ++k) {
-    const uint32_t s = k * kThreads + tid;
+  for (uint32_t k = 0; k < K / 2; ++k) {
+    const uint32_t s = 2 * (k * kThreads + tid);
     const uint32_t rl = s >> lg, g = s & (Lp - 1u);
     const uint32_t col = g * 8u;
-    const int nvalid = rl < nr ? int(min(inner, col + 8u)) - int(min(inner, col)) : 0;
-    const u32x4 x = nvalid > 0 ? stage[s] : u32x4{0u, 0u, 0u, 0u};
-    const MxCodes c = mx_encode(x);
+    const int nvalid = rl < nr ? int(min(inner, col + 16u)) - int(min(inner, col)) : 0;
+    const u32x4 xa = nvalid > 0 ? stage[s] : u32x4{0u, 0u, 0u, 0u};
+    const u32x4 xb = nvalid > 8 ? stage[s + 1] : u32x4{0u, 0u, 0u, 0u};
+    const MxCodes c = mx_encode(xa, xb);
     if (nvalid > 0) {
       const uint64_t doff = R->dst_off + (kOneRow ? do1 : row_off(r0 + rl, e0, e1, nouter, d0, d1, d2)) + col;
       for (uint32_t j = 0; j < nd; ++j) {
         char* d = static_cast<char*>(a.ptr[R->dst_ptr[j]]) + doff;
-        if (nvalid == 8 && (reinterpret_cast<uintptr_t>(d) & 7u) == 0) {
-          u32x2 v;
-          v.x = c.lo;
-          v.y = c.hi;
-          __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(d));
+        if (nvalid == 16 && (reinterpret_cast<uintptr_t>(d) & 15u) == 0) {
+          __builtin_nontemporal_store(c.v, reinterpret_cast<u32x4*>(d));
         } else {
-          for (int i = 0; i < 8; ++i)
-            if (i < nvalid) d[i] = char(((i < 4 ? c.lo : c.hi) >> (8 * (i & 3))) & 0xFFu);
+          const uint32_t w[4] = {c.v.x, c.v.y, c.v.z, c.v.w};
+          for (int i = 0; i < 16; ++i)
+            if (i < nvalid) d[i] = char((w[i >> 2] >> (8 * (i & 3))) & 0xFFu);
         }
       }
-      if ((g & 3u) == 0) {
-#if RS_MX_SC_STAGE
-        sc_stage[s >> 2] = c.scale;
-#else
-        const uint64_t so = R->sc_off + row_off(r0 + rl, e0, e1, nouter, c0, c1, c2) + uint64_t(g >> 2) * sc_inner;
-        for (uint32_t j = 0; j < nd; ++j) *(static_cast<char*>(a.ptr[R->sc_ptr[j]]) + so) = char(c.scale);
-#endif
-      }
+      if ((g & 3u) == 0) sc_stage[s >> 2] = c.scale;
     }
   }
-#if RS_MX_SC_STAGE
   // Phase 3: the unit's block scales, block b of row i at LDS byte
   // (i << lg) / 4 + b, written by consecutive lanes.
   __syncthreads();
@@ -661,13 +657,9 @@ __device__ __forceinline__ void mx_unit(const LaunchArgs& a, const MxRegion* R, 
     if (rl < nr && b < nb) {
       const uint64_t so = R->sc_off + row_off(r0 + rl, e0, e1, nouter, c0, c1, c2) + uint64_t(b) * sc_inner;
       const char v = char(sc_stage[t]);
-      for (uint32_t j = 0; j < nd; ++j) *(static_cast<char*>(a.ptr[R->sc_ptr[j]]) + so) = v;
+      for (uint32_t j = 0; j < nd; ++j) __builtin_nontemporal_store(v, static_cast<char*>(a.ptr[R->sc_ptr[j]]) + so);
     }
   }
-#else
-  (void)sc_stage;
-  (void)c0; (void)c1; (void)c2; (void)sc_inner;
-#endif
 }
 
 __global__ __launch_bounds__(kThreads, RS_MX_MIN_WAVES) void rs_mx_kernel(LaunchArgs a) {
