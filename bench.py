@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "rs_bulk_kernel_moe_dsv3_counters.json")
+PROFILE_COUNTERS_MX = os.path.join(ROOT, "profiles", "rs_mx_kernel_moe_dsv3_mxfp8_counters.json")
 KERNEL_SOURCE = os.path.join(ROOT, "rl_weight_refit_amd", "csrc", "kernels.hip")
 
 
@@ -430,6 +431,21 @@ def main():
         if c.get("kernel_source_sha256_16") == kernel_hash() and c.get("kernel") == dominant:
             traffic = c.get("traffic_bytes_per_launch")
 
+    # The MXFP8 kernel's own roofline (its plan takes two launches per
+    # execute; achieved is per execute, from the same HIP events).
+    roof_mx = None
+    if do_mx:
+        ach_mx = bytes_mx / (statistics.mean(t_mx) * 1e-3) / 1e9
+        traffic_mx = None
+        if os.path.exists(PROFILE_COUNTERS_MX):
+            with open(PROFILE_COUNTERS_MX) as f:
+                c = json.load(f)
+            if c.get("kernel_source_sha256_16") == kernel_hash():
+                traffic_mx = c.get("traffic_bytes_per_execute")
+        roof_mx = {"kernel": "rs_mx_kernel", "bound": "hbm", "achieved": round(ach_mx, 1),
+                   "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach_mx / HBM_PEAK_GBPS, 4),
+                   "traffic": traffic_mx, "per": "execute (%d launches)" % i_mx["n_launches"]}
+
     out = {
         "metric": "reshard effective HBM GB/s (read+write) and % of MI355X HBM peak; plan us",
         "value": round(value, 1),
@@ -460,6 +476,7 @@ def main():
         "roofline": {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
+        "roofline_mxfp8": roof_mx,
         "device": torch.cuda.get_device_name(0),
     }
     del src, d_copy, d_mx
