@@ -295,19 +295,37 @@ def secondary(torch, binding, stream):
     return out
 
 
-def cpu_baseline():
+def host_info():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "cpu_model": model}
+
+
+def cpu_baseline(experts=16, threads=6):
     """The oracle (as it stands) on a bounded sample of the same workload: the
-    same layer shape and meshes with 16 experts instead of 256 (1/16 of the
-    bytes), bf16 relayout plus MXFP8 install, on the host."""
+    same layer shape and meshes with `experts` experts instead of 256, bf16
+    relayout plus MXFP8 install, on the host.  Timed once with the six oracle
+    calls (3 tensors x 2 variants) one after another on one core, and once
+    with the same calls spread over a thread pool (numpy releases the GIL in
+    its copies).  Returns (single, threaded)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from oracle import golden as ogolden
     from rl_weight_refit_amd import synth
     import helpers  # test-side glue: oracle inputs from a workload
 
+    jobs = []
     total_bytes = 0
-    elapsed = 0.0
     for quant in (None, "mxfp8"):
-        wl = synth.moe_experts(16, 7168, 2048, 16, 8, 8, seed=5, quant=quant)
+        wl = synth.moe_experts(experts, 7168, 2048, 16, 8, 8, seed=5, quant=quant)
         for t in wl["tensors"]:
             G = synth.host_values(t)
             src = helpers.source_buffers(t, G)
@@ -315,17 +333,32 @@ def cpu_baseline():
             one = dict(wl)
             one["tensors"] = [t]
             _, per = helpers.alloc_destinations(one)
-            t0 = time.perf_counter()
-            ogolden.reshard(helpers.src_desc_for(t), helpers.odesc(t, "dst"), src, per[0])
-            elapsed += time.perf_counter() - t0
+            jobs.append((helpers.src_desc_for(t), helpers.odesc(t, "dst"), src, per[0]))
             n = int(np.prod(t["shape"]))
             # bf16 relayout: 2n read + 2n written; MXFP8: 2n read + n codes + n/32 scales
             total_bytes += 4 * n if quant is None else 3 * n + n // 32
-            del src, per
-    return {"value": round(total_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": "same layer shape and meshes with 16 of 256 experts (1/16 of the bytes), "
-                      "bf16 relayout + MXFP8 install, numpy on the host, %.1f s" % elapsed}
+
+    def run(job):
+        ogolden.reshard(*job)
+
+    t0 = time.perf_counter()
+    for job in jobs:
+        run(job)
+    single = time.perf_counter() - t0
+    nthr = min(threads, len(jobs))
+    with ThreadPoolExecutor(max_workers=nthr) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(run, jobs))
+        threaded = time.perf_counter() - t0
+    sample = ("same layer shape and meshes with %d of 256 experts (%d/256 of the bytes), bf16 relayout + "
+              "MXFP8 install, numpy on the host" % (experts, experts))
+    one = {"value": round(total_bytes / single / 1e9, 4), "unit": "GB/s", "cores": 1,
+           "kind": "oracle", "sample": sample + ", one call after another, %.1f s" % single}
+    many = {"value": round(total_bytes / threaded / 1e9, 4), "unit": "GB/s", "cores": nthr,
+            "kind": "oracle", "sample": sample + ", the %d oracle calls (tensor x variant) on a thread "
+                                                 "pool of %d, %.1f s" % (len(jobs), nthr, threaded),
+            "host": host_info()}
+    return one, many
 
 
 def main():
@@ -487,7 +520,7 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("cpu baseline ...", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline()
+        out["cpu_baseline"], out["cpu_baseline_threads"] = cpu_baseline()
     print(json.dumps(out), flush=True)
     return 0
 
