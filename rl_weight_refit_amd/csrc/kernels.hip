@@ -582,7 +582,7 @@ __device__ __forceinline__ MxCodes mx_encode(u32x4 xa, u32x4 xb) {
 template <bool kOneRow>
 __device__ __forceinline__ void mx_unit(const LaunchArgs& a, const MxRegion* R, uint32_t r0, uint32_t nr,
                                         u32x4* stage, uint8_t* sc_stage) {
-  constexpr uint32_t K = kMxSlots / kThreads;
+  constexpr uint32_t K = kMxSlots / kMxThreads;
   const uint32_t tid = threadIdx.x;
   const uint64_t s0 = R->sstr[0], s1 = R->sstr[1], s2 = R->sstr[2];
   const uint64_t d0 = R->dstr[0], d1 = R->dstr[1], d2 = R->dstr[2];
@@ -601,13 +601,13 @@ __device__ __forceinline__ void mx_unit(const LaunchArgs& a, const MxRegion* R, 
   // gathered element by element (zero-filled) and written by its lane.
 #pragma unroll
   for (uint32_t k = 0; k < K; ++k) {
-    const uint32_t s = k * kThreads + tid;
+    const uint32_t s = k * kMxThreads + tid;
     const uint32_t rl = s >> lg, g = s & (Lp - 1u);
     if (rl < nr && g < ng) {
       const char* p = sp + (kOneRow ? so1 : row_off(r0 + rl, e0, e1, nouter, s0, s1, s2)) +
                       uint64_t(g) * 16u;
       if (g * 8u + 8u <= inner && (reinterpret_cast<uintptr_t>(p) & 15u) == 0) {
-        __builtin_amdgcn_global_load_lds(p, (lds_void*)(stage + k * kThreads + (tid & ~63u)), 16, 0,
+        __builtin_amdgcn_global_load_lds(p, (lds_void*)(stage + k * kMxThreads + (tid & ~63u)), 16, 0,
                                          RS_MX_LDS_AUX);
       } else {
         const uint16_t* q = reinterpret_cast<const uint16_t*>(p);
@@ -626,7 +626,7 @@ __device__ __forceinline__ void mx_unit(const LaunchArgs& a, const MxRegion* R, 
   // block) and stores their 16 code bytes to every replica.
 #pragma unroll
   for (uint32_t k = 0; k < K / 2; ++k) {
-    const uint32_t s = 2 * (k * kThreads + tid);
+    const uint32_t s = 2 * (k * kMxThreads + tid);
     const uint32_t rl = s >> lg, g = s & (Lp - 1u);
     const uint32_t col = g * 8u;
     const int nvalid = rl < nr ? int(min(inner, col + 16u)) - int(min(inner, col)) : 0;
@@ -652,7 +652,7 @@ __device__ __forceinline__ void mx_unit(const LaunchArgs& a, const MxRegion* R, 
   // (i << lg) / 4 + b, written by consecutive lanes.
   __syncthreads();
   const uint32_t nb = (inner + 31u) >> 5;
-  for (uint32_t t = tid; t < kMxSlots / 4; t += kThreads) {
+  for (uint32_t t = tid; t < kMxSlots / 4; t += kMxThreads) {
     const uint32_t rl = t >> (lg - 2), b = t & ((Lp >> 2) - 1u);
     if (rl < nr && b < nb) {
       const uint64_t so = R->sc_off + row_off(r0 + rl, e0, e1, nouter, c0, c1, c2) + uint64_t(b) * sc_inner;
@@ -662,7 +662,7 @@ __device__ __forceinline__ void mx_unit(const LaunchArgs& a, const MxRegion* R, 
   }
 }
 
-__global__ __launch_bounds__(kThreads, RS_MX_MIN_WAVES) void rs_mx_kernel(LaunchArgs a) {
+__global__ __launch_bounds__(kMxThreads, RS_MX_MIN_WAVES) void rs_mx_kernel(LaunchArgs a) {
   __shared__ u32x4 stage[kMxSlots];
   __shared__ uint8_t sc_stage[kMxSlots / 4];
   const uint32_t unit = unit_of_block<RS_MX_XCD_MAP != 0>(blockIdx.x, gridDim.x, RS_XCD_CHUNK);
@@ -701,7 +701,7 @@ hipError_t launch(uint32_t bucket, uint32_t grid, const LaunchArgs& args, hipStr
     }
     case kThin: hipLaunchKernelGGL(rs_thin_kernel, dim3(grid), dim3(kThreads), 0, stream, args); break;
     case kTiny: hipLaunchKernelGGL(rs_tiny_kernel, dim3(grid), dim3(kThreads), 0, stream, args); break;
-    case kMx: hipLaunchKernelGGL(rs_mx_kernel, dim3(grid), dim3(kThreads), 0, stream, args); break;
+    case kMx: hipLaunchKernelGGL(rs_mx_kernel, dim3(grid), dim3(kMxThreads), 0, stream, args); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -21,9 +21,13 @@ constexpr uint32_t kChunkShift = 8;   // the unit table holds the region of ever
 #ifndef RS_MX_SLOTS
 #define RS_MX_SLOTS 1024
 #endif
+#ifndef RS_MX_THREADS
+#define RS_MX_THREADS 256
+#endif
 constexpr uint32_t kMxSlots = RS_MX_SLOTS;
+constexpr uint32_t kMxThreads = RS_MX_THREADS;   // threads per MXFP8 workgroup
 constexpr uint32_t kMxBatchElems = kMxSlots * 8;
-static_assert(kMxSlots >= uint32_t(kThreads) && kMxSlots % kThreads == 0, "whole slots per lane");
+static_assert(kMxThreads % 64 == 0 && kMxSlots % (2 * kMxThreads) == 0, "whole slot pairs per lane");
 
 constexpr uint32_t mx_slot_shift(uint32_t inner) {
   uint32_t s = 2;
