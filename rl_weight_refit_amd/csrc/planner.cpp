@@ -120,6 +120,38 @@ void dense_view(const Interval* box, int ndim, int64_t last_div, rs_view* v) {
   }
 }
 
+// Every byte count and byte offset of a plan stays below 2^62, so sums and
+// products of them cannot overflow 64-bit arithmetic.
+constexpr int64_t kMaxBytes = int64_t(1) << 62;
+constexpr int64_t kMaxPtrs = int64_t(1) << 31;   // buffer pointers per side of a tensor
+
+// True when prod(shape) * esize < 2^62 (zero extents ignored, so the dense
+// strides of any box of the tensor stay below the bound too).
+bool fits_bytes(const int64_t* shape, int ndim, int64_t esize) {
+  int64_t v = esize;
+  for (int i = 0; i < ndim; ++i) {
+    if (shape[i] == 0) continue;
+    if (v >= kMaxBytes / shape[i]) return false;
+    v *= shape[i];
+  }
+  return v < kMaxBytes;
+}
+
+// True when the highest byte the view addresses for a box (last extent
+// divided by last_div, rounded up; dim 0 skipped for split parts) is below
+// 2^62.  Negative fields are reported separately and pass here.
+bool view_fits(const rs_view& v, const Interval* box, int ndim, bool split, int64_t last_div,
+               int64_t esize) {
+  unsigned __int128 hi = v.base > 0 ? uint64_t(v.base) : 0;
+  for (int i = split ? 1 : 0; i < ndim; ++i) {
+    int64_t n = box[i].len;
+    if (i == ndim - 1 && last_div > 1) n = (n + last_div - 1) / last_div;
+    if (n == 0) return true;   // an empty box addresses nothing
+    if (v.strides[i] > 0) hi += (unsigned __int128)(n - 1) * uint64_t(v.strides[i]);
+  }
+  return (hi + 1) * uint64_t(esize) < (unsigned __int128)kMaxBytes;
+}
+
 bool parse_layout(const rs_tensor_desc* d, const char* side, int t, bool is_dst, Layout& L,
                   Errors& E) {
   const int before = E.invalid;
@@ -135,10 +167,17 @@ bool parse_layout(const rs_tensor_desc* d, const char* side, int t, bool is_dst,
   L.dtype = d->dtype;
   L.esize = esize_of(d->dtype);
   if (!L.esize) E.add(&E.invalid, "tensor ", t, " ", side, ": unknown dtype ", d->dtype);
+  bool shape_ok = true;
   for (int i = 0; i < L.ndim; ++i) {
     L.shape[i] = d->global_shape[i];
-    if (L.shape[i] < 0)
+    if (L.shape[i] < 0) {
       E.add(&E.invalid, "tensor ", t, " ", side, ": global_shape[", i, "] = ", L.shape[i], " < 0");
+      shape_ok = false;
+    }
+  }
+  if (shape_ok && !fits_bytes(L.shape, L.ndim, L.esize ? L.esize : 1)) {
+    E.add(&E.invalid, "tensor ", t, " ", side, ": the global tensor holds 2^62 bytes or more");
+    shape_ok = false;
   }
   if (d->mesh_ndim < 1 || d->mesh_ndim > RS_MAX_MESH) {
     E.add(&E.invalid, "tensor ", t, " ", side, ": mesh_ndim ", d->mesh_ndim, " not in [1, ",
@@ -155,7 +194,7 @@ bool parse_layout(const rs_tensor_desc* d, const char* side, int t, bool is_dst,
       E.add(&E.invalid, "tensor ", t, " ", side, ": mesh_shape[", i, "] = ", L.mesh[i], " < 1");
       mesh_ok = false;
     } else if (L.nslots <= kMaxSlots) {
-      L.nslots *= L.mesh[i];
+      L.nslots = L.mesh[i] > kMaxSlots ? kMaxSlots + 1 : L.nslots * L.mesh[i];
     }
     if (L.pl[i] != RS_REPLICATE && (L.pl[i] < 0 || L.pl[i] >= L.ndim))
       E.add(&E.invalid, "tensor ", t, " ", side, ": placements[", i, "] = ", L.pl[i],
@@ -185,6 +224,7 @@ bool parse_layout(const rs_tensor_desc* d, const char* side, int t, bool is_dst,
     L.slot_to_coord[s] = static_cast<int32_t>(c);
   }
 
+  if (!shape_ok) return false;
   for (int i = 0; i < L.mesh_ndim; ++i) {
     if (L.pl[i] == RS_REPLICATE) {
       L.rep_md.push_back(i);
@@ -229,6 +269,10 @@ bool parse_layout(const rs_tensor_desc* d, const char* side, int t, bool is_dst,
   for (int64_t s = 0; s < L.nslots; ++s) {
     L.ptr_base[s] = L.nptrs;
     L.nptrs += L.split ? L.slot_box(s)[0].len : 1;
+    if (L.nptrs > kMaxPtrs) {
+      E.add(&E.invalid, "tensor ", t, " ", side, ": more than ", kMaxPtrs, " buffer pointers");
+      return false;
+    }
   }
   L.views.resize(L.nslots);
   for (int64_t s = 0; s < L.nslots; ++s) {
@@ -239,6 +283,8 @@ bool parse_layout(const rs_tensor_desc* d, const char* side, int t, bool is_dst,
       for (int i = 0; i < L.ndim; ++i)
         if (L.views[s].strides[i] < 0)
           E.add(&E.invalid, "tensor ", t, " ", side, ": views[", s, "].strides[", i, "] < 0");
+      if (!view_fits(L.views[s], L.slot_box(s), L.ndim, L.split, 1, L.esize ? L.esize : 1))
+        E.add(&E.invalid, "tensor ", t, " ", side, ": views[", s, "] reaches 2^62 bytes or more");
     } else {
       dense_view(L.slot_box(s), L.ndim, 1, &L.views[s]);
     }
@@ -253,6 +299,8 @@ bool parse_layout(const rs_tensor_desc* d, const char* side, int t, bool is_dst,
         for (int i = 0; i < L.ndim; ++i)
           if (L.scale_views[s].strides[i] < 0)
             E.add(&E.invalid, "tensor ", t, " ", side, ": scale_views[", s, "].strides[", i, "] < 0");
+        if (!view_fits(L.scale_views[s], L.slot_box(s), L.ndim, L.split, kMxBlock, 1))
+          E.add(&E.invalid, "tensor ", t, " ", side, ": scale_views[", s, "] reaches 2^62 bytes or more");
       } else {
         dense_view(L.slot_box(s), L.ndim, kMxBlock, &L.scale_views[s]);
       }

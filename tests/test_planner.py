@@ -245,6 +245,36 @@ def test_every_violation_is_reported():
     assert "global_shape[1]" in msg and "dtype" in msg
 
 
+@pytest.mark.parametrize("field,value,needle", [
+    ("shape", [1 << 40, 1 << 22], "2^62 bytes"),
+    ("shape", [1 << 62, 1], "2^62 bytes"),
+    ("mesh", [3, 1 << 62], "slots"),
+    ("mesh", [1 << 62], "slots"),
+])
+def test_sizes_past_the_64_bit_range_are_rejected(field, value, needle):
+    """Extents and mesh sizes whose products would overflow 64-bit byte
+    arithmetic are reported, not planned."""
+    src = {"shape": [8, 8], "dtype": "bf16", "mesh": [2], "placements": [0]}
+    dst = dict(src)
+    if field == "shape":
+        src = dict(src, shape=value)
+        dst = dict(dst, shape=value)
+    else:
+        src = dict(src, mesh=value, placements=[-1] * len(value))
+    with pytest.raises(binding.ReshardError) as e:
+        binding.reshard_plan([src], [dst])
+    assert e.value.status == 1 and needle in str(e.value)
+
+
+def test_view_reaching_past_the_64_bit_range_is_rejected():
+    src = {"shape": [8, 8], "dtype": "f32", "mesh": [2], "placements": [0]}
+    dst = {"shape": [8, 8], "dtype": "f32", "mesh": [2], "placements": [0],
+           "views": [(0, [1 << 61, 1]), (0, [8, 1])]}
+    with pytest.raises(binding.ReshardError) as e:
+        binding.reshard_plan([src], [dst])
+    assert e.value.status == 1 and "views[0]" in str(e.value)
+
+
 def test_mxfp8_block_spanning_sources_is_unsupported():
     src = {"shape": [4, 100], "dtype": "bf16", "mesh": [2], "placements": [1]}
     dst = {"shape": [4, 100], "dtype": "u8", "mesh": [1], "placements": [-1], "quant": "mxfp8"}
