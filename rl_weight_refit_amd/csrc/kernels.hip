@@ -90,7 +90,7 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) {
 #define RS_XCD_MAP 1     // bulk kernel: 1 = map workgroups so each XCD walks its own units
 #endif
 #ifndef RS_XCD_CHUNK
-#define RS_XCD_CHUNK 0   // units per XCD turn (0: one contiguous eighth per XCD)
+#define RS_XCD_CHUNK 4096   // units per XCD turn (0: one contiguous eighth per XCD)
 #endif
 #ifndef RS_MX_XCD_MAP
 #define RS_MX_XCD_MAP 0  // MXFP8 kernel: same choice
@@ -99,7 +99,10 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) {
 // Work unit of workgroup b out of n.  Workgroups are dispatched round-robin
 // over the 8 XCDs (b -> XCD b % 8), each with its own L2.  Remapped, XCD x
 // takes runs of `chunk` consecutive units in turn (or, with chunk 0, one
-// contiguous eighth of all units), so neighbouring units stay on one XCD.
+// contiguous eighth of all units), so neighbouring units stay on one XCD;
+// taking turns keeps every XCD's share a mix of the plan's regions, so an
+// XCD that drew only the slower regions does not finish last.  Units past
+// the last whole round of 8 chunks keep their order.
 template <bool kMap>
 __device__ __forceinline__ uint32_t unit_of_block(uint32_t b, uint32_t n, uint32_t chunk) {
   if (!kMap) return b;
