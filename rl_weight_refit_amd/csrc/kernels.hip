@@ -249,6 +249,47 @@ __device__ __forceinline__ void bulk_short_rows(const LaunchArgs& a, const CopyR
   }
 }
 
+#ifndef RS_SHORT_FLAT
+#define RS_SHORT_FLAT 1   // 1: short aligned rows use the flat vector numbering below
+#endif
+
+// Short aligned rows of a region with at most one outer dim (row r at
+// r * stride on each side), numbered flat: vector f = i * vpr + v (row
+// r0 + i, vector v of it).  Lane tid takes f = f0 + tid + k * kThreads, so
+// every lane loads RS_UNROLL vectors and a unit of up to RS_UNROLL * kThreads
+// vectors is one load batch, whatever vpr is.  The row is floor(f / vpr),
+// computed as (f * ceil(2^32 / vpr)) >> 32: exact for f < 2^20 and vpr < 2^11
+// (the error term f / 2^32 stays below the smallest gap 1 / vpr).
+template <bool kFan1>
+__device__ __forceinline__ void bulk_short_flat(const LaunchArgs& a, const CopyRegion* R,
+                                                const char* sp, uint64_t dst_off, uint32_t r0,
+                                                uint32_t r1, uint32_t vpr, uint64_t s0, uint64_t d0,
+                                                uint32_t nd) {
+  constexpr int U = RS_UNROLL;
+  const uint32_t tid = threadIdx.x;
+  const uint64_t magic = ((uint64_t(1) << 32) + vpr - 1) / vpr;
+  const uint32_t nvec = (r1 - r0) * vpr;
+  for (uint32_t f0 = 0; f0 < nvec; f0 += U * kThreads) {
+    u32x4 x[U];
+    uint64_t o[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const uint32_t f = f0 + k * kThreads + tid;
+      const uint32_t i = uint32_t((uint64_t(f) * magic) >> 32);
+      const uint32_t r = r0 + i;
+      const uint32_t v = f - i * vpr;
+      o[k] = uint64_t(r) * d0 + 16ull * v;
+      if (f < nvec) x[k] = ld16(sp + uint64_t(r) * s0 + 16ull * v);
+    }
+    for (uint32_t j = 0; j < nd; ++j) {
+      char* d = static_cast<char*>(a.ptr[R->dst_ptr[kFan1 ? 0 : j]]) + dst_off;
+#pragma unroll
+      for (int k = 0; k < U; ++k)
+        if (f0 + k * kThreads + tid < nvec) st16(d + o[k], x[k]);
+    }
+  }
+}
+
 template <bool kFan1>
 __device__ __forceinline__ void bulk_body(const LaunchArgs& a, const CopyRegion* R, uint32_t unit) {
   const uint32_t tid = threadIdx.x;
@@ -319,6 +360,12 @@ __device__ __forceinline__ void bulk_body(const LaunchArgs& a, const CopyRegion*
     // most 64), 64 / L rows per wave step; each lane moves one or two
     // vectors of each of several rows per iteration.
     const uint32_t vpr = inner >> 4;
+#if RS_SHORT_FLAT
+    if (nouter <= 1) {
+      bulk_short_flat<kFan1>(a, R, sp, dst_off, r0, r1, vpr, s0, d0, nd);
+      return;
+    }
+#endif
     uint32_t L = 1;
     while (L < vpr && L < 64u) L <<= 1;
     if (vpr > L)
