@@ -11,6 +11,8 @@
 //        runs on the scalar unit), short rows are split among sub-wave lane
 //        groups.  Otherwise each wave copies one row at the widest granule the
 //        source/destination co-alignment allows, with byte head and tail.
+//        Launched so that at most five workgroups share a CU (see
+//        bulk_lds_pad): fewer streams concurrently per CU copy faster.
 //  thin  runs shorter than the thin threshold (e.g. the 8-byte rows of a
 //        column shard): rows are gathered through an LDS tile so the side
 //        that is contiguous across rows is written (or read) with 16-byte
@@ -33,6 +35,8 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+
+#include <atomic>
 
 #include "rs_device.hpp"
 
@@ -731,6 +735,36 @@ __global__ __launch_bounds__(kMxThreads, RS_MX_MIN_WAVES) void rs_mx_kernel(Laun
 #define RS_BULK_WG_PER_CU 0   // 0: one workgroup per unit; n > 0: persistent grid of n per CU
 #endif
 
+// Bulk workgroups resident per CU.  The copy streams best with fewer than
+// the register file would allow (on MI355X 4-5 per CU beat 7, and 3 or 6 are
+// slower), so each bulk launch asks for enough dynamic LDS, which the kernel
+// never touches, to leave room for only this many.  0 = no cap.
+#ifndef RS_BULK_RESIDENT
+#define RS_BULK_RESIDENT 5
+#endif
+constexpr int kMaxDevices = 64;
+
+// Dynamic LDS bytes per bulk workgroup on the current device (cached).
+size_t bulk_lds_pad() {
+  static std::atomic<int> cache[kMaxDevices];   // 0: not yet known; else pad + 1
+  if (RS_BULK_RESIDENT <= 0) return 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return size_t(c - 1);
+  }
+  int per_cu = 0, per_wg = 0;
+  if (hipDeviceGetAttribute(&per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
+      hipDeviceGetAttribute(&per_wg, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+      per_cu <= 0 || per_wg <= 0)
+    return 0;
+  int pad = (per_cu / RS_BULK_RESIDENT) & ~511;
+  if (pad > per_wg) pad = per_wg;
+  if (dev >= 0 && dev < kMaxDevices) cache[dev].store(pad + 1, std::memory_order_relaxed);
+  return size_t(pad);
+}
+
 hipError_t launch(uint32_t bucket, uint32_t grid, const LaunchArgs& args, hipStream_t stream) {
   if (grid == 0) return hipSuccess;
   switch (bucket) {
@@ -746,7 +780,7 @@ hipError_t launch(uint32_t bucket, uint32_t grid, const LaunchArgs& args, hipStr
       }
       g = min(grid, uint32_t(cus) * RS_BULK_WG_PER_CU);
 #endif
-      hipLaunchKernelGGL(rs_bulk_kernel, dim3(g), dim3(kThreads), 0, stream, args);
+      hipLaunchKernelGGL(rs_bulk_kernel, dim3(g), dim3(kThreads), bulk_lds_pad(), stream, args);
       break;
     }
     case kThin: hipLaunchKernelGGL(rs_thin_kernel, dim3(grid), dim3(kThreads), 0, stream, args); break;
