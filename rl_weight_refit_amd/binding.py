@@ -208,7 +208,7 @@ class Plan:
             pass
 
 
-def reshard_plan(src_specs, dst_specs, fanout=True, unit_bytes=16384, tiny_bytes=1024,
+def reshard_plan(src_specs, dst_specs, fanout=True, unit_bytes=16384, tiny_bytes=256,
                  thin_bytes=128):
     """Plan len(src_specs) tensor pairs into one region table."""
     lib = load()

@@ -497,16 +497,55 @@ __device__ __forceinline__ uint32_t region_granule(const LaunchArgs& a, const Co
   return low_granule(al);
 }
 
+// One granule of g bytes (g in {1,2,4,8,16}, p g-aligned) into / out of a
+// 16-byte register.
+__device__ __forceinline__ u32x4 load_granule(const char* p, uint32_t g) {
+  u32x4 v = u32x4{0u, 0u, 0u, 0u};
+  switch (g) {
+    case 16: v = *reinterpret_cast<const u32x4*>(p); break;
+    case 8: {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+      v.x = w.x;
+      v.y = w.y;
+      break;
+    }
+    case 4: v.x = *reinterpret_cast<const uint32_t*>(p); break;
+    case 2: v.x = *reinterpret_cast<const uint16_t*>(p); break;
+    default: v.x = uint8_t(*p); break;
+  }
+  return v;
+}
+__device__ __forceinline__ void store_granule(char* p, uint32_t g, u32x4 v) {
+  switch (g) {
+    case 16: *reinterpret_cast<u32x4*>(p) = v; break;
+    case 8: *reinterpret_cast<u32x2*>(p) = u32x2{v.x, v.y}; break;
+    case 4: *reinterpret_cast<uint32_t*>(p) = v.x; break;
+    case 2: *reinterpret_cast<uint16_t*>(p) = uint16_t(v.x); break;
+    default: *p = char(v.x); break;
+  }
+}
+
+// Each lane owns one region (its granule size and granule count go to LDS);
+// a wave-level inclusive scan of the counts numbers the wave's granules, and
+// the 64 lanes then walk them together, each finding its granule's region by
+// a binary search over the wave's starts, kTinyInFlight granules per lane at
+// a time so their loads overlap.
+constexpr int kTinyInFlight = 4;
+
 __global__ __launch_bounds__(kThreads) void rs_tiny_kernel(LaunchArgs a) {
   __shared__ uint32_t start[kThreads];
+  __shared__ uint32_t gpr_of[kThreads];
+  __shared__ uint8_t gsize[kThreads];
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63u, wave = tid >> 6;
   const CopyRegion* regs = static_cast<const CopyRegion*>(a.regions);
   const uint32_t ri = blockIdx.x * kThreads + tid;
-  uint32_t cnt = 0;
+  uint32_t cnt = 0, g = 1, gpr = 0;
   if (ri < a.n_regions) {
     const CopyRegion* R = regs + ri;
-    cnt = R->rows * (R->inner / region_granule(a, R));
+    g = region_granule(a, R);
+    gpr = R->inner / g;
+    cnt = R->rows * gpr;
   }
   // Inclusive scan of the per-lane granule counts across the wave.
   uint32_t scan = cnt;
@@ -516,29 +555,48 @@ __global__ __launch_bounds__(kThreads) void rs_tiny_kernel(LaunchArgs a) {
   }
   const uint32_t total = __shfl(scan, 63, 64);
   start[tid] = scan - cnt;
+  gpr_of[tid] = gpr;
+  gsize[tid] = uint8_t(g);
   __syncthreads();
   const uint32_t* ws = start + wave * 64;
   const uint32_t base = blockIdx.x * kThreads + wave * 64;
-  for (uint32_t f = lane; f < total; f += 64) {
-    // Last lane whose start <= f (empty regions share starts; take the last).
-    uint32_t lo = 0, hi = 64;
-    while (hi - lo > 1) {
-      const uint32_t mid = (lo + hi) >> 1;
-      if (ws[mid] <= f) lo = mid; else hi = mid;
+  for (uint32_t f0 = lane; f0 < total; f0 += kTinyInFlight * 64) {
+    u32x4 v[kTinyInFlight];
+    uint32_t owner[kTinyInFlight];
+    uint64_t dofs[kTinyInFlight];
+#pragma unroll
+    for (int u = 0; u < kTinyInFlight; ++u) {
+      const uint32_t f = f0 + u * 64;
+      owner[u] = 0;
+      dofs[u] = 0;
+      if (f < total) {
+        // Last lane whose start <= f (empty regions share starts; take the last).
+        uint32_t lo = 0, hi = 64;
+        while (hi - lo > 1) {
+          const uint32_t mid = (lo + hi) >> 1;
+          if (ws[mid] <= f) lo = mid; else hi = mid;
+        }
+        owner[u] = lo;
+        const CopyRegion* R = regs + base + lo;
+        const uint32_t gl = gsize[wave * 64 + lo], gp = gpr_of[wave * 64 + lo];
+        const uint32_t local = f - ws[lo];
+        const uint32_t row = local / gp;
+        const uint32_t k = local - row * gp;
+        const uint32_t nouter = R->flags & kFlagOuterMask;
+        const uint64_t so = row_off(row, R->e0, R->e1, nouter, R->sstr[0], R->sstr[1], R->sstr[2]);
+        dofs[u] = R->dst_off + row_off(row, R->e0, R->e1, nouter, R->dstr[0], R->dstr[1], R->dstr[2]) +
+                  uint64_t(k) * gl;
+        v[u] = load_granule(static_cast<const char*>(a.ptr[R->src_ptr]) + R->src_off + so + uint64_t(k) * gl, gl);
+      }
     }
-    const CopyRegion* R = regs + base + lo;
-    const uint32_t g = region_granule(a, R);
-    const uint32_t gpr = R->inner / g;
-    const uint32_t local = f - ws[lo];
-    const uint32_t row = local / gpr;
-    const uint32_t k = local - row * gpr;
-    const uint32_t nouter = R->flags & kFlagOuterMask;
-    const uint64_t so = row_off(row, R->e0, R->e1, nouter, R->sstr[0], R->sstr[1], R->sstr[2]);
-    const uint64_t dof = row_off(row, R->e0, R->e1, nouter, R->dstr[0], R->dstr[1], R->dstr[2]);
-    const char* s = static_cast<const char*>(a.ptr[R->src_ptr]) + R->src_off + so + uint64_t(k) * g;
-    for (uint32_t j = 0; j < R->n_dst; ++j) {
-      char* d = static_cast<char*>(a.ptr[R->dst_ptr[j]]) + R->dst_off + dof + uint64_t(k) * g;
-      copy_granule(d, s, g);
+#pragma unroll
+    for (int u = 0; u < kTinyInFlight; ++u) {
+      if (f0 + u * 64 < total) {
+        const CopyRegion* R = regs + base + owner[u];
+        const uint32_t gl = gsize[wave * 64 + owner[u]];
+        for (uint32_t j = 0; j < R->n_dst; ++j)
+          store_granule(static_cast<char*>(a.ptr[R->dst_ptr[j]]) + dofs[u], gl, v[u]);
+      }
     }
   }
 }

@@ -429,7 +429,7 @@ void merge_outer(Dims& o, bool with_scale) {
 struct Opts {
   bool fanout = true;
   uint64_t unit = 16384;
-  uint64_t tiny = 1024;
+  uint64_t tiny = 256;
   uint64_t thin = 128;
 };
 

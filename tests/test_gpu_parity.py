@@ -93,6 +93,14 @@ def test_uneven_layouts_bucket_variants(seed, kw):
     gh.check_against_oracle(synth.uneven_case(seed), **kw)
 
 
+@pytest.mark.parametrize("fanout", [True, False])
+@pytest.mark.parametrize("seed", range(0, 500, 25))
+def test_uneven_layouts_through_tiny_kernel(seed, fanout):
+    """Every region up to 64 KiB through the wave-scan kernel: thousands of
+    granules per wave, several granules in flight per lane, replicas."""
+    gh.check_against_oracle(synth.uneven_case(seed), tiny_bytes=1 << 16, fanout=fanout)
+
+
 @pytest.mark.parametrize("shifts", [(4, 0), (0, 2), (6, 10)])
 @pytest.mark.parametrize("seed", range(0, 500, 50))
 def test_uneven_layouts_misaligned(seed, shifts):
@@ -218,17 +226,19 @@ def test_mxfp8_every_bf16_pattern():
     gh.check_against_oracle(wl, globals_=[G])
 
 
+@pytest.mark.parametrize("tiny_bytes", [256, 1024])
 @pytest.mark.parametrize("reverse", [False, True], ids=["pack", "unpack"])
-def test_misc_pack_full_size(reverse):
+def test_misc_pack_full_size(reverse, tiny_bytes):
     """61 layers of small tensors (norms, router, bias) packed into one
-    buffer, and unpacked again: many regions of mixed sizes in one plan, the
-    tiny bucket included."""
+    buffer, and unpacked again: many regions of mixed sizes in one plan.  With
+    a 1 KiB tiny threshold the 1 KiB bias regions go through the wave-scan
+    kernel (many granules per wave)."""
     wl = synth.misc_pack()
     if reverse:
         wl = synth.reverse(wl)
     gh.log(wl["name"])
-    plan = gh.check_against_oracle(wl)
-    assert plan.info()["regions"]["tiny"] > 0
+    plan = gh.check_against_oracle(wl, tiny_bytes=tiny_bytes)
+    assert (plan.info()["regions"]["tiny"] > 0) == (tiny_bytes == 1024)
 
 
 @pytest.mark.parametrize("kw", [{}, {"src_split": True}])
