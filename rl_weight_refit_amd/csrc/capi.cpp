@@ -15,7 +15,8 @@
 #include "rs_device.hpp"
 
 namespace rs {
-hipError_t launch(uint32_t bucket, uint32_t grid, const LaunchArgs& args, hipStream_t stream);
+// Enqueues one launch of a bucket's kernel on `stream`, whose device is `dev`.
+hipError_t launch(uint32_t bucket, uint32_t grid, const LaunchArgs& args, hipStream_t stream, int dev);
 }
 
 struct rs_plan {
@@ -69,9 +70,44 @@ rs_status reshard_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int
   return RS_OK;
 }
 
-rs_status reshard_execute(const rs_plan* plan, void* const* src_ptrs, void* const* dst_ptrs,
-                          void* stream) {
-  g_error.clear();
+}  // extern "C"
+
+namespace {
+
+// Device tables of a plan on `dev`, uploaded on first use (blocking).
+rs_status plan_tables(const rs_plan* plan, int dev, char** base) {
+  std::lock_guard<std::mutex> lock(plan->mu);
+  for (const auto& t : plan->tables)
+    if (t.device == dev) {
+      *base = static_cast<char*>(t.ptr);
+      return RS_OK;
+    }
+  int cur = 0;
+  hipError_t he = hipGetDevice(&cur);
+  if (he != hipSuccess) return fail(RS_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(he) + "\n");
+  if (cur != dev && (he = hipSetDevice(dev)) != hipSuccess)
+    return fail(RS_ERR_HIP, std::string("hipSetDevice: ") + hipGetErrorString(he) + "\n");
+  const std::vector<uint8_t>& img = plan->d.image;
+  void* p = nullptr;
+  rs_status st = RS_OK;
+  std::string msg;
+  he = hipMalloc(&p, img.size());
+  if (he != hipSuccess) {
+    st = RS_ERR_ALLOC;
+    msg = std::string("hipMalloc of the plan tables: ") + hipGetErrorString(he) + "\n";
+  } else if ((he = hipMemcpy(p, img.data(), img.size(), hipMemcpyHostToDevice)) != hipSuccess) {
+    (void)hipFree(p);
+    st = RS_ERR_HIP;
+    msg = std::string("upload of the plan tables: ") + hipGetErrorString(he) + "\n";
+  } else {
+    plan->tables.push_back({dev, p});
+    *base = static_cast<char*>(p);
+  }
+  if (cur != dev) (void)hipSetDevice(cur);
+  return st == RS_OK ? RS_OK : fail(st, msg);
+}
+
+rs_status execute(const rs_plan* plan, void* const* src_ptrs, void* const* dst_ptrs, void* stream) {
   if (!plan) return fail(RS_ERR_INVALID, "plan is NULL\n");
   const rs::PlanData& d = plan->d;
   std::ostringstream err;
@@ -119,28 +155,14 @@ rs_status reshard_execute(const rs_plan* plan, void* const* src_ptrs, void* cons
   if (nerr) return fail(RS_ERR_INVALID, err.str());
   if (d.launches.empty()) return RS_OK;
 
+  // The kernels run on the stream's device, so the tables must live there.
   int dev = 0;
-  hipError_t he = hipGetDevice(&dev);
-  if (he != hipSuccess) return fail(RS_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(he) + "\n");
+  hipError_t he = stream ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev) : hipGetDevice(&dev);
+  if (he != hipSuccess)
+    return fail(RS_ERR_HIP, std::string("device of the stream: ") + hipGetErrorString(he) + "\n");
   char* base = nullptr;
-  {
-    std::lock_guard<std::mutex> lock(plan->mu);
-    for (const auto& t : plan->tables)
-      if (t.device == dev) base = static_cast<char*>(t.ptr);
-    if (!base) {
-      void* p = nullptr;
-      he = hipMalloc(&p, d.image.size());
-      if (he != hipSuccess)
-        return fail(RS_ERR_ALLOC, std::string("hipMalloc of the plan tables: ") + hipGetErrorString(he) + "\n");
-      he = hipMemcpy(p, d.image.data(), d.image.size(), hipMemcpyHostToDevice);
-      if (he != hipSuccess) {
-        (void)hipFree(p);
-        return fail(RS_ERR_HIP, std::string("upload of the plan tables: ") + hipGetErrorString(he) + "\n");
-      }
-      plan->tables.push_back({dev, p});
-      base = static_cast<char*>(p);
-    }
-  }
+  const rs_status ts = plan_tables(plan, dev, &base);
+  if (ts != RS_OK) return ts;
   for (const rs::Launch& L : d.launches) {
     rs::LaunchArgs args;
     std::memset(&args, 0, sizeof(args));
@@ -152,11 +174,25 @@ rs_status reshard_execute(const rs_plan* plan, void* const* src_ptrs, void* cons
       const uint32_t e = L.pool[k];
       args.ptr[k] = (e & rs::kDstBit) ? dst_ptrs[e & ~rs::kDstBit] : src_ptrs[e];
     }
-    he = rs::launch(L.bucket, L.n_units, args, static_cast<hipStream_t>(stream));
+    he = rs::launch(L.bucket, L.n_units, args, static_cast<hipStream_t>(stream), dev);
     if (he != hipSuccess)
       return fail(RS_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(he) + "\n");
   }
   return RS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rs_status reshard_execute(const rs_plan* plan, void* const* src_ptrs, void* const* dst_ptrs,
+                          void* stream) {
+  g_error.clear();
+  try {
+    return execute(plan, src_ptrs, dst_ptrs, stream);
+  } catch (const std::bad_alloc&) {
+    return fail(RS_ERR_ALLOC, "host allocation failed\n");
+  }
 }
 
 rs_status reshard_plan_info(const rs_plan* plan, rs_plan_info* info) {
@@ -177,10 +213,14 @@ rs_status reshard_plan_region(const rs_plan* plan, uint64_t index, rs_region* ou
 rs_status reshard_shard_box(const rs_tensor_desc* desc, int64_t slot, int64_t* offsets,
                             int64_t* lengths) {
   g_error.clear();
-  std::string err;
-  const rs_status st = rs::shard_box(desc, slot, offsets, lengths, err);
-  if (st != RS_OK) return fail(st, err);
-  return RS_OK;
+  try {
+    std::string err;
+    const rs_status st = rs::shard_box(desc, slot, offsets, lengths, err);
+    if (st != RS_OK) return fail(st, err);
+    return RS_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(RS_ERR_ALLOC, "host allocation failed\n");
+  }
 }
 
 void reshard_plan_destroy(rs_plan* plan) {

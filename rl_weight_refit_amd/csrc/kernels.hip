@@ -393,16 +393,13 @@ __device__ __forceinline__ void bulk_body(const LaunchArgs& a, const CopyRegion*
 }
 
 __global__ __launch_bounds__(kThreads, RS_BULK_MIN_WAVES) void rs_bulk_kernel(LaunchArgs a) {
-  // gridDim.x may be smaller than the number of units (a persistent grid):
-  // each workgroup then takes units blockIdx.x, blockIdx.x + gridDim.x, ...
-  for (uint32_t ub = blockIdx.x; ub < a.n_units; ub += gridDim.x) {
-    const uint32_t unit = gridDim.x == a.n_units ? unit_of_block<RS_XCD_MAP != 0>(ub, a.n_units, RS_XCD_CHUNK) : ub;
-    const CopyRegion* R = find_region<CopyRegion>(a, unit);
-    if (R->n_dst == 1)
-      bulk_body<true>(a, R, unit);
-    else
-      bulk_body<false>(a, R, unit);
-  }
+  // One workgroup per work unit (looping workgroups measured slower).
+  const uint32_t unit = unit_of_block<RS_XCD_MAP != 0>(blockIdx.x, gridDim.x, RS_XCD_CHUNK);
+  const CopyRegion* R = find_region<CopyRegion>(a, unit);
+  if (R->n_dst == 1)
+    bulk_body<true>(a, R, unit);
+  else
+    bulk_body<false>(a, R, unit);
 }
 
 // ---------------------------------------------------------------------------
@@ -789,10 +786,6 @@ __global__ __launch_bounds__(kMxThreads, RS_MX_MIN_WAVES) void rs_mx_kernel(Laun
 
 }  // namespace
 
-#ifndef RS_BULK_WG_PER_CU
-#define RS_BULK_WG_PER_CU 0   // 0: one workgroup per unit; n > 0: persistent grid of n per CU
-#endif
-
 // Bulk workgroups resident per CU.  The copy streams best with fewer than
 // the register file would allow (on MI355X 4-5 per CU beat 7, and 3 or 6 are
 // slower), so each bulk launch asks for enough dynamic LDS, which the kernel
@@ -802,12 +795,10 @@ __global__ __launch_bounds__(kMxThreads, RS_MX_MIN_WAVES) void rs_mx_kernel(Laun
 #endif
 constexpr int kMaxDevices = 64;
 
-// Dynamic LDS bytes per bulk workgroup on the current device (cached).
-size_t bulk_lds_pad() {
+// Dynamic LDS bytes per bulk workgroup on device `dev` (cached).
+size_t bulk_lds_pad(int dev) {
   static std::atomic<int> cache[kMaxDevices];   // 0: not yet known; else pad + 1
   if (RS_BULK_RESIDENT <= 0) return 0;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (dev >= 0 && dev < kMaxDevices) {
     const int c = cache[dev].load(std::memory_order_relaxed);
     if (c > 0) return size_t(c - 1);
@@ -823,24 +814,12 @@ size_t bulk_lds_pad() {
   return size_t(pad);
 }
 
-hipError_t launch(uint32_t bucket, uint32_t grid, const LaunchArgs& args, hipStream_t stream) {
+hipError_t launch(uint32_t bucket, uint32_t grid, const LaunchArgs& args, hipStream_t stream, int dev) {
   if (grid == 0) return hipSuccess;
   switch (bucket) {
-    case kBulk: {
-      uint32_t g = grid;
-#if RS_BULK_WG_PER_CU > 0
-      static int cus = 0;
-      if (!cus) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-          cus = 256;
-      }
-      g = min(grid, uint32_t(cus) * RS_BULK_WG_PER_CU);
-#endif
-      hipLaunchKernelGGL(rs_bulk_kernel, dim3(g), dim3(kThreads), bulk_lds_pad(), stream, args);
+    case kBulk:
+      hipLaunchKernelGGL(rs_bulk_kernel, dim3(grid), dim3(kThreads), bulk_lds_pad(dev), stream, args);
       break;
-    }
     case kThin: hipLaunchKernelGGL(rs_thin_kernel, dim3(grid), dim3(kThreads), 0, stream, args); break;
     case kTiny: hipLaunchKernelGGL(rs_tiny_kernel, dim3(grid), dim3(kThreads), 0, stream, args); break;
     case kMx: hipLaunchKernelGGL(rs_mx_kernel, dim3(grid), dim3(kMxThreads), 0, stream, args); break;
