@@ -34,7 +34,8 @@ ELEM_NAN = 0x7F
 def bf16_bits_to_f64(bits):
     """Exact float64 values of bfloat16 bit patterns (uint16 array)."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
-    return b.view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):   # signalling NaN patterns widen to quiet NaNs
+        return b.view(np.float32).astype(np.float64)
 
 
 def floor_log2(x):

@@ -56,11 +56,11 @@ class DevBuf:
         return bool((g == self.poison).all()) and bool((head == self.poison).all())
 
 
-def device_run(workload, sources, per_tensor_dst_host, poison=0xA5, src_shift=0, dst_shift=0,
-               plan=None, stream=None, **plan_kw):
-    """Upload sources, allocate poisoned destinations shaped like the host
-    images, execute the HIP path, return the device buffers in pointer order.
-    """
+def device_buffers(workload, sources, per_tensor_dst_host, poison=0xA5, src_shift=0, dst_shift=0):
+    """Upload sources and allocate poisoned destinations shaped like the host
+    images.  Returns (src_dev, src_ptrs, dst_ptrs, dst_dev_flat) in the
+    library's pointer order; dst_dev_flat pairs each destination pointer's
+    host image with its device buffer."""
     src_dev = []
     src_seen = {}
     for t_src in sources:
@@ -86,6 +86,32 @@ def device_run(workload, sources, per_tensor_dst_host, poison=0xA5, src_shift=0,
                 dst_ptrs.append(seen[id(hb)].ptr)
                 dst_dev_flat.append((hb, seen[id(hb)]))
     src_ptrs = [b.ptr for ts in src_dev for b in ts]
+    return src_dev, src_ptrs, dst_ptrs, dst_dev_flat
+
+
+def check_device(workload_name, dst_dev_flat):
+    """Every destination buffer equals its oracle image (poison outside the
+    views included) and its guard bytes are intact."""
+    checked = set()
+    for host_img, dev in dst_dev_flat:
+        if id(dev) in checked:
+            continue
+        checked.add(id(dev))
+        got = dev.host()
+        if not np.array_equal(got, host_img):
+            bad = np.nonzero(got != host_img)[0]
+            raise AssertionError("%s: %d bytes differ, first at %d (got %#x want %#x)"
+                                 % (workload_name, bad.size, bad[0], got[bad[0]], host_img[bad[0]]))
+        assert dev.guard_ok(), "%s: guard bytes overwritten" % workload_name
+
+
+def device_run(workload, sources, per_tensor_dst_host, poison=0xA5, src_shift=0, dst_shift=0,
+               plan=None, stream=None, **plan_kw):
+    """Upload sources, allocate poisoned destinations shaped like the host
+    images, execute the HIP path, return the device buffers in pointer order.
+    """
+    src_dev, src_ptrs, dst_ptrs, dst_dev_flat = device_buffers(
+        workload, sources, per_tensor_dst_host, poison, src_shift, dst_shift)
     if plan is None:
         plan = lh.plan_workload(workload, **plan_kw)
     s = stream if stream is not None else torch.cuda.current_stream()
@@ -103,18 +129,7 @@ def check_against_oracle(workload, poison=0xA5, src_shift=0, dst_shift=0, global
     # Fresh poisoned host images shaped like the oracle's, for allocation only.
     plan, src_dev, dst_dev = device_run(workload, sources, per, poison=poison,
                                         src_shift=src_shift, dst_shift=dst_shift, **plan_kw)
-    checked = set()
-    for host_img, dev in dst_dev:
-        if id(dev) in checked:
-            continue
-        checked.add(id(dev))
-        got = dev.host()
-        if not np.array_equal(got, host_img):
-            bad = np.nonzero(got != host_img)[0]
-            raise AssertionError("%s: %d bytes differ, first at %d (got %#x want %#x)"
-                                 % (workload["name"], bad.size, bad[0], got[bad[0]],
-                                    host_img[bad[0]]))
-        assert dev.guard_ok(), "%s: guard bytes overwritten" % workload["name"]
+    check_device(workload["name"], dst_dev)
     for t_src, t_dev in zip(sources, src_dev):
         host = [hb for e in t_src for hb in (e["parts"] if "parts" in e else [e["buf"]])]
         for hb, d in zip(host, t_dev):

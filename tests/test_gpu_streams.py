@@ -1,0 +1,128 @@
+"""GPU execution contract: plans on non-default streams, one plan executed
+concurrently on several streams (and from several host threads) into
+separate destinations, two plans at once, and an execute captured into a
+HIP graph and replayed.  Every result is compared byte for byte with the
+CPU oracle, poison and guard bytes included.
+"""
+
+import threading
+
+import pytest
+import torch
+
+from rl_weight_refit_amd import binding, synth
+
+import gpu_helpers as gh
+import helpers
+import lib_helpers as lh
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _cuda():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.load()
+    yield
+
+
+WORKLOADS = {
+    "worked_8x8_tiny": synth.worked_example,
+    "moe_small": lambda: synth.moe_experts(16, 512, 192, 8, 4, 4, seed=9),
+    "moe_small_mxfp8": lambda: synth.moe_experts(16, 512, 192, 8, 4, 4, seed=9, quant="mxfp8"),
+    "uneven_7": lambda: synth.uneven_case(7),
+    "dense_ffn_fanout": lambda: synth.dense_ffn(hidden=256, inter=1000, src_tp=4, dst_tp=2, dst_dp=2),
+}
+
+
+def _setup(name, copies=1):
+    wl = WORKLOADS[name]()
+    _, sources, _, per = helpers.golden_workload(wl)
+    bufs = [gh.device_buffers(wl, sources, per) for _ in range(copies)]
+    torch.cuda.synchronize()   # poison fills ran on the current stream
+    return wl, lh.plan_workload(wl), bufs
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
+def test_non_default_stream(name):
+    wl, plan, [(src_dev, sp, dp, flat)] = _setup(name)
+    s = torch.cuda.Stream()
+    binding.reshard_execute(plan, sp, dp, s.cuda_stream)
+    s.synchronize()
+    gh.check_device(wl["name"], flat)
+
+
+@pytest.mark.parametrize("name", ["moe_small", "moe_small_mxfp8", "uneven_7"])
+def test_one_plan_on_several_streams(name):
+    """The same plan, four streams, four destination sets, no synchronisation
+    between the executes."""
+    wl, plan, bufs = _setup(name, copies=4)
+    streams = [torch.cuda.Stream() for _ in bufs]
+    for rep in range(3):
+        for (src_dev, sp, dp, flat), s in zip(bufs, streams):
+            binding.reshard_execute(plan, sp, dp, s.cuda_stream)
+    torch.cuda.synchronize()
+    for _, _, _, flat in bufs:
+        gh.check_device(wl["name"], flat)
+
+
+def test_one_plan_from_several_threads():
+    """Host threads share one plan (the first execute uploads its tables
+    under the plan's lock); each thread has its own stream and buffers."""
+    wl, plan, bufs = _setup("moe_small_mxfp8", copies=4)
+    errors = []
+
+    def work(k):
+        try:
+            s = torch.cuda.Stream()
+            _, sp, dp, _ = bufs[k]
+            for _ in range(10):
+                binding.reshard_execute(plan, sp, dp, s.cuda_stream)
+            s.synchronize()
+        except Exception as e:  # reported below, in the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(k,)) for k in range(len(bufs))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for _, _, _, flat in bufs:
+        gh.check_device(wl["name"], flat)
+
+
+def test_two_plans_at_once():
+    wa, pa, [(_, spa, dpa, fa)] = _setup("moe_small_mxfp8")
+    wb, pb, [(_, spb, dpb, fb)] = _setup("dense_ffn_fanout")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    binding.reshard_execute(pa, spa, dpa, s1.cuda_stream)
+    binding.reshard_execute(pb, spb, dpb, s2.cuda_stream)
+    torch.cuda.synchronize()
+    gh.check_device(wa["name"], fa)
+    gh.check_device(wb["name"], fb)
+
+
+@pytest.mark.parametrize("name", ["worked_8x8_tiny", "moe_small_mxfp8", "uneven_7", "dense_ffn_fanout"])
+def test_graph_capture_and_replay(name):
+    """After its first execute (which uploads the tables) a plan only enqueues
+    kernels, so it can be captured into a HIP graph.  Each replay follows an
+    eager re-poisoning of every destination and must rewrite them exactly."""
+    wl, plan, [(src_dev, sp, dp, flat)] = _setup(name)
+    s = torch.cuda.Stream()
+    binding.reshard_execute(plan, sp, dp, s.cuda_stream)
+    s.synchronize()
+    gh.check_device(wl["name"], flat)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        binding.reshard_execute(plan, sp, dp, torch.cuda.current_stream().cuda_stream)
+    dsts = {id(d): d for _, d in flat}.values()
+    for rep in range(4):
+        for d in dsts:
+            d.body().fill_(d.poison)     # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        gh.check_device(wl["name"], flat)
