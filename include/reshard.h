@@ -220,7 +220,8 @@ rs_status reshard_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int
  * checked before anything is launched (a NULL pointer for a non-empty slot
  * fails the whole call with RS_ERR_INVALID and nothing written).  The first
  * call on a device uploads the plan's tables there (a blocking allocation
- * and copy); later calls allocate nothing.  Errors: RS_ERR_INVALID,
+ * and copy); later calls allocate nothing and only enqueue kernels, so they
+ * may be captured into a HIP graph.  Errors: RS_ERR_INVALID,
  * RS_ERR_ALLOC, RS_ERR_HIP (launch or upload failure).  Faults during
  * execution surface on the stream like any HIP error. */
 rs_status reshard_execute(const rs_plan* plan, void* const* src_ptrs, void* const* dst_ptrs,
