@@ -101,6 +101,41 @@ def test_uneven_layouts_through_tiny_kernel(seed, fanout):
     gh.check_against_oracle(synth.uneven_case(seed), tiny_bytes=1 << 16, fanout=fanout)
 
 
+SECOND_POISON = {
+    "worked_8x8": synth.worked_example,
+    "moe_small": lambda: synth.moe_experts(16, 512, 192, 8, 4, 4, seed=9),
+    "moe_small_mxfp8": lambda: synth.moe_experts(16, 512, 192, 8, 4, 4, seed=9, quant="mxfp8"),
+    "uneven_3": lambda: synth.uneven_case(3),
+    "dense_ffn_fanout": lambda: synth.dense_ffn(hidden=256, inter=1000, src_tp=4, dst_tp=2, dst_dp=2),
+}
+
+
+@pytest.mark.parametrize("poison", [0x00, 0xFF])
+@pytest.mark.parametrize("name", sorted(SECOND_POISON))
+def test_other_poison_bytes(name, poison):
+    """Destinations poisoned with 0x00 and 0xFF instead of 0xA5: a byte the
+    kernels fail to write, or write outside a view, cannot hide behind a
+    coincidence with one poison value."""
+    gh.check_against_oracle(SECOND_POISON[name](), poison=poison)
+
+
+def _identity(wl):
+    out = dict(wl)
+    out["tensors"] = [dict(t, dst=dict(t["src"])) for t in wl["tensors"]]
+    out["name"] = wl["name"] + "_identity"
+    return out
+
+
+@pytest.mark.parametrize("seed", range(0, 500, 50))
+def test_identity_layouts(seed):
+    """A -> A: the destination layout equals the source layout."""
+    gh.check_against_oracle(_identity(synth.uneven_case(seed)))
+
+
+def test_identity_moe_layer():
+    gh.check_against_oracle(_identity(synth.moe_experts(16, 512, 192, 8, 4, 4, seed=9)))
+
+
 @pytest.mark.parametrize("shifts", [(4, 0), (0, 2), (6, 10)])
 @pytest.mark.parametrize("seed", range(0, 500, 50))
 def test_uneven_layouts_misaligned(seed, shifts):
