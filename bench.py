@@ -35,12 +35,18 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "rs_bulk_kernel_moe_dsv3_counters.json")
 PROFILE_COUNTERS_MX = os.path.join(ROOT, "profiles", "rs_mx_kernel_moe_dsv3_mxfp8_counters.json")
-KERNEL_SOURCE = os.path.join(ROOT, "rl_weight_refit_amd", "csrc", "kernels.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "rl_weight_refit_amd", "csrc", f)
+                  for f in ("kernels.hip", "rs_device.hpp")]
 
 
 def kernel_hash():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the device code (kernels and the tables they read); counter
+    profiles taken from other sources are not reported as this kernel's."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def parse():

@@ -8,7 +8,12 @@
 namespace rs {
 
 constexpr int kThreads = 256;         // threads per workgroup (4 wave64s)
-constexpr int kPool = 320;            // device pointers passed per launch (kernel arguments)
+// Device pointers passed per launch in the kernel arguments: 500 keeps
+// LaunchArgs (24 + 8 * kPool bytes) under the 4 KiB kernel-argument budget.
+#ifndef RS_POOL
+#define RS_POOL 500
+#endif
+constexpr int kPool = RS_POOL;
 constexpr int kMaxFan = 16;           // destination replicas per region
 constexpr uint32_t kThinTile = 16384; // LDS tile of the thin bucket, bytes
 constexpr uint32_t kLongRow = 2048;   // bulk rows at least this long are walked row by row
@@ -100,5 +105,6 @@ struct LaunchArgs {
   uint32_t n_units;
   void* ptr[kPool];
 };
+static_assert(sizeof(LaunchArgs) <= 4096, "kernel arguments must fit in 4 KiB");
 
 }  // namespace rs
