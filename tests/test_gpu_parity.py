@@ -208,6 +208,29 @@ def test_mxfp8_fanout_and_row_lengths(shape, inner, mesh, pl):
     gh.check_against_oracle({"name": "mx_fan", "buffers": {}, "tensors": [t]})
 
 
+@pytest.mark.parametrize("dst_mesh,dst_pl", [([2], [1]), ([2, 2], [0, -1]), ([3], [2])])
+def test_mxfp8_strided_scale_views(dst_mesh, dst_pl):
+    """Element rows padded to a longer pitch and block scales with a last-dim
+    stride of 3 bytes (every third byte of a padded scale row): the kernel's
+    per-block scale addressing, with replicas and a split last dim."""
+    shape = [4, 20, 200]
+    t = {"name": "w", "shape": shape, "dtype": "bf16", "src": synth.side([2], [0]),
+         "values": {"kind": "normal", "std": 0.02, "seed": 31}}
+    nslots = 1
+    for m in dst_mesh:
+        nslots *= m
+    # local shapes: last dim up to 200 (or 67 when split in 3), <= 10 / 20 rows
+    pitch, rows, blocks = 256, 4 * 20, 7
+    slots, scales, bufs = [], [], {}
+    for k in range(nslots):
+        bufs["e/%d" % k] = {"dtype": "u8", "elems": 5 + rows * pitch}
+        bufs["s/%d" % k] = {"dtype": "u8", "elems": 2 + rows * 3 * (blocks + 1) * 2}
+        slots.append({"buf": "e/%d" % k, "view": (5, [20 * pitch, pitch, 1])})
+        scales.append({"buf": "s/%d" % k, "view": (2, [20 * 3 * (blocks + 1) * 2, 3 * (blocks + 1) * 2, 3])})
+    t["dst"] = synth.side(dst_mesh, dst_pl, slots=slots, quant="mxfp8", scale_slots=scales)
+    gh.check_against_oracle({"name": "mx_strided_scales", "buffers": bufs, "tensors": [t]})
+
+
 def test_mxfp8_extreme_values():
     """Blocks spanning many binades, zeros, negative zeros, bf16 subnormals,
     the largest bf16 and NaN/Inf blocks (the NaN/Inf convention is the
