@@ -218,7 +218,11 @@ rs_status reshard_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int
  * completes.  Sources and destinations must not overlap.
  * Asynchronous: returns once the launches are enqueued.  Every argument is
  * checked before anything is launched (a NULL pointer for a non-empty slot
- * fails the whole call with RS_ERR_INVALID and nothing written).  The first
+ * fails the whole call with RS_ERR_INVALID and nothing written).  With the
+ * environment variable RESHARD_DEBUG_CHECKS=1 it also checks that sources
+ * and destinations do not overlap and that every pointer is device memory of
+ * the stream's device with room for every byte its regions reach (a few
+ * microseconds per pointer).  The first
  * call on a device uploads the plan's tables there (a blocking allocation
  * and copy); later calls allocate nothing and only enqueue kernels, so they
  * may be captured into a HIP graph.  Errors: RS_ERR_INVALID,

@@ -160,6 +160,39 @@ rs_status execute(const rs_plan* plan, void* const* src_ptrs, void* const* dst_p
   hipError_t he = stream ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev) : hipGetDevice(&dev);
   if (he != hipSuccess)
     return fail(RS_ERR_HIP, std::string("device of the stream: ") + hipGetErrorString(he) + "\n");
+  if (debug_checks()) {
+    // Every pointer is device memory of the stream's device, with room for
+    // every byte its regions reach (a short buffer would fault the GPU).
+    auto check = [&](const char* side, size_t i, void* p, uint64_t span) {
+      hipDeviceptr_t base = nullptr;
+      size_t size = 0;
+      hipPointerAttribute_t attr;
+      hipError_t e = hipMemGetAddressRange(&base, &size, p);
+      if (e == hipSuccess) e = hipPointerGetAttributes(&attr, p);
+      if (e != hipSuccess) {
+        (void)hipGetLastError();
+        err << side << "[" << i << "] is not device memory (" << hipGetErrorString(e) << ")\n";
+        ++nerr;
+        return;
+      }
+      const uintptr_t end = reinterpret_cast<uintptr_t>(base) + size, at = reinterpret_cast<uintptr_t>(p);
+      if (at + span > end) {
+        err << side << "[" << i << "] needs " << span << " bytes but its allocation ends " << (end - at)
+            << " bytes after it\n";
+        ++nerr;
+      }
+      if (attr.type == hipMemoryTypeDevice && attr.device != dev) {
+        err << side << "[" << i << "] is memory of device " << attr.device << ", the stream runs on device "
+            << dev << "\n";
+        ++nerr;
+      }
+    };
+    for (size_t i = 0; i < d.src_used.size(); ++i)
+      if (d.src_used[i]) check("src_ptrs", i, src_ptrs[i], d.src_span[i]);
+    for (size_t i = 0; i < d.dst_used.size(); ++i)
+      if (d.dst_used[i]) check("dst_ptrs", i, dst_ptrs[i], d.dst_span[i]);
+    if (nerr) return fail(RS_ERR_INVALID, err.str());
+  }
   char* base = nullptr;
   const rs_status ts = plan_tables(plan, dev, &base);
   if (ts != RS_OK) return ts;

@@ -126,3 +126,36 @@ def test_graph_capture_and_replay(name):
         g.replay()
         torch.cuda.synchronize()
         gh.check_device(wl["name"], flat)
+
+
+def test_debug_checks_reject_a_short_allocation(monkeypatch):
+    """With RESHARD_DEBUG_CHECKS=1 every pointer is checked against its
+    allocation before anything is launched.  Destination 2 of the worked
+    example gets a 60-byte allocation where the plan writes 64 bytes: the
+    call fails naming it.  (Allocations are rounded up to whole pages, so
+    even a missed check could not write outside mapped memory.)"""
+    import ctypes
+    wl = WORKLOADS["worked_8x8_tiny"]()
+    _, sources, _, per = helpers.golden_workload(wl)
+    _, sp, dp, flat = gh.device_buffers(wl, sources, per)
+    torch.cuda.synchronize()
+    plan = lh.plan_workload(wl)
+    hip = ctypes.CDLL("libamdhip64.so")
+    short = ctypes.c_void_p()
+    assert hip.hipMalloc(ctypes.byref(short), ctypes.c_size_t(60)) == 0
+    try:
+        monkeypatch.setenv("RESHARD_DEBUG_CHECKS", "1")
+        bad = list(dp)
+        bad[2] = short.value
+        stream = torch.cuda.current_stream().cuda_stream
+        with pytest.raises(binding.ReshardError) as e:
+            binding.reshard_execute(plan, sp, bad, stream)
+        assert e.value.status == 1
+        assert "dst_ptrs[2] needs 64 bytes but its allocation ends 60 bytes after it" in str(e.value)
+        # the right buffers pass the same checks
+        binding.reshard_execute(plan, sp, dp, stream)
+        torch.cuda.synchronize()
+        gh.check_device(wl["name"], flat)
+    finally:
+        torch.cuda.synchronize()
+        hip.hipFree(short)
