@@ -10,6 +10,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 if HERE not in sys.path:
     sys.path.insert(0, HERE)
 
+# Every execute in the tests checks its pointers against their allocations
+# first, so a buffer a test sized wrongly fails the call instead of
+# faulting the GPU.
+os.environ.setdefault("RESHARD_DEBUG_CHECKS", "1")
+
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
