@@ -8,9 +8,11 @@
 //  bulk  one workgroup per work unit (<= unit_bytes).  16-byte vectors when
 //        every address of the region is 16-byte aligned: long rows are walked
 //        row by row by the whole workgroup (row address math is uniform, so it
-//        runs on the scalar unit), short rows are split among sub-wave lane
-//        groups.  Otherwise each wave copies one row at the widest granule the
-//        source/destination co-alignment allows, with byte head and tail.
+//        runs on the scalar unit); the vectors of short rows are numbered
+//        across the unit so every lane loads its share in one batch (sub-wave
+//        lane groups per row when rows have several outer dims).  Otherwise
+//        each wave copies one row at the widest granule the source/destination
+//        co-alignment allows, with byte head and tail.
 //        Launched so that at most five workgroups share a CU (see
 //        bulk_lds_pad): fewer streams concurrently per CU copy faster.
 //  thin  runs shorter than the thin threshold (e.g. the 8-byte rows of a
@@ -67,9 +69,6 @@ __device__ __forceinline__ uint64_t row_off(uint32_t r, uint32_t e0, uint32_t e1
 #endif
 #ifndef RS_UNROLL
 #define RS_UNROLL 4   // 16-byte vectors in flight per lane in the bulk kernel
-#endif
-#ifndef RS_PIPE
-#define RS_PIPE 0     // 1: software-pipeline the long-row copy loop
 #endif
 #ifndef RS_BULK_MIN_WAVES
 #define RS_BULK_MIN_WAVES 1  // occupancy floor (waves per SIMD) for the bulk kernel
@@ -253,10 +252,6 @@ __device__ __forceinline__ void bulk_short_rows(const LaunchArgs& a, const CopyR
   }
 }
 
-#ifndef RS_SHORT_FLAT
-#define RS_SHORT_FLAT 1   // 1: short aligned rows use the flat vector numbering below
-#endif
-
 // Short aligned rows of a region with at most one outer dim (row r at
 // r * stride on each side), numbered flat: vector f = i * vpr + v (row
 // r0 + i, vector v of it).  Lane tid takes f = f0 + tid + k * kThreads, so
@@ -322,29 +317,6 @@ __device__ __forceinline__ void bulk_body(const LaunchArgs& a, const CopyRegion*
       const uint64_t so = row_off(r, e0, e1, nouter, s0, s1, s2);
       const uint64_t dof = row_off(r, e0, e1, nouter, d0, d1, d2);
       const char* s = sp + so;
-#if RS_PIPE
-      // Software pipelined: the next batch of loads is issued before the
-      // current batch is stored.
-      u32x4 x[RS_UNROLL], y[RS_UNROLL];
-      uint32_t v = tid;
-#pragma unroll
-      for (int k = 0; k < RS_UNROLL; ++k)
-        if (v + k * kThreads < vpr) x[k] = ld16(s + 16ull * (v + k * kThreads));
-      for (; v < vpr; v += RS_UNROLL * kThreads) {
-        const uint32_t vn = v + RS_UNROLL * kThreads;
-#pragma unroll
-        for (int k = 0; k < RS_UNROLL; ++k)
-          if (vn + k * kThreads < vpr) y[k] = ld16(s + 16ull * (vn + k * kThreads));
-        for (uint32_t j = 0; j < nd; ++j) {
-          char* d = (kFan1 ? dp0 : static_cast<char*>(a.ptr[R->dst_ptr[j]]) + dst_off) + dof;
-#pragma unroll
-          for (int k = 0; k < RS_UNROLL; ++k)
-            if (v + k * kThreads < vpr) st16(d + 16ull * (v + k * kThreads), x[k]);
-        }
-#pragma unroll
-        for (int k = 0; k < RS_UNROLL; ++k) x[k] = y[k];
-      }
-#else
       for (uint32_t v = tid; v < vpr; v += RS_UNROLL * kThreads) {
         u32x4 x[RS_UNROLL];
 #pragma unroll
@@ -357,19 +329,17 @@ __device__ __forceinline__ void bulk_body(const LaunchArgs& a, const CopyRegion*
             if (v + k * kThreads < vpr) st16(d + 16ull * (v + k * kThreads), x[k]);
         }
       }
-#endif
     }
   } else if (al == 0) {
-    // Short rows: L lanes per row (a power of two >= the row's vectors, at
-    // most 64), 64 / L rows per wave step; each lane moves one or two
+    // Short rows.  With at most one outer dim the unit's vectors are numbered
+    // flat; otherwise L lanes per row (a power of two >= the row's vectors,
+    // at most 64), 64 / L rows per wave step, each lane moving one or two
     // vectors of each of several rows per iteration.
     const uint32_t vpr = inner >> 4;
-#if RS_SHORT_FLAT
     if (nouter <= 1) {
       bulk_short_flat<kFan1>(a, R, sp, dst_off, r0, r1, vpr, s0, d0, nd);
       return;
     }
-#endif
     uint32_t L = 1;
     while (L < vpr && L < 64u) L <<= 1;
     if (vpr > L)
