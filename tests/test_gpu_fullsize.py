@@ -218,3 +218,50 @@ def test_full_size_round_trip():
             assert torch.equal(a, b)
     del src, named, dst_bufs, out
     torch.cuda.empty_cache()
+
+
+def test_rows_past_2_31():
+    """One byte per row, 2^31 + 1000 rows: a [N, 2] u8 tensor split by
+    columns over two sources, gathered into one replicated [N, 2]
+    destination.  The planner splits the column regions below 2^31 rows
+    (the kernels' row indices are 32-bit).  Shard(1) -> Replicate is
+    torch.cat of the columns, so the destination must equal G exactly
+    (G[i, j] = (2 i + j) mod 256, the index values): checked for every byte,
+    and sampled element by element against the oracle's source lookup,
+    around row 2^31 included."""
+    N = (1 << 31) + 1000
+    t = {"name": "col", "shape": [N, 2], "dtype": "u8", "src": synth.side([2], [1]),
+         "dst": synth.side([1], [-1]), "values": {"kind": "index"}}
+    wl = {"name": "rows_past_2_31", "buffers": {}, "tensors": [t]}
+    plan = lh.plan_workload(wl)
+    regs = plan.regions()
+    assert all(r["ext"][0] * r["ext"][1] * r["ext"][2] < (1 << 31) for r in regs)
+    assert sum(r["inner"] * r["ext"][0] * r["ext"][1] * r["ext"][2] for r in regs) == 2 * N
+    dev = torch.device("cuda")
+    step = 1 << 28
+    src = []
+    for j in range(2):
+        s = torch.empty(N, dtype=torch.uint8, device=dev)
+        for a in range(0, N, step):
+            b = min(N, a + step)
+            s[a:b] = ((torch.arange(a, b, dtype=torch.int64, device=dev) * 2 + j) & 0xFF).to(torch.uint8)
+        src.append(s)
+    dst = torch.full((2 * N,), POISON, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    binding.reshard_execute(plan, [s.data_ptr() for s in src], [dst.data_ptr()],
+                            torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    for a in range(0, 2 * N, step):
+        b = min(2 * N, a + step)
+        want = (torch.arange(a, b, dtype=torch.int64, device=dev) & 0xFF).to(torch.uint8)
+        assert bool(torch.equal(dst[a:b], want)), "bytes %d..%d differ" % (a, b)
+    rng = np.random.default_rng(31)
+    rows = np.concatenate([rng.integers(0, N, 2000), [0, (1 << 31) - 1, 1 << 31, (1 << 31) + 1, N - 1]])
+    sd = helpers.src_desc_for(t)
+    for i in rows:
+        for j in range(2):
+            slot, loc = ogolden.source_location(sd, [int(i), j])
+            want = int(src[slot][loc[0]].item())
+            assert int(dst[2 * int(i) + j].item()) == want, (i, j)
+    del src, dst
+    torch.cuda.empty_cache()

@@ -119,6 +119,26 @@ def test_other_poison_bytes(name, poison):
     gh.check_against_oracle(SECOND_POISON[name](), poison=poison)
 
 
+EMPTY_CASES = [
+    # (shape, src mesh, src placements, dst mesh, dst placements)
+    ([0, 5], [2], [0], [3], [1]),            # no elements at all
+    ([3, 40], [8], [0], [4], [1]),           # 5 of 8 source shards empty
+    ([2, 3, 7], [2, 4], [1, 2], [8], [0]),   # 6 of 8 destination shards empty
+    ([5, 1], [3], [-1], [6], [1]),           # replicated sources, 5 of 6 destinations empty
+]
+
+
+@pytest.mark.parametrize("dtype", ["u8", "bf16", "f32"])
+@pytest.mark.parametrize("case", range(len(EMPTY_CASES)))
+def test_empty_shards(case, dtype):
+    """Zero-extent tensors and meshes larger than the dim they shard (the
+    torch.chunk rule leaves trailing shards empty)."""
+    shape, sm, sp, dm, dp = EMPTY_CASES[case]
+    t = {"name": "e", "shape": shape, "dtype": dtype, "src": synth.side(sm, sp),
+         "dst": synth.side(dm, dp), "values": {"kind": "index"}}
+    gh.check_against_oracle({"name": "empty_%d" % case, "buffers": {}, "tensors": [t]})
+
+
 def _identity(wl):
     out = dict(wl)
     out["tensors"] = [dict(t, dst=dict(t["src"])) for t in wl["tensors"]]

@@ -335,3 +335,14 @@ def test_mxfp8_source_must_be_two_byte_aligned():
     with pytest.raises(binding.ReshardError) as e:
         binding.reshard_execute(plan, [0x1001] * n_src, [0x100000 + 0x1000 * i for i in range(n_dst)])
     assert "aligned" in str(e.value)
+
+
+@pytest.mark.parametrize("rows", [(1 << 31) - 1, 1 << 31, 5 * (1 << 31) + 3])
+def test_regions_stay_below_2_31_rows(rows):
+    """Kernels index rows with 32 bits: the planner splits longer regions."""
+    t = {"name": "col", "shape": [rows, 2], "dtype": "u8", "src": synth.side([2], [1]),
+         "dst": synth.side([1], [-1]), "values": {"kind": "index"}}
+    p = lh.plan_workload({"name": "rows", "buffers": {}, "tensors": [t]})
+    regs = p.regions()
+    assert all(r["ext"][0] * r["ext"][1] * r["ext"][2] < (1 << 31) for r in regs)
+    assert sum(r["inner"] * r["ext"][0] * r["ext"][1] * r["ext"][2] for r in regs) == 2 * rows
