@@ -125,14 +125,27 @@ def _views(vs, ndim):
 
 
 def make_desc(spec):
-    """C description of one side; returns (TensorDesc, objects to keep alive)."""
+    """C description of one side; returns (TensorDesc, objects to keep alive).
+    The C side reads one entry per mesh slot from slot_of_coord, views and
+    scale_views, so their lengths are checked here."""
     d = TensorDesc()
     shape = list(spec["shape"])
+    mesh = list(spec["mesh"])
+    if len(spec["placements"]) != len(mesh):
+        raise ValueError("%d placements for a %d-dim mesh" % (len(spec["placements"]), len(mesh)))
+    if len(shape) > RS_MAX_DIMS or len(mesh) > RS_MAX_MESH:
+        raise ValueError("rank %d / mesh rank %d above the limits %d / %d"
+                         % (len(shape), len(mesh), RS_MAX_DIMS, RS_MAX_MESH))
+    nslots = 1
+    for m in mesh:
+        nslots *= int(m)
+    for key in ("slot_of_coord", "views", "scale_views"):
+        if spec.get(key) is not None and len(spec[key]) != nslots:
+            raise ValueError("%s has %d entries for %d mesh slots" % (key, len(spec[key]), nslots))
     d.ndim = len(shape)
     d.dtype = DTYPES[spec["dtype"]]
     for i, n in enumerate(shape):
         d.global_shape[i] = int(n)
-    mesh = list(spec["mesh"])
     d.mesh_ndim = len(mesh)
     for i, (m, p) in enumerate(zip(mesh, spec["placements"])):
         d.mesh_shape[i] = int(m)
@@ -166,6 +179,8 @@ class Plan:
 
     def __init__(self, handle):
         self._h = ctypes.c_void_p(handle)
+        info = self.info()
+        self.n_src_ptrs, self.n_dst_ptrs = info["n_src_ptrs"], info["n_dst_ptrs"]
 
     @property
     def handle(self):
@@ -239,6 +254,9 @@ def _ptr_array(ptrs):
 def reshard_execute(plan, src_ptrs, dst_ptrs, stream=None):
     """Enqueue the plan on a HIP stream (an int handle, e.g.
     torch.cuda.current_stream().cuda_stream; None = the default stream)."""
+    if len(src_ptrs) != plan.n_src_ptrs or len(dst_ptrs) != plan.n_dst_ptrs:
+        raise ValueError("the plan takes %d source and %d destination pointers, got %d and %d"
+                         % (plan.n_src_ptrs, plan.n_dst_ptrs, len(src_ptrs), len(dst_ptrs)))
     s = _ptr_array(src_ptrs)
     d = _ptr_array(dst_ptrs)
     _check(load().reshard_execute(plan.handle, s, d, ctypes.c_void_p(stream or 0)))

@@ -346,3 +346,26 @@ def test_regions_stay_below_2_31_rows(rows):
     regs = p.regions()
     assert all(r["ext"][0] * r["ext"][1] * r["ext"][2] < (1 << 31) for r in regs)
     assert sum(r["inner"] * r["ext"][0] * r["ext"][1] * r["ext"][2] for r in regs) == 2 * rows
+
+
+def test_binding_checks_pointer_counts():
+    """The C side reads as many pointers as the plan names; the binding
+    refuses shorter or longer lists before calling it."""
+    plan = lh.plan_workload(synth.worked_example())
+    with pytest.raises(ValueError, match="2 source and 4 destination"):
+        binding.reshard_execute(plan, [0x1000], [0x2000, 0x3000, 0x4000, 0x5000])
+    with pytest.raises(ValueError):
+        binding.reshard_execute(plan, [0x1000, 0x1100], [0x2000] * 5)
+
+
+@pytest.mark.parametrize("bad", [
+    {"placements": [0, 1]},                          # two placements, one mesh dim
+    {"slot_of_coord": [0, 1, 2]},                    # 3 entries for 2 slots
+    {"views": [(0, [8, 1])]},                        # 1 view for 2 slots
+])
+def test_binding_checks_per_slot_lengths(bad):
+    spec = {"shape": [8, 8], "dtype": "i32", "mesh": [2], "placements": [0]}
+    spec.update(bad)
+    dst = {"shape": [8, 8], "dtype": "i32", "mesh": [2], "placements": [1]}
+    with pytest.raises(ValueError):
+        binding.reshard_plan([spec], [dst])
