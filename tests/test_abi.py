@@ -72,3 +72,55 @@ def test_last_error_is_empty_after_success():
                                 [{"shape": [4], "dtype": "u8", "mesh": [2], "placements": [0]}])
     plan.info()
     assert binding.reshard_last_error() == ""
+
+
+C_CLIENT = r"""
+#include <stdio.h>
+#include "reshard.h"
+int main(void) {
+  rs_tensor_desc src = {0}, dst = {0};
+  src.ndim = 2; src.dtype = RS_BF16;
+  src.global_shape[0] = 14336; src.global_shape[1] = 4096;
+  src.mesh_ndim = 1; src.mesh_shape[0] = 4; src.placements[0] = 0;
+  dst = src;
+  dst.mesh_ndim = 2; dst.mesh_shape[0] = 2; dst.mesh_shape[1] = 2;
+  dst.placements[0] = 0; dst.placements[1] = RS_REPLICATE;
+  rs_plan* plan = NULL;
+  if (reshard_plan(&src, &dst, 1, NULL, &plan) != RS_OK) {
+    fprintf(stderr, "%s", reshard_last_error());
+    return 1;
+  }
+  rs_plan_info info;
+  if (reshard_plan_info(plan, &info) != RS_OK) return 2;
+  int64_t off[RS_MAX_DIMS], len[RS_MAX_DIMS];
+  if (reshard_shard_box(&dst, 3, off, len) != RS_OK) return 3;
+  printf("%llu %llu %llu %lld %lld\n", (unsigned long long)info.n_src_ptrs,
+         (unsigned long long)info.n_dst_ptrs, (unsigned long long)info.bytes_written,
+         (long long)off[0], (long long)len[0]);
+  reshard_plan_destroy(plan);
+  dst.placements[1] = 7;   /* not a tensor dim */
+  if (reshard_plan(&src, &dst, 1, NULL, &plan) != RS_ERR_INVALID) return 4;
+  printf("%s", reshard_last_error());
+  return 0;
+}
+"""
+
+
+def test_plain_c_client(tmp_path):
+    """A C99 program compiled with gcc against the header and the library
+    plans a layout, reads its summary and a shard box, and gets a readable
+    error for a bad placement (planning needs no GPU)."""
+    src = tmp_path / "client.c"
+    src.write_text(C_CLIENT)
+    exe = tmp_path / "client"
+    libdir = os.path.dirname(binding.LIB_PATH)
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                        str(src), "-o", str(exe), "-L", libdir, "-lreshard", "-Wl,-rpath," + libdir],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    first, rest = r.stdout.split("\n", 1)
+    # 4 source and 4 destination slots; both DP replicas receive 14336 x 4096 bf16; slot 3 = rows 7168..
+    assert first.split() == ["4", "4", str(2 * 14336 * 4096 * 2), "7168", "7168"]
+    assert "placements[1] = 7" in rest
