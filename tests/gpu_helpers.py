@@ -76,15 +76,15 @@ def device_buffers(workload, sources, per_tensor_dst_host, poison=0xA5, src_shif
     dst_ptrs = []
     dst_dev_flat = []
     for t, slots in zip(workload["tensors"], per_tensor_dst_host):
-        for key in ("buf", "scale_buf"):
+        for key, parts_key in (("buf", "parts"), ("scale_buf", "scale_parts")):
             if key == "scale_buf" and t["dst"].get("quant") != "mxfp8":
                 continue
             for e in slots:
-                hb = e[key]
-                if id(hb) not in seen:
-                    seen[id(hb)] = DevBuf(hb.size, shift=dst_shift, poison=poison)
-                dst_ptrs.append(seen[id(hb)].ptr)
-                dst_dev_flat.append((hb, seen[id(hb)]))
+                for hb in (e[parts_key] if parts_key in e else [e[key]]):
+                    if id(hb) not in seen:
+                        seen[id(hb)] = DevBuf(hb.size, shift=dst_shift, poison=poison)
+                    dst_ptrs.append(seen[id(hb)].ptr)
+                    dst_dev_flat.append((hb, seen[id(hb)]))
     src_ptrs = [b.ptr for ts in src_dev for b in ts]
     return src_dev, src_ptrs, dst_ptrs, dst_dev_flat
 

@@ -88,6 +88,18 @@ def alloc_destinations(workload, poison=0xA5):
         slots = []
         boxes = olayout.slot_boxes(desc)
         for k, box in enumerate(boxes):
+            ln = box[1]
+            if d.get("split0"):
+                # one dense buffer per local dim-0 index (and per-part scales)
+                per = olayout.box_volume((None, list(ln[1:]))) if len(ln) > 1 else 1
+                e = {"parts": [np.full(per * esize, poison, dtype=np.uint8) for _ in range(ln[0])],
+                     "view": None}
+                if d.get("quant") == "mxfp8":
+                    nsc = olayout.box_volume((None, list(ln[1:-1]) + [-(-ln[-1] // 32)]))
+                    e["scale_parts"] = [np.full(nsc, poison, dtype=np.uint8) for _ in range(ln[0])]
+                    e["scale_view"] = None
+                slots.append(e)
+                continue
             if d["slots"] is None:
                 nbytes = olayout.box_volume(box) * esize
                 e = {"buf": np.full(nbytes, poison, dtype=np.uint8), "view": None}

@@ -251,6 +251,29 @@ def test_mxfp8_strided_scale_views(dst_mesh, dst_pl):
     gh.check_against_oracle({"name": "mx_strided_scales", "buffers": bufs, "tensors": [t]})
 
 
+@pytest.mark.parametrize("quant", [None, "mxfp8"])
+@pytest.mark.parametrize("layout", [([2], [1], [3], [0]), ([2, 2], [0, 1], [4], [0]), ([3], [-1], [2, 2], [0, 2])])
+def test_per_part_destinations(layout, quant):
+    """Destinations held as one buffer per local dim-0 index (e.g. one per
+    expert on the receiving side), MXFP8 scale buffers split the same way."""
+    sm, sp, dm, dp = layout
+    t = {"name": "w", "shape": [6, 40, 96], "dtype": "bf16", "src": synth.side(sm, sp),
+         "dst": synth.side(dm, dp, quant=quant, split0=True),
+         "values": {"kind": "normal", "std": 0.02, "seed": 41}}
+    gh.check_against_oracle({"name": "dst_parts", "buffers": {}, "tensors": [t]})
+
+
+@pytest.mark.parametrize("quant", [None, "mxfp8"])
+@pytest.mark.parametrize("mesh,pl", [([20], [-1]), ([2, 17], [-1, -1]), ([4, 6], [0, -1])])
+def test_more_than_16_replicas(mesh, pl, quant):
+    """Fan-out groups hold at most 16 destination replicas: 20, 34 and 6
+    replicas per shard, each written in full."""
+    t = {"name": "w", "shape": [8, 64, 96], "dtype": "bf16", "src": synth.side([2], [0]),
+         "dst": synth.side(mesh, pl, quant=quant), "values": {"kind": "normal", "std": 0.02, "seed": 43}}
+    plan = gh.check_against_oracle({"name": "fan", "buffers": {}, "tensors": [t]})
+    assert max(len(r["dst_index"]) for r in plan.regions()) <= 16
+
+
 def test_mxfp8_extreme_values():
     """Blocks spanning many binades, zeros, negative zeros, bf16 subnormals,
     the largest bf16 and NaN/Inf blocks (the NaN/Inf convention is the
