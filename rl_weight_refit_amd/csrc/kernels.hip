@@ -6,13 +6,17 @@
 // flight per CU.
 //
 //  bulk  one workgroup per work unit (<= unit_bytes).  16-byte vectors when
-//        every address of the region is 16-byte aligned: long rows are walked
-//        row by row by the whole workgroup (row address math is uniform, so it
-//        runs on the scalar unit); the vectors of short rows are numbered
-//        across the unit so every lane loads its share in one batch (sub-wave
-//        lane groups per row when rows have several outer dims).  Otherwise
-//        each wave copies one row at the widest granule the source/destination
-//        co-alignment allows, with byte head and tail.
+//        every address of the region is 16-byte aligned.  Eight consecutive
+//        whole units of a region form a spread group: its bytes are cut into
+//        1 KiB pieces dealt round-robin to the eight workgroups, so each
+//        workgroup's loads and stores spread over the group's range rather
+//        than one contiguous run (about 7 % faster on MI355X).  Units outside
+//        whole groups: long rows are walked row by row by the whole workgroup;
+//        the vectors of short rows are numbered across the unit so every lane
+//        loads its share in one batch (sub-wave lane groups per row when rows
+//        have several outer dims).  Misaligned regions: each wave copies one
+//        row at the widest granule the source/destination co-alignment
+//        allows, with byte head and tail.
 //        Launched so that at most five workgroups share a CU (see
 //        bulk_lds_pad): fewer streams concurrently per CU copy faster.
 //  thin  runs shorter than the thin threshold (e.g. the 8-byte rows of a
@@ -289,6 +293,113 @@ __device__ __forceinline__ void bulk_short_flat(const LaunchArgs& a, const CopyR
   }
 }
 
+// Spread groups (aligned rows).  The kSpread consecutive units of a group
+// cover rows g0 .. g0 + kSpread * rpu - 1 of the region, numbered as one run
+// of 16-byte vectors cut into pieces of kPieceVec vectors; the group's
+// workgroup j takes pieces j, j + kSpread, j + 2 kSpread, ...  It moves one
+// unit's worth of bytes, as before, but from kSpread-apart pieces spread
+// over the group's range: on MI355X a plain copy that spreads each
+// workgroup this way streams about 10 % faster than one that gives each
+// workgroup one contiguous run.
+constexpr uint32_t kPieceVec = kSpreadPiece / 16;
+constexpr uint32_t kWaves = kThreads / 64;
+
+// Rows with at most one outer dim (row r at r * stride): lane by lane, group
+// vector f is row f / vpr (magic division, exact while f * vpr < 2^32).
+template <bool kFan1>
+__device__ __forceinline__ void bulk_spread_flat(const LaunchArgs& a, const CopyRegion* R,
+                                                 const char* sp, uint64_t dst_off, uint32_t g0,
+                                                 uint32_t j, uint32_t nvec, uint32_t vpr,
+                                                 uint64_t s0, uint64_t d0, uint32_t nd) {
+  constexpr int U = RS_UNROLL;
+  const uint32_t tid = threadIdx.x;
+  const uint64_t magic = ((uint64_t(1) << 32) + vpr - 1) / vpr;
+  for (uint32_t t0 = 0; t0 < nvec; t0 += U * kThreads) {
+    u32x4 x[U];
+    uint64_t o[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const uint32_t t = t0 + k * kThreads + tid;
+      const uint32_t f = ((t / kPieceVec) * kSpread + j) * kPieceVec + t % kPieceVec;
+      const uint32_t i = uint32_t((uint64_t(f) * magic) >> 32);
+      const uint64_t r = g0 + i;
+      const uint32_t v = f - i * vpr;
+      o[k] = r * d0 + 16ull * v;
+      if (t < nvec) x[k] = ld16(sp + r * s0 + 16ull * v);
+    }
+    for (uint32_t jd = 0; jd < nd; ++jd) {
+      char* d = static_cast<char*>(a.ptr[R->dst_ptr[kFan1 ? 0 : jd]]) + dst_off;
+#pragma unroll
+      for (int k = 0; k < U; ++k)
+        if (t0 + k * kThreads + tid < nvec) st16(d + o[k], x[k]);
+    }
+  }
+}
+
+// Rows of whole 1 KiB pieces (vpr a multiple of 64), any number of outer
+// dims: a piece lies in one row and is one wave's 64 vectors, so all row
+// arithmetic is uniform.  A wave's pieces are kWaves * kSpread apart in the
+// group; it splits its first piece's row into outer indices once and then
+// advances piece column and indices by carries, with no division per piece.
+template <bool kFan1>
+__device__ __forceinline__ void bulk_spread_rows(const LaunchArgs& a, const CopyRegion* R,
+                                                 const char* sp, uint64_t dst_off, uint32_t g0,
+                                                 uint32_t j, uint32_t npu, uint32_t ppr,
+                                                 uint32_t e0, uint32_t e1, uint32_t nouter,
+                                                 uint64_t s0, uint64_t s1, uint64_t s2,
+                                                 uint64_t d0, uint64_t d1, uint64_t d2, uint32_t nd) {
+  constexpr int U = RS_UNROLL;
+  constexpr uint32_t kStep = kWaves * kSpread;
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint64_t lo = 16ull * lane;
+  const uint32_t di = kStep / ppr, dc = kStep % ppr;
+  const uint32_t p0 = wave * kSpread + j;
+  uint32_t c = p0 % ppr;
+  uint32_t i0 = g0 + p0 / ppr, i1 = 0, i2 = 0;
+  if (nouter >= 2) {
+    i1 = i0 / e0;
+    i0 -= i1 * e0;
+    if (nouter == 3) {
+      i2 = i1 / e1;
+      i1 -= i2 * e1;
+    }
+  }
+  for (uint32_t l0 = 0; l0 < npu; l0 += U * kWaves) {
+    u32x4 x[U];
+    uint64_t o[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const uint64_t cb = uint64_t(c) * kSpreadPiece + lo;
+      o[k] = i0 * d0 + i1 * d1 + i2 * d2 + cb;
+      if (l0 + k * kWaves + wave < npu) x[k] = ld16(sp + (i0 * s0 + i1 * s1 + i2 * s2 + cb));
+      // the wave's next piece: kStep pieces on, carried into row and outer indices
+      c += dc;
+      uint32_t adv = di;
+      if (c >= ppr) {
+        c -= ppr;
+        ++adv;
+      }
+      i0 += adv;
+      if (nouter >= 2) {
+        while (i0 >= e0) {
+          i0 -= e0;
+          if (++i1 == e1 && nouter == 3) {
+            i1 = 0;
+            ++i2;
+          }
+        }
+      }
+    }
+    for (uint32_t jd = 0; jd < nd; ++jd) {
+      char* d = static_cast<char*>(a.ptr[R->dst_ptr[kFan1 ? 0 : jd]]) + dst_off;
+#pragma unroll
+      for (int k = 0; k < U; ++k)
+        if (l0 + k * kWaves + wave < npu) st16(d + o[k], x[k]);
+    }
+  }
+}
+
 template <bool kFan1>
 __device__ __forceinline__ void bulk_body(const LaunchArgs& a, const CopyRegion* R, uint32_t unit) {
   const uint32_t tid = threadIdx.x;
@@ -309,6 +420,25 @@ __device__ __forceinline__ void bulk_body(const LaunchArgs& a, const CopyRegion*
 
   const uint32_t r0 = (unit - ub) * rpu;
   const uint32_t r1 = min(r0 + rpu, rows);
+
+  if (kSpread > 1 && al == 0) {
+    // A whole group of whole-piece units goes the spread way.
+    const uint32_t vpr = inner >> 4;
+    const uint64_t nvec = uint64_t(rpu) * vpr;
+    const uint32_t ul = unit - ub, j = ul % kSpread;
+    const uint64_t g0 = uint64_t(ul - j) * rpu;
+    if (g0 + uint64_t(kSpread) * rpu <= rows && nvec % kPieceVec == 0) {
+      if (nouter <= 1 && nvec * kSpread * vpr < (uint64_t(1) << 32)) {
+        bulk_spread_flat<kFan1>(a, R, sp, dst_off, uint32_t(g0), j, uint32_t(nvec), vpr, s0, d0, nd);
+        return;
+      }
+      if (kPieceVec == 64 && vpr % kPieceVec == 0) {
+        bulk_spread_rows<kFan1>(a, R, sp, dst_off, uint32_t(g0), j, uint32_t(nvec / kPieceVec),
+                                vpr / kPieceVec, e0, e1, nouter, s0, s1, s2, d0, d1, d2, nd);
+        return;
+      }
+    }
+  }
 
   if (al == 0 && inner >= kLongRow) {
     // Long rows: the workgroup walks one row at a time.

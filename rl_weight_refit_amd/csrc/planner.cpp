@@ -30,6 +30,7 @@
 #include <algorithm>
 #include <chrono>
 #include <cstring>
+#include <numeric>
 #include <sstream>
 #include <utility>
 
@@ -911,6 +912,9 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
       } else {
         f.bucket = kBulk;
         rpu = std::max<uint64_t>(1, o.unit / r.inner);
+        // Whole spread pieces per unit, where that keeps at least half of it.
+        const uint64_t m = kSpreadPiece / std::gcd<uint64_t>(r.inner, kSpreadPiece);
+        if (kSpread > 1 && rpu >= m) rpu -= rpu % m;
       }
       f.rows_per_unit = uint32_t(std::min<uint64_t>(rpu, f.rows));
       bytes_read += total;

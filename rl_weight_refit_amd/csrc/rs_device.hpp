@@ -18,6 +18,20 @@ constexpr int kMaxFan = 16;           // destination replicas per region
 constexpr uint32_t kThinTile = 16384; // LDS tile of the thin bucket, bytes
 constexpr uint32_t kLongRow = 2048;   // bulk rows at least this long are walked row by row
 constexpr uint32_t kChunkShift = 8;   // the unit table holds the region of every 256th unit
+// Bulk spread groups: kSpread consecutive whole units of a region are copied
+// together in pieces of kSpreadPiece bytes dealt round-robin to the group's
+// workgroups, so each workgroup's bytes are spread over the group's range
+// (kSpread 1: off).  The planner sizes bulk units to whole pieces where it can.
+#ifndef RS_SPREAD
+#define RS_SPREAD 8
+#endif
+#ifndef RS_SPREAD_PIECE
+#define RS_SPREAD_PIECE 1024
+#endif
+constexpr uint32_t kSpread = RS_SPREAD;
+constexpr uint32_t kSpreadPiece = RS_SPREAD_PIECE;
+static_assert(kSpread >= 1 && kSpreadPiece >= 16 && (kSpreadPiece & (kSpreadPiece - 1)) == 0,
+              "spread pieces are a power of two of 16-byte vectors");
 // MXFP8 work units are staged in LDS, kMxSlots 16-byte slots (8 bf16
 // elements each) per workgroup.  A row takes 2^mx_slot_shift(inner) slots
 // (the power of two at or above its 8-element groups, at least one 32-element
