@@ -32,7 +32,8 @@
 //        workgroups per CU keep their loads in flight.  Then two lanes per
 //        32-element block: integer amax, exact scaled E4M3 conversion, 16
 //        code bytes per lane; the block scales are gathered in LDS and
-//        written by consecutive lanes at the end.
+//        written by consecutive lanes at the end.  Units are taken in the
+//        same XCD turns as the bulk kernel's (6 % faster than dispatch order).
 //
 // Fan-out: a region may name up to 16 destination replicas; the data is read
 // once and stored to each (the one-GPU analogue of serving every replica from
@@ -100,7 +101,10 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) {
 #define RS_XCD_CHUNK 4096   // units per XCD turn (0: one contiguous eighth per XCD)
 #endif
 #ifndef RS_MX_XCD_MAP
-#define RS_MX_XCD_MAP 0  // MXFP8 kernel: same choice
+#define RS_MX_XCD_MAP 1  // MXFP8 kernel: same choice
+#endif
+#ifndef RS_MX_XCD_CHUNK
+#define RS_MX_XCD_CHUNK RS_XCD_CHUNK
 #endif
 
 // Work unit of workgroup b out of n.  Workgroups are dispatched round-robin
@@ -874,7 +878,7 @@ __device__ __forceinline__ void mx_unit(const LaunchArgs& a, const MxRegion* R, 
 __global__ __launch_bounds__(kMxThreads, RS_MX_MIN_WAVES) void rs_mx_kernel(LaunchArgs a) {
   __shared__ u32x4 stage[kMxSlots];
   __shared__ uint8_t sc_stage[kMxSlots / 4];
-  const uint32_t unit = unit_of_block<RS_MX_XCD_MAP != 0>(blockIdx.x, gridDim.x, RS_XCD_CHUNK);
+  const uint32_t unit = unit_of_block<RS_MX_XCD_MAP != 0>(blockIdx.x, gridDim.x, RS_MX_XCD_CHUNK);
   const MxRegion* R = find_region<MxRegion>(a, unit);
   const uint32_t r0 = (unit - R->unit_begin) * R->rows_per_unit;
   const uint32_t nr = min(R->rows_per_unit, R->rows - r0);
