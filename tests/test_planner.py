@@ -369,3 +369,25 @@ def test_binding_checks_per_slot_lengths(bad):
     dst = {"shape": [8, 8], "dtype": "i32", "mesh": [2], "placements": [1]}
     with pytest.raises(ValueError):
         binding.reshard_plan([spec], [dst])
+
+
+# Bulk work units hold whole 1 KiB pieces (the copy kernel deals pieces of
+# eight consecutive units round-robin to their workgroups) where that keeps
+# at least half a unit: 768-byte rows need a multiple of 4 rows, so a unit of
+# 8 / 16 / 32 / 64 KiB takes 8 / 20 / 40 / 84 rows, not 10 / 21 / 42 / 85;
+# 7 KiB rows are whole pieces already (2 rows per 16 KiB unit).
+@pytest.mark.parametrize("unit_bytes,units", [(8192, 4 * 50), (16384, 4 * 20), (32768, 4 * 10),
+                                              (65536, 4 * 5)])
+def test_bulk_units_hold_whole_pieces(unit_bytes, units):
+    import spread_layouts as sl
+    plan = lh.plan_workload(sl.flat_short_rows(), unit_bytes=unit_bytes)
+    assert plan.info()["units"]["bulk"] == units
+    assert lh.plan_workload(sl.rows_seven_pieces()).info()["units"]["bulk"] == 4 * 60
+
+
+@pytest.mark.parametrize("unit_bytes", [8192, 16384, 65536])
+@pytest.mark.parametrize("name", ["rows_two_outer", "rows_three_outer", "rows_seven_pieces",
+                                  "flat_short_rows", "flat_short_rows_fanout"])
+def test_interpreted_spread_layouts(name, unit_bytes):
+    import spread_layouts as sl
+    run_interpreted(sl.ALL[name](), unit_bytes=unit_bytes)
