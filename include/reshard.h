@@ -144,7 +144,10 @@ typedef struct rs_tensor_desc {
 typedef struct rs_plan_opts {
   uint32_t struct_size;   /* sizeof(rs_plan_opts) */
   uint32_t fanout;        /* 1 (default): destination replicas with equal views share one read */
-  uint64_t unit_bytes;    /* bulk work-unit size, power of two in [4096, 2^24]; default 16384 */
+  uint64_t unit_bytes;    /* bulk work-unit size, power of two in [4096, 2^24]; default 16384.
+                             A unit holds whole rows (rows longer than a unit are cut into
+                             unit-sized parts); its row count is trimmed to make the unit a whole
+                             number of KiB wherever that keeps at least half of it */
   uint32_t tiny_bytes;    /* regions of at most this many bytes are batched 64 per wave (0: none);
                              default 256 (larger regions copy faster one workgroup each) */
   uint32_t thin_bytes;    /* contiguous runs shorter than this are staged through LDS; default 128 */
