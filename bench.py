@@ -23,6 +23,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -40,12 +41,17 @@ KERNEL_SOURCES = [os.path.join(ROOT, "rl_weight_refit_amd", "csrc", f)
 
 
 def kernel_hash():
-    """Hash of the device code (kernels and the tables they read); counter
-    profiles taken from other sources are not reported as this kernel's."""
+    """Hash of the device code (kernels and the tables they read), comments
+    and blank lines left out; counter profiles taken from other code are not
+    reported as this kernel's."""
     h = hashlib.sha256()
     for path in KERNEL_SOURCES:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+        h.update(code.encode())
     return h.hexdigest()[:16]
 
 

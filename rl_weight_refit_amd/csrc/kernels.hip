@@ -891,9 +891,10 @@ __global__ __launch_bounds__(kMxThreads, RS_MX_MIN_WAVES) void rs_mx_kernel(Laun
 }  // namespace
 
 // Bulk workgroups resident per CU.  The copy streams best with fewer than
-// the register file would allow (on MI355X 4-5 per CU beat 7, and 3 or 6 are
-// slower), so each bulk launch asks for enough dynamic LDS, which the kernel
-// never touches, to leave room for only this many.  0 = no cap.
+// the register file would allow (on MI355X, with spread groups, 4 to 6 per CU
+// tie, 8 is about 1 % slower and 3 about 14 % slower), so each bulk launch
+// asks for enough dynamic LDS, which the kernel never touches, to leave room
+// for only this many.  0 = no cap.
 #ifndef RS_BULK_RESIDENT
 #define RS_BULK_RESIDENT 5
 #endif
