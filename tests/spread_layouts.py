@@ -20,12 +20,14 @@ def rows_two_outer():
     return {"name": "spread_rows_2", "buffers": {}, "tensors": [t]}
 
 
-def rows_three_outer():
+def rows_three_outer(replicas=1):
     """[8, 4, 64, 512] bf16, dim 0 split 2 ways -> dims 2 and 1 split on a
-    2 x 2 mesh: 16 KiB rows with e0 = 2, e1 = 2, e2 = 4 (nothing merges)."""
+    2 x 2 mesh (times `replicas` destination replicas): 16 KiB rows with
+    e0 = 2, e1 = 2, e2 = 4 (nothing merges)."""
+    mesh, pl = ([2, 2], [2, 1]) if replicas == 1 else ([2, 2, replicas], [2, 1, -1])
     t = {"name": "w", "shape": [8, 4, 64, 512], "dtype": "bf16", "src": synth.side([2], [0]),
-         "dst": synth.side([2, 2], [2, 1]), "values": dict(VALS)}
-    return {"name": "spread_rows_3", "buffers": {}, "tensors": [t]}
+         "dst": synth.side(mesh, pl), "values": dict(VALS)}
+    return {"name": "spread_rows_3x%d" % replicas, "buffers": {}, "tensors": [t]}
 
 
 def rows_seven_pieces():
@@ -56,5 +58,6 @@ def flat_short_rows(replicas=1):
 
 
 ALL = {"rows_two_outer": rows_two_outer, "rows_three_outer": rows_three_outer,
+       "rows_three_outer_fanout": lambda: rows_three_outer(3),
        "rows_seven_pieces": rows_seven_pieces, "flat_short_rows": flat_short_rows,
        "flat_short_rows_fanout": lambda: flat_short_rows(3)}

@@ -386,7 +386,7 @@ def test_bulk_units_hold_whole_pieces(unit_bytes, units):
 
 
 @pytest.mark.parametrize("unit_bytes", [8192, 16384, 65536])
-@pytest.mark.parametrize("name", ["rows_two_outer", "rows_three_outer", "rows_seven_pieces",
+@pytest.mark.parametrize("name", ["rows_two_outer", "rows_three_outer", "rows_three_outer_fanout", "rows_seven_pieces",
                                   "flat_short_rows", "flat_short_rows_fanout"])
 def test_interpreted_spread_layouts(name, unit_bytes):
     import spread_layouts as sl
