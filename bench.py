@@ -57,14 +57,16 @@ def kernel_hash():
 
 def parse():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--variant", choices=["both", "copy", "mxfp8"], default="both")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--plan-reps", type=int, default=1000)
-    ap.add_argument("--ceiling-bytes", type=int, default=8 << 30)
+    ap.add_argument("--gpus", type=int, default=1, help="must be 1: the relayout runs on one GPU")
+    ap.add_argument("--steps", type=int, default=10, help="timed steps")
+    ap.add_argument("--warmup", type=int, default=1, help="untimed steps before them")
+    ap.add_argument("--variant", choices=["both", "copy", "mxfp8"], default="both",
+                    help="what a step runs: the bf16 relayout, the MXFP8 install, or both")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing on the host")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the other layouts")
+    ap.add_argument("--plan-reps", type=int, default=1000, help="planner calls timed for plan_us")
+    ap.add_argument("--ceiling-bytes", type=int, default=8 << 30,
+                    help="size of the plain device copy timed as copy_ceiling_GBps")
     ap.add_argument("--procs", type=int, default=1,
                     help="run the bench in this many fresh processes and report their median")
     return ap.parse_args()
