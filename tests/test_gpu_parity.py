@@ -349,6 +349,18 @@ def test_fp8_blockwise_layer_small(kw):
     gh.check_against_oracle(synth.fp8_moe_experts(8, 256, 512, 4, 2, 2, seed=3, **kw))
 
 
+@pytest.mark.parametrize("src_split", [False, True])
+@pytest.mark.parametrize("shape", [(10, 256, 768, 4, 3, 2, 128), (6, 320, 384, 2, 3, 3, 64),
+                                   (5, 128, 256, 5, 1, 2, 128), (12, 384, 512, 3, 4, 4, 128)])
+def test_fp8_blockwise_uneven_expert_splits(shape, src_split):
+    """Blockwise FP8 with uneven expert splits (10 experts over 4 -> 3
+    ranks), three-way TP, 64-element blocks, a single destination EP rank
+    and per-expert source buffers: weight bytes and scales byte for byte."""
+    e, h, i, se, de, dt, b = shape
+    gh.check_against_oracle(synth.fp8_moe_experts(e, h, i, se, de, dt, seed=6, block=b,
+                                                  src_split=src_split))
+
+
 def test_fp8_blockwise_dsv3_shape_32_experts():
     """32 experts of the DeepSeek-V3 FP8 layer (hidden 7168, intermediate
     2048, 128 x 128 blocks), EP16 -> EP8 x TP8."""
