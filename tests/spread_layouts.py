@@ -61,3 +61,38 @@ ALL = {"rows_two_outer": rows_two_outer, "rows_three_outer": rows_three_outer,
        "rows_three_outer_fanout": lambda: rows_three_outer(3),
        "rows_seven_pieces": rows_seven_pieces, "flat_short_rows": flat_short_rows,
        "flat_short_rows_fanout": lambda: flat_short_rows(3)}
+
+
+def random_case(seed):
+    """Seeded random layouts with large regions for the spread paths: 2 to 4
+    dims, 1 to 12 MB, a last dim of 16 B .. 20 KiB (16-byte multiples or
+    not), source and destination meshes of 1 to 3 dims with Shard / Replicate
+    placements (so rows, outer dims, uneven splits and replicas vary), bf16,
+    f32 or u8 values."""
+    import numpy as np
+    rng = np.random.Generator(np.random.PCG64(70_000 + seed))
+    dtype = ["bf16", "f32", "u8"][int(rng.integers(3))]
+    es = {"bf16": 2, "f32": 4, "u8": 1}[dtype]
+    ndim = int(rng.integers(2, 5))
+    last_bytes = int(rng.choice([16, 48, 512, 768, 1024, 1040, 2048, 3072, 4096, 7168, 8192,
+                                 14336, 16384, 20480]))
+    if rng.random() < 0.3:
+        last_bytes += int(rng.integers(1, 16)) * es   # not a 16-byte multiple
+    last = max(1, last_bytes // es)
+    total = int(rng.integers(1 << 20, 12 << 20)) // es
+    rest = max(1, total // last)
+    shape = [last]
+    for d in range(ndim - 2):
+        k = int(rng.integers(2, 9))
+        shape.insert(0, k)
+        rest = max(1, rest // k)
+    shape.insert(0, rest)
+
+    def side_():
+        mdim = int(rng.integers(1, 4))
+        mesh = [int(rng.integers(1, 5)) for _ in range(mdim)]
+        pl = [int(rng.integers(-1, ndim)) for _ in mesh]
+        return synth.side(mesh, pl)
+    t = {"name": "t", "shape": shape, "dtype": dtype, "src": side_(), "dst": side_(),
+         "values": {"kind": "uniform", "seed": seed} if dtype != "u8" else {"kind": "index"}}
+    return {"name": "spread_random_%d" % seed, "buffers": {}, "tensors": [t]}

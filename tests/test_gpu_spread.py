@@ -39,3 +39,15 @@ def test_spread_layouts_shifted_pointers(name, shifts):
     """Buffers moved by 16 or 32 bytes keep the 16-byte alignment the spread
     paths need; a 4-byte shift takes the misaligned path instead."""
     gh.check_against_oracle(sl.ALL[name](), src_shift=shifts[0], dst_shift=shifts[1])
+
+
+@pytest.mark.parametrize("seed", range(80))
+def test_spread_random_layouts(seed):
+    """Seeded random layouts with large regions (row lengths, outer dims,
+    uneven splits and replicas all vary), a work unit of 8, 16 or 32 KiB and
+    buffers shifted by 0, 16 or 4 bytes."""
+    unit = (8192, 16384, 32768)[seed % 3]
+    shift = (0, 16, 4)[(seed // 3) % 3]
+    gh.log("spread random %d unit %d shift %d" % (seed, unit, shift))
+    gh.check_against_oracle(sl.random_case(seed), unit_bytes=unit, src_shift=shift,
+                            dst_shift=(shift * 3) % 32)

@@ -391,3 +391,9 @@ def test_bulk_units_hold_whole_pieces(unit_bytes, units):
 def test_interpreted_spread_layouts(name, unit_bytes):
     import spread_layouts as sl
     run_interpreted(sl.ALL[name](), unit_bytes=unit_bytes)
+
+
+@pytest.mark.parametrize("seed", range(0, 80, 8))
+def test_interpreted_spread_random_layouts(seed):
+    import spread_layouts as sl
+    run_interpreted(sl.random_case(seed), unit_bytes=(8192, 16384, 32768)[seed % 3])
