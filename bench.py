@@ -282,27 +282,32 @@ def secondary(torch, binding, stream):
                       "tensors": info["n_tensors"], "regions": info["regions"],
                       "launches": info["n_launches"], "plan_us": info["plan_ns"] / 1e3}
     del src, named, named2
-    # Tall-thin column slabs (the worked example's shape at scale): [1048576, 8]
-    # int32, rows split over 2 sources, columns over 4 destinations; each
-    # region is 524,288 rows x 8 bytes.  LDS-staged thin kernel vs the bulk
-    # kernel's direct path (thin bucket disabled).
-    wl = {"name": "slabs", "buffers": {}, "tensors": [
-        {"name": "w", "shape": [1 << 20, 8], "dtype": "i32", "src": synth.side([2], [0]),
-         "dst": synth.side([4], [1]), "values": {"kind": "uniform", "seed": 1}}]}
-    t = wl["tensors"][0]
-    srcs = [torch.empty((1 << 19) * 8 * 4, dtype=torch.uint8, device="cuda").fill_(7) for _ in range(2)]
-    dsts = [torch.empty((1 << 20) * 2 * 4, dtype=torch.uint8, device="cuda") for _ in range(4)]
-    sp = [x.data_ptr() for x in srcs]
-    dp = [x.data_ptr() for x in dsts]
-    slab = {}
-    for label, kw in (("lds_thin_kernel", {}), ("bulk_direct", {"thin_bytes": 1})):
-        plan = binding.reshard_plan([spec(t, "src")], [spec(t, "dst")], **kw)
-        info = plan.info()
-        ms = time_plan(torch, binding, plan, sp, dp, stream)
-        nb = info["bytes_read"] + info["bytes_written"]
-        slab[label] = {"ms": round(ms, 4), "GBps": round(nb / ms / 1e6, 1),
-                       "regions": info["regions"]}
-    out["column_slabs_1Mx8_i32_2row_to_4col"] = slab
+    # Tall-thin column slabs (the worked example's shape at scale): [R, 8]
+    # int32, rows split over 2 sources, columns over 4 destinations, each
+    # region R/2 rows x 8 bytes; R = 1M (32 MiB, cache-resident) and 16M
+    # (512 MiB each way, past the caches: the four column regions of a source
+    # row block share their reads only when they run together, as thin
+    # sibling groups).  LDS-staged thin kernel vs the bulk kernel's direct
+    # path (thin bucket disabled).
+    for rows, key in ((1 << 20, "column_slabs_1Mx8_i32_2row_to_4col"),
+                      (1 << 24, "column_slabs_16Mx8_i32_2row_to_4col")):
+        t = {"name": "w", "shape": [rows, 8], "dtype": "i32", "src": synth.side([2], [0]),
+             "dst": synth.side([4], [1]), "values": {"kind": "uniform", "seed": 1}}
+        srcs = [torch.empty((rows // 2) * 8 * 4, dtype=torch.uint8, device="cuda").fill_(7)
+                for _ in range(2)]
+        dsts = [torch.empty(rows * 2 * 4, dtype=torch.uint8, device="cuda") for _ in range(4)]
+        sp = [x.data_ptr() for x in srcs]
+        dp = [x.data_ptr() for x in dsts]
+        slab = {}
+        for label, kw in (("lds_thin_kernel", {}), ("bulk_direct", {"thin_bytes": 1})):
+            plan = binding.reshard_plan([spec(t, "src")], [spec(t, "dst")], **kw)
+            info = plan.info()
+            ms = time_plan(torch, binding, plan, sp, dp, stream)
+            nb = info["bytes_read"] + info["bytes_written"]
+            slab[label] = {"ms": round(ms, 4), "GBps": round(nb / ms / 1e6, 1),
+                           "regions": info["regions"]}
+        out[key] = slab
+        del srcs, dsts
     # Execution time of the uneven layouts (fp32 / bf16 [1000,3000] and
     # [7,513,257], meshes [3] / [2,3] -> [7] / [4,2]); small, cache-resident.
     ex = []

@@ -22,7 +22,10 @@
 //  thin  runs shorter than the thin threshold (e.g. the 8-byte rows of a
 //        column shard): rows are gathered through an LDS tile so the side
 //        that is contiguous across rows is written (or read) with 16-byte
-//        vectors.
+//        vectors.  Sibling regions (same source rows, different columns)
+//        take their units member-fastest, in short XCD turns, so the
+//        workgroups reading one block of source rows run together on one
+//        XCD and share its lines instead of each fetching them from HBM.
 //  tiny  regions of at most a few hundred bytes: one lane per region, a
 //        wave-level prefix sum of their granule counts, then all 64 lanes
 //        share the wave's granules.
@@ -99,6 +102,9 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) {
 #endif
 #ifndef RS_XCD_CHUNK
 #define RS_XCD_CHUNK 4096   // units per XCD turn (0: one contiguous eighth per XCD)
+#endif
+#ifndef RS_THIN_XCD_CHUNK
+#define RS_THIN_XCD_CHUNK 16  // thin kernel: units per XCD turn (0: dispatch order)
 #endif
 #ifndef RS_MX_XCD_MAP
 #define RS_MX_XCD_MAP 1  // MXFP8 kernel: same choice
@@ -513,13 +519,25 @@ __global__ __launch_bounds__(kThreads, RS_BULK_MIN_WAVES) void rs_bulk_kernel(La
 __global__ __launch_bounds__(kThreads) void rs_thin_kernel(LaunchArgs a) {
   __shared__ __attribute__((aligned(16))) char tile[kThinTile + 16];
   const uint32_t tid = threadIdx.x;
-  const uint32_t unit = blockIdx.x;
+  const uint32_t unit = unit_of_block<RS_THIN_XCD_CHUNK != 0>(blockIdx.x, gridDim.x, RS_THIN_XCD_CHUNK);
   const CopyRegion* R = find_region<CopyRegion>(a, unit);
+  uint32_t ul = unit - R->unit_begin;
+  const uint32_t gm = (R->flags >> 16) & 255u;
+  if (gm > 1) {
+    // Sibling group (same source rows, different columns): its units are
+    // taken member-fastest, so the workgroups reading the same source rows
+    // run together and share the fetched lines.
+    const uint32_t m = R->flags >> 24;
+    const uint32_t nu = (R->rows + R->rows_per_unit - 1) / R->rows_per_unit;
+    const uint32_t local = ul + m * nu;
+    R = R - m + local % gm;
+    ul = local / gm;
+  }
   const uint64_t src_off = R->src_off, dst_off = R->dst_off;
   const uint64_t s0 = R->sstr[0], s1 = R->sstr[1], s2 = R->sstr[2];
   const uint64_t d0 = R->dstr[0], d1 = R->dstr[1], d2 = R->dstr[2];
   const uint32_t e0 = R->e0, e1 = R->e1, rows = R->rows, inner = R->inner;
-  const uint32_t rpu = R->rows_per_unit, ub = R->unit_begin, flags = R->flags;
+  const uint32_t rpu = R->rows_per_unit, flags = R->flags;
   const uint32_t nd = R->n_dst;
   const uint32_t nouter = flags & kFlagOuterMask;
   const char* sp = static_cast<const char*>(a.ptr[R->src_ptr]) + src_off;
@@ -531,7 +549,7 @@ __global__ __launch_bounds__(kThreads) void rs_thin_kernel(LaunchArgs a) {
   const uint32_t g = low_granule(al);
   const uint32_t gpr = inner / g;
 
-  const uint32_t r0 = (unit - ub) * rpu;
+  const uint32_t r0 = ul * rpu;
   const uint32_t r1 = min(r0 + rpu, rows);
   const uint32_t T = r1 - r0;
   const uint32_t nbytes = T * inner;

@@ -427,6 +427,10 @@ void merge_outer(Dims& o, bool with_scale) {
   o = m;
 }
 
+#ifndef RS_THIN_SIBLINGS
+#define RS_THIN_SIBLINGS 1   // group thin regions that read the same source rows
+#endif
+
 struct Opts {
   bool fanout = true;
   uint64_t unit = 16384;
@@ -1017,6 +1021,36 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
       out.image.resize(out.image.size() + rsz * batch.size(), 0);
       uint32_t ub = 0;
       std::vector<uint32_t> unit_region;
+      // Thin sibling groups: consecutive thin regions that read the same
+      // source rows (same source buffer, outer dims and row count, column
+      // offsets within one source row) take their units interleaved in the
+      // kernel, so the workgroups reading the same rows run together and
+      // share the fetched lines.  Flags bits 16-23 hold the group size,
+      // bits 24-31 the member index.
+      std::vector<uint32_t> sib(batch.size(), 0);
+      if (RS_THIN_SIBLINGS && bucket == kThin) {
+        auto same_rows = [](const Final& x, const Final& y) {
+          if (x.rp->src_index != y.rp->src_index || x.rows != y.rows || x.units != y.units ||
+              x.rows_per_unit != y.rows_per_unit || x.rp->outer.size() != y.rp->outer.size() ||
+              x.rp->outer.size() == 0)
+            return false;
+          uint64_t xe[3], xs[3], xd[3], xc[3], ye[3], ys[3], yd[3], yc[3];
+          outer_fields(x.rp->outer, xe, xs, xd, xc);
+          outer_fields(y.rp->outer, ye, ys, yd, yc);
+          for (int q = 0; q < 3; ++q)
+            if (xe[q] != ye[q] || xs[q] != ys[q]) return false;
+          const uint64_t a = x.rp->src_off, b = y.rp->src_off;
+          return (a > b ? a - b : b - a) < xs[0];
+        };
+        size_t k = 0;
+        while (k < batch.size()) {
+          size_t e = k + 1;
+          while (e < batch.size() && e - k < 255 && same_rows(*batch[k], *batch[e])) ++e;
+          if (e - k >= 2)
+            for (size_t q = k; q < e; ++q) sib[q] = (uint32_t(e - k) << 16) | (uint32_t(q - k) << 24);
+          k = e;
+        }
+      }
       for (size_t k = 0; k < batch.size(); ++k) {
         const Final& f = *batch[k];
         const Raw& r = *f.rp;
@@ -1066,7 +1100,7 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
           c.inner = uint32_t(r.inner);
           c.rows_per_unit = f.rows_per_unit;
           c.unit_begin = ub;
-          c.flags = f.flags | (uint32_t(al & 15) << 8);
+          c.flags = f.flags | (uint32_t(al & 15) << 8) | sib[k];
           c.src_ptr = pool(r.src_index);
           c.n_dst = uint16_t(r.n_dst);
           for (uint32_t j = 0; j < r.n_dst; ++j) c.dst_ptr[j] = pool(r.dst_index[j] | kDstBit);

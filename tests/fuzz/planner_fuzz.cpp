@@ -28,6 +28,7 @@ namespace {
 
 uint64_t g_bucket_regions[4] = {};   // regions replayed, per bucket
 uint64_t g_valid_rejected = 0;       // uncorrupted cases the planner declined (e.g. MXFP8 blocks across sources)
+uint64_t g_sibling_groups = 0;       // thin sibling groups checked
 
 struct Rng {
   uint64_t s;
@@ -300,6 +301,48 @@ bool run_case(Rng& g, uint64_t c, bool corrupt) {
   if (sbuf.size() != P.info.n_src_ptrs || dbuf.size() != P.info.n_dst_ptrs)
     die("pointer counts differ from the documented order", c);
 
+  // Work units as the copy kernels take them: every launch's units cover
+  // each of its regions' units exactly once.  Thin sibling groups (flags
+  // bits 16-31) must be consecutive regions with equal unit counts, which
+  // the thin kernel relies on when it takes their units member-fastest.
+  for (const rs::Launch& L : P.launches) {
+    if (L.bucket == rs::kTiny || L.bucket == rs::kMx) continue;
+    const rs::CopyRegion* regs = reinterpret_cast<const rs::CopyRegion*>(P.image.data() + L.regions_off);
+    std::vector<std::vector<uint8_t>> seen(L.n_regions);
+    for (uint32_t k = 0; k < L.n_regions; ++k) {
+      const uint32_t nu = (regs[k].rows + regs[k].rows_per_unit - 1) / regs[k].rows_per_unit;
+      seen[k].assign(nu, 0);
+      const uint32_t gm = (regs[k].flags >> 16) & 255u, m = regs[k].flags >> 24;
+      if (L.bucket != rs::kThin && gm) die("sibling group outside the thin bucket", c);
+      if (gm == 1 || (gm && m >= gm) || (!gm && m)) die("bad sibling group fields", c);
+      if (gm && (k < m || k - m + gm > L.n_regions)) die("sibling group leaves its launch", c);
+      if (gm && m == 0) ++g_sibling_groups;
+      if (gm) {
+        const rs::CopyRegion& h = regs[k - m];
+        if (((h.flags >> 16) & 255u) != gm || (h.flags >> 24) != 0 || h.rows != regs[k].rows ||
+            h.rows_per_unit != regs[k].rows_per_unit || h.unit_begin + m * nu != regs[k].unit_begin)
+          die("sibling group members differ", c);
+      }
+    }
+    for (uint32_t u = 0; u < L.n_units; ++u) {
+      uint32_t k = 0;
+      while (k + 1 < L.n_regions && regs[k + 1].unit_begin <= u) ++k;
+      uint32_t ul = u - regs[k].unit_begin;
+      const uint32_t gm = (regs[k].flags >> 16) & 255u;
+      if (gm > 1) {
+        const uint32_t m = regs[k].flags >> 24;
+        const uint32_t nu = (regs[k].rows + regs[k].rows_per_unit - 1) / regs[k].rows_per_unit;
+        const uint32_t local = ul + m * nu;
+        k = k - m + local % gm;
+        ul = local / gm;
+      }
+      if (ul >= seen[k].size() || seen[k][ul]++) die("a work unit is missed or taken twice", c);
+    }
+    for (const auto& v : seen)
+      for (uint8_t x : v)
+        if (x != 1) die("a work unit is not taken", c);
+  }
+
   // Replay every region.
   for (uint64_t k = 0; k < P.info.n_regions; ++k) {
     rs_region R;
@@ -405,8 +448,9 @@ int main(int argc, char** argv) {
   }
   std::printf("cases %" PRIu64 ": planned and replayed %" PRIu64 ", rejected %" PRIu64
               " (%" PRIu64 " of them uncorrupted, unsupported), corrupted but accepted %" PRIu64
-              "; regions replayed: bulk %" PRIu64 ", thin %" PRIu64 ", tiny %" PRIu64 ", mxfp8 %" PRIu64 "\n",
+              "; regions replayed: bulk %" PRIu64 ", thin %" PRIu64 ", tiny %" PRIu64 ", mxfp8 %" PRIu64
+              "; thin sibling groups %" PRIu64 "\n",
               cases, planned, rejected, g_valid_rejected, corrupt_ok, g_bucket_regions[0],
-              g_bucket_regions[1], g_bucket_regions[2], g_bucket_regions[3]);
+              g_bucket_regions[1], g_bucket_regions[2], g_bucket_regions[3], g_sibling_groups);
   return 0;
 }

@@ -2,8 +2,10 @@
 code only, built with g++, no GPU): tests/fuzz/planner_fuzz.cpp plans
 random layouts, replays every region on host buffers of exactly the size
 each view needs, and checks that every destination element is written
-exactly once with its own global index; corrupted descriptors must be
-rejected with a message.  Any sanitizer report fails the run.
+exactly once with its own global index, and walks each copy launch's work
+units as the kernels take them (thin sibling groups member-fastest) to check
+that every unit of every region is taken exactly once; corrupted descriptors
+must be rejected with a message.  Any sanitizer report fails the run.
 """
 
 import os
@@ -40,3 +42,5 @@ def test_planner_fuzz_sanitized(fuzz_exe, seed):
                        env=env)
     assert r.returncode == 0, (r.stdout[-4000:] + r.stderr[-4000:])
     assert "planned and replayed" in r.stdout
+    groups = int(r.stdout.split("thin sibling groups")[1].split()[0])
+    assert groups > 0, r.stdout
