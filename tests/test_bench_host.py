@@ -1,0 +1,35 @@
+"""Host-side checks of bench.py (no GPU): the one-GPU refusal, and the
+device-source hash that decides whether committed counter profiles belong to
+the kernels being timed (comments and blank lines do not count, code does)."""
+
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_kernel_hash_ignores_comments_not_code(tmp_path, monkeypatch):
+    copies = []
+    for path in bench.KERNEL_SOURCES:
+        q = tmp_path / os.path.basename(path)
+        q.write_text(open(path, encoding="utf-8").read(), encoding="utf-8")
+        copies.append(q)
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", [str(q) for q in copies])
+    h0 = bench.kernel_hash()
+    text = copies[0].read_text(encoding="utf-8")
+    copies[0].write_text("// a new comment line\n\n" + text.replace("\n", "  \n", 3) +
+                         "\n/* a block\n   comment */\n", encoding="utf-8")
+    assert bench.kernel_hash() == h0
+    copies[0].write_text(text.replace("kThreads", "kThreads ", 1) + "\nstatic int x;\n",
+                         encoding="utf-8")
+    assert bench.kernel_hash() != h0
