@@ -218,6 +218,18 @@ def secondary(torch, binding, stream):
     after the timed region (not part of `value`)."""
     from rl_weight_refit_amd import synth
     out = {}
+    # The library's own copy on the plainest layout (one contiguous 8 GiB
+    # region, identity relayout): the reference the relayouts compare with.
+    n = 8 << 30
+    t = {"name": "flat", "shape": [n], "dtype": "u8", "src": synth.side([1], [-1]),
+         "dst": synth.side([1], [-1]), "values": {"kind": "index"}}
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    plan = binding.reshard_plan([spec(t, "src")], [spec(t, "dst")])
+    ms = time_plan(torch, binding, plan, [a.data_ptr()], [b.data_ptr()], stream)
+    out["plain_copy_8GiB_contiguous"] = {"ms": round(ms, 4), "GBps": round(2 * n / ms / 1e6, 1)}
+    plan.destroy()
+    del a, b
     for name, wl in (("dense_ffn_4096x14336_tp4_to_tp2xdp2", synth.dense_ffn()),
                      ("moe_128e_4096x1536_ep8_to_ep4xtp4", synth.moe_128e())):
         src = device_sources(torch, binding, wl)
