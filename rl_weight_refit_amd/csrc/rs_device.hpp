@@ -77,7 +77,9 @@ struct alignas(16) CopyRegion {
   uint32_t rows_per_unit;
   uint32_t unit_begin;      // first work unit of this region in its launch
   uint32_t flags;           // bits 0-7: kFlag*; bits 8-11: low bits of the OR of
-                            // offsets, strides and inner (they bound the vector width)
+                            // offsets, strides and inner (they bound the vector width);
+                            // thin regions, bits 16-23: size of the sibling group the
+                            // region belongs to (0: none), bits 24-31: its index there
   uint16_t src_ptr;         // index into the launch's pointer pool
   uint16_t n_dst;
   uint16_t dst_ptr[kMaxFan];
