@@ -149,8 +149,11 @@ typedef struct rs_plan_opts {
                              unit-sized parts); its row count is trimmed to make the unit a whole
                              number of KiB wherever that keeps at least half of it */
   uint32_t tiny_bytes;    /* regions of at most this many bytes are batched 64 per wave (0: none);
-                             default 256 (larger regions copy faster one workgroup each) */
-  uint32_t thin_bytes;    /* contiguous runs shorter than this are staged through LDS; default 128 */
+                             default 256 (larger regions copy faster one workgroup each);
+                             at most 65536, else RS_ERR_INVALID */
+  uint32_t thin_bytes;    /* contiguous runs shorter than this are staged through LDS; default 128
+                             (0: default); at most 16384 (the LDS tile a thin work unit fills),
+                             else RS_ERR_INVALID */
   uint32_t reserved[4];   /* must be zero */
 } rs_plan_opts;
 

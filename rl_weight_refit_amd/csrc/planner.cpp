@@ -40,6 +40,7 @@ namespace {
 constexpr int64_t kMaxSlots = 65536;
 constexpr uint64_t kMaxRows = (1ull << 31) - 1;
 constexpr uint32_t kMaxUnitsPerLaunch = 1u << 23;
+constexpr uint32_t kMaxTinyBytes = 1u << 16;   // largest opts.tiny_bytes
 constexpr int kMxBlock = 32;
 
 int esize_of(int32_t dt) {
@@ -588,6 +589,14 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
       E.add(&E.invalid, "opts.unit_bytes = ", u, " is not a power of two in [4096, 2^24]");
     for (int i = 0; i < 4; ++i)
       if (popts->reserved[i]) E.add(&E.invalid, "opts.reserved[", i, "] must be 0");
+    // The thin kernel stages a unit of whole rows in its kThinTile LDS tile,
+    // so no thin row may be longer than the tile; the tiny kernel numbers a
+    // wave's granules (up to 64 regions of tiny_bytes) with 32-bit counters.
+    if (popts->thin_bytes > kThinTile)
+      E.add(&E.invalid, "opts.thin_bytes = ", popts->thin_bytes, " exceeds the ", kThinTile,
+            "-byte LDS tile of the thin kernel");
+    if (popts->tiny_bytes > kMaxTinyBytes)
+      E.add(&E.invalid, "opts.tiny_bytes = ", popts->tiny_bytes, " exceeds ", kMaxTinyBytes);
     o.fanout = popts->fanout != 0;
     o.unit = u;
     o.tiny = popts->tiny_bytes;

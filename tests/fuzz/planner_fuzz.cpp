@@ -159,8 +159,8 @@ bool run_case(Rng& g, uint64_t c, bool corrupt) {
   opts.struct_size = sizeof(opts);
   opts.fanout = g.coin(80) ? 1 : 0;
   opts.unit_bytes = g.coin(70) ? 0 : (4096u << g.uni(0, 4));
-  opts.tiny_bytes = g.coin(50) ? 1024 : (g.coin(50) ? 0 : uint32_t(g.uni(0, 4096)));
-  opts.thin_bytes = g.coin(70) ? 128 : uint32_t(g.uni(1, 4096));
+  opts.tiny_bytes = g.coin(50) ? 1024 : (g.coin(50) ? 0 : (g.coin(90) ? uint32_t(g.uni(0, 4096)) : 65536u));
+  opts.thin_bytes = g.coin(70) ? 128 : (g.coin(80) ? uint32_t(g.uni(1, 4096)) : uint32_t(g.uni(4096, 16384)));
 
   std::vector<rs_tensor_desc> S(nt), D(nt);
   for (int t = 0; t < nt; ++t) {

@@ -266,6 +266,43 @@ def test_sizes_past_the_64_bit_range_are_rejected(field, value, needle):
     assert e.value.status == 1 and needle in str(e.value)
 
 
+@pytest.mark.parametrize("kw,ok", [
+    ({"thin_bytes": 16384}, True), ({"thin_bytes": 16385}, False),
+    ({"thin_bytes": 1 << 20}, False),
+    ({"tiny_bytes": 65536}, True), ({"tiny_bytes": 65537}, False),
+    ({"tiny_bytes": 1 << 31}, False),
+])
+def test_thin_and_tiny_thresholds_are_bounded(kw, ok):
+    """A thin work unit stages its rows in a 16 KiB LDS tile, and the tiny
+    kernel counts a wave's granules in 32 bits: thresholds past those limits
+    are refused instead of planning rows the kernels cannot hold."""
+    t = {"name": "w", "shape": [64, 4000], "dtype": "u8", "src": synth.side([2], [0]),
+         "dst": synth.side([4], [1]), "values": {"kind": "index"}}
+    wl = {"name": "bounds", "buffers": {}, "tensors": [t]}
+    if ok:
+        plan = lh.plan_workload(wl, **kw)
+        for r in plan.regions():
+            if r["bucket"] == "thin":
+                assert r["inner"] < 16384
+    else:
+        with pytest.raises(binding.ReshardError) as e:
+            lh.plan_workload(wl, **kw)
+        assert e.value.status == 1 and ("thin_bytes" in str(e.value) or "tiny_bytes" in str(e.value))
+
+
+def test_thin_rows_at_the_tile_limit_interpret_correctly():
+    """Rows of 16,383 bytes with the largest thin threshold go through the
+    thin bucket one row per unit; the host interpreter of the plan matches
+    the oracle."""
+    t = {"name": "w", "shape": [6, 2 * 16383], "dtype": "u8", "src": synth.side([1], [-1]),
+         "dst": synth.side([2], [1]), "values": {"kind": "index"}}
+    wl = {"name": "thin_limit", "buffers": {}, "tensors": [t]}
+    plan, _, count = run_interpreted(wl, thin_bytes=16384, tiny_bytes=0)
+    assert {r["bucket"] for r in plan.regions()} == {"thin"}
+    assert all(r["inner"] == 16383 for r in plan.regions())
+    assert_exact_once(count)
+
+
 def test_view_reaching_past_the_64_bit_range_is_rejected():
     src = {"shape": [8, 8], "dtype": "f32", "mesh": [2], "placements": [0]}
     dst = {"shape": [8, 8], "dtype": "f32", "mesh": [2], "placements": [0],
