@@ -179,9 +179,12 @@ def device_destinations(torch, binding, wl):
     return named, ptrs
 
 
-def copy_ceiling(torch, nbytes, stream):
-    """Plain device-to-device copy of nbytes (torch's copy kernel), GB/s of
-    read + write, best of 5."""
+def copy_ceiling(torch, binding, nbytes, stream):
+    """Plain contiguous device-to-device copies of nbytes, GB/s of read +
+    write: torch's copy_ (best of 6) and this library's own copy of the
+    same bytes as one region (identity layout, median of 10).  The ceiling
+    is the faster of the two."""
+    from rl_weight_refit_amd import synth
     a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
     a.fill_(1)
@@ -195,17 +198,31 @@ def copy_ceiling(torch, nbytes, stream):
             e1.record(stream)
             e1.synchronize()
             best = max(best, 2 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    t = {"name": "flat", "shape": [nbytes], "dtype": "u8", "src": synth.side([1], [-1]),
+         "dst": synth.side([1], [-1]), "values": {"kind": "index"}}
+    plan = binding.reshard_plan([spec(t, "src")], [spec(t, "dst")])
+    ms = time_plan(torch, binding, plan, [a.data_ptr()], [b.data_ptr()], stream)
+    plan.destroy()
+    lib = 2 * nbytes / (ms * 1e-3) / 1e9
     del a, b
-    return best
+    return {"GBps": round(max(best, lib), 1), "torch_copy_GBps": round(best, 1),
+            "library_copy_GBps": round(lib, 1), "bytes_each_way": nbytes}
 
 
-def time_plan(torch, binding, plan, src_ptrs, dst_ptrs, stream, reps=10):
-    """Median event-timed execute of a plan on `stream` (ms)."""
+def time_plan(torch, binding, plan, src_ptrs, dst_ptrs, stream, reps=10, poison=()):
+    """Median event-timed execute of a plan on `stream` (ms).  The buffers
+    in `poison` are filled with 0xFF on the stream before every timed rep,
+    outside the timed events, so no rep finds the previous rep's output in a
+    cache."""
     for _ in range(2):
         binding.reshard_execute(plan, src_ptrs, dst_ptrs, stream.cuda_stream)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(reps)]
     for a, b in evs:
+        if poison:
+            with torch.cuda.stream(stream):
+                for t in poison:
+                    t.fill_(0xFF)
         a.record(stream)
         binding.reshard_execute(plan, src_ptrs, dst_ptrs, stream.cuda_stream)
         b.record(stream)
@@ -218,18 +235,6 @@ def secondary(torch, binding, stream):
     after the timed region (not part of `value`)."""
     from rl_weight_refit_amd import synth
     out = {}
-    # The library's own copy on the plainest layout (one contiguous 8 GiB
-    # region, identity relayout): the reference the relayouts compare with.
-    n = 8 << 30
-    t = {"name": "flat", "shape": [n], "dtype": "u8", "src": synth.side([1], [-1]),
-         "dst": synth.side([1], [-1]), "values": {"kind": "index"}}
-    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-    b = torch.empty_like(a)
-    plan = binding.reshard_plan([spec(t, "src")], [spec(t, "dst")])
-    ms = time_plan(torch, binding, plan, [a.data_ptr()], [b.data_ptr()], stream)
-    out["plain_copy_8GiB_contiguous"] = {"ms": round(ms, 4), "GBps": round(2 * n / ms / 1e6, 1)}
-    plan.destroy()
-    del a, b
     for name, wl in (("dense_ffn_4096x14336_tp4_to_tp2xdp2", synth.dense_ffn()),
                      ("moe_128e_4096x1536_ep8_to_ep4xtp4", synth.moe_128e())):
         src = device_sources(torch, binding, wl)
@@ -237,10 +242,11 @@ def secondary(torch, binding, stream):
         named, dp = device_destinations(torch, binding, wl)
         plan = plan_of(binding, wl)
         info = plan.info()
-        ms = time_plan(torch, binding, plan, sp, dp, stream)
+        ms = time_plan(torch, binding, plan, sp, dp, stream, poison=list(named.values()))
         nb = info["bytes_read"] + info["bytes_written"]
+        nbf = info["bytes_read_no_fanout"] + info["bytes_written"]
         out[name] = {"ms": round(ms, 4), "GBps": round(nb / ms / 1e6, 1), "bytes": nb,
-                     "bytes_no_fanout": info["bytes_read_no_fanout"] + info["bytes_written"],
+                     "bytes_no_fanout": nbf, "GBps_no_fanout_credit": round(nbf / ms / 1e6, 1),
                      "regions": info["n_regions"]}
         del src, named
     # The DSV3 layer with every source expert in a buffer of its own (no
@@ -251,7 +257,7 @@ def secondary(torch, binding, stream):
     named, dp = device_destinations(torch, binding, wl)
     plan = plan_of(binding, wl)
     info = plan.info()
-    ms = time_plan(torch, binding, plan, sp, dp, stream)
+    ms = time_plan(torch, binding, plan, sp, dp, stream, poison=list(named.values()))
     nb = info["bytes_read"] + info["bytes_written"]
     out["moe_dsv3_per_expert_sources"] = {"ms": round(ms, 4), "GBps": round(nb / ms / 1e6, 1),
                                           "bytes": nb, "regions": info["n_regions"],
@@ -267,7 +273,7 @@ def secondary(torch, binding, stream):
     named, dp = device_destinations(torch, binding, wl)
     plan = plan_of(binding, wl)
     info = plan.info()
-    ms = time_plan(torch, binding, plan, sp, dp, stream)
+    ms = time_plan(torch, binding, plan, sp, dp, stream, poison=list(named.values()))
     nb = info["bytes_read"] + info["bytes_written"]
     out["fp8_blockwise_dsv3_with_scales"] = {"ms": round(ms, 4), "GBps": round(nb / ms / 1e6, 1),
                                              "bytes": nb, "regions": info["regions"],
@@ -288,7 +294,8 @@ def secondary(torch, binding, stream):
             named2, dp = device_destinations(torch, binding, w)
         plan = plan_of(binding, w)
         info = plan.info()
-        ms = time_plan(torch, binding, plan, sp, dp, stream)
+        ms = time_plan(torch, binding, plan, sp, dp, stream,
+                       poison=list((named if label.startswith("misc_pack") else named2).values()))
         nb = info["bytes_read"] + info["bytes_written"]
         out[label] = {"ms": round(ms, 4), "GBps": round(nb / ms / 1e6, 1), "bytes": nb,
                       "tensors": info["n_tensors"], "regions": info["regions"],
@@ -314,7 +321,7 @@ def secondary(torch, binding, stream):
         for label, kw in (("lds_thin_kernel", {}), ("bulk_direct", {"thin_bytes": 1})):
             plan = binding.reshard_plan([spec(t, "src")], [spec(t, "dst")], **kw)
             info = plan.info()
-            ms = time_plan(torch, binding, plan, sp, dp, stream)
+            ms = time_plan(torch, binding, plan, sp, dp, stream, poison=dsts)
             nb = info["bytes_read"] + info["bytes_written"]
             slab[label] = {"ms": round(ms, 4), "GBps": round(nb / ms / 1e6, 1),
                            "regions": info["regions"]}
@@ -353,6 +360,12 @@ def secondary(torch, binding, stream):
     return out
 
 
+def device_info(torch):
+    p = torch.cuda.get_device_properties(0)
+    return {"name": torch.cuda.get_device_name(0), "arch": getattr(p, "gcnArchName", None),
+            "compute_units": p.multi_processor_count, "memory_GiB": round(p.total_memory / 2**30, 1)}
+
+
 def host_info():
     model = None
     try:
@@ -366,15 +379,62 @@ def host_info():
     return {"nproc": os.cpu_count(), "cpu_model": model}
 
 
-def cpu_baseline(experts=16, threads=6):
+def host_workers():
+    """Worker processes for the parallel oracle leg: the host CPUs available
+    to this process, at most 16 (the CPU share of one GPU on the box)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, os.cpu_count() or n, 16))
+
+
+_FORK_JOB = None
+
+
+def _fork_call(i):
+    fn, items = _FORK_JOB
+    fn(items[i])
+    return 0
+
+
+def fork_map(n):
+    """A map over n forked worker processes: the function and its items are
+    inherited by the workers (nothing is pickled but an index), so a worker
+    sees the oracle's assembled tensor and writes its destination slots into
+    the shared-memory images the parent reads."""
+    import multiprocessing as mp
+
+    def run(fn, items):
+        global _FORK_JOB
+        _FORK_JOB = (fn, list(items))
+        with mp.get_context("fork").Pool(n) as pool:
+            pool.map(_fork_call, range(len(_FORK_JOB[1])), chunksize=1)
+        _FORK_JOB = None
+        return []
+    return run
+
+
+def shared_image(arr):
+    """Copy of a host byte image in anonymous shared memory (visible to
+    forked workers' writes)."""
+    import mmap
+    m = mmap.mmap(-1, max(arr.nbytes, 1))
+    out = np.frombuffer(m, dtype=np.uint8, count=arr.nbytes)
+    out[:] = arr.reshape(-1)
+    return out
+
+
+def cpu_baseline(experts=16):
     """The oracle (as it stands) on a bounded sample of the same workload: the
     same layer shape and meshes with `experts` experts instead of 256, bf16
     relayout plus MXFP8 install, on the host.  Timed once with the six oracle
-    calls (3 tensors x 2 variants) one after another on one core, and once
-    with the same calls spread over a thread pool (numpy releases the GIL in
-    its copies).  Returns (single, threaded)."""
-    from concurrent.futures import ThreadPoolExecutor
-
+    calls (3 tensors x 2 variants) one after another in this process, and once
+    with each call's destination slots spread over forked worker processes,
+    one per available host CPU (the oracle's MXFP8 step is a Python loop over
+    blocks that holds the GIL, so threads would not run it in parallel).
+    Must run before this process touches the GPU.  Returns (parallel,
+    single)."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from oracle import golden as ogolden
     from rl_weight_refit_amd import synth
@@ -391,32 +451,37 @@ def cpu_baseline(experts=16, threads=6):
             one = dict(wl)
             one["tensors"] = [t]
             _, per = helpers.alloc_destinations(one)
+            shared = {}
+            for e in per[0]:
+                for key in ("buf", "scale_buf"):
+                    if key in e:
+                        if id(e[key]) not in shared:
+                            shared[id(e[key])] = shared_image(e[key])
+                        e[key] = shared[id(e[key])]
             jobs.append((helpers.src_desc_for(t), helpers.odesc(t, "dst"), src, per[0]))
             n = int(np.prod(t["shape"]))
             # bf16 relayout: 2n read + 2n written; MXFP8: 2n read + n codes + n/32 scales
             total_bytes += 4 * n if quant is None else 3 * n + n // 32
 
-    def run(job):
-        ogolden.reshard(*job)
-
     t0 = time.perf_counter()
     for job in jobs:
-        run(job)
+        ogolden.reshard(*job)
     single = time.perf_counter() - t0
-    nthr = min(threads, len(jobs))
-    with ThreadPoolExecutor(max_workers=nthr) as ex:
-        t0 = time.perf_counter()
-        list(ex.map(run, jobs))
-        threaded = time.perf_counter() - t0
+    nw = host_workers()
+    t0 = time.perf_counter()
+    for job in jobs:
+        ogolden.reshard(*job, map_fn=fork_map(nw))
+    parallel = time.perf_counter() - t0
     sample = ("same layer shape and meshes with %d of 256 experts (%d/256 of the bytes), bf16 relayout + "
               "MXFP8 install, numpy on the host" % (experts, experts))
-    one = {"value": round(total_bytes / single / 1e9, 4), "unit": "GB/s", "cores": 1,
-           "kind": "oracle", "sample": sample + ", one call after another, %.1f s" % single}
-    many = {"value": round(total_bytes / threaded / 1e9, 4), "unit": "GB/s", "cores": nthr,
-            "kind": "oracle", "sample": sample + ", the %d oracle calls (tensor x variant) on a thread "
-                                                 "pool of %d, %.1f s" % (len(jobs), nthr, threaded),
+    many = {"value": round(total_bytes / parallel / 1e9, 4), "unit": "GB/s", "cores": nw,
+            "kind": "oracle", "sample": sample + ", each of the %d oracle calls (tensor x variant) with "
+                                                 "its destination slots on %d forked worker processes, "
+                                                 "%.1f s" % (len(jobs), nw, parallel),
             "host": host_info()}
-    return one, many
+    one = {"value": round(total_bytes / single / 1e9, 4), "unit": "GB/s", "cores": 1,
+           "kind": "oracle", "sample": sample + ", one call after another in one process, %.1f s" % single}
+    return many, one
 
 
 def main():
@@ -428,6 +493,12 @@ def main():
         return 2
     if args.procs > 1:
         return run_processes(args)
+    # The oracle's CPU baseline forks worker processes, so it runs before
+    # anything here touches the GPU.
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("cpu baseline ...", file=sys.stderr, flush=True)
+        cpu = cpu_baseline()
     import torch
     from rl_weight_refit_amd import binding, synth
 
@@ -456,7 +527,8 @@ def main():
           file=sys.stderr, flush=True)
 
     stream = torch.cuda.Stream()
-    ceiling = copy_ceiling(torch, args.ceiling_bytes, stream) if args.ceiling_bytes else None
+    ceil_info = copy_ceiling(torch, binding, args.ceiling_bytes, stream) if args.ceiling_bytes else None
+    ceiling = ceil_info["GBps"] if ceil_info else None
     print("copy ceiling %.1f GB/s" % (ceiling or 0), file=sys.stderr, flush=True)
 
     src = device_sources(torch, binding, wl_copy)
@@ -512,6 +584,18 @@ def main():
     wall = time.perf_counter() - t0
     print("timed %d steps in %.3f s" % (args.steps, wall), file=sys.stderr, flush=True)
 
+    # The same executes again, outside the timed steps, with every
+    # destination byte poison-filled (0xFF) on the stream before each rep
+    # and outside its events: no rep can find the previous one's output in
+    # a cache.
+    poisoned = {}
+    if do_copy:
+        poisoned["bf16"] = time_plan(torch, binding, p_copy, src_ptrs, ptr_copy, stream, reps=5,
+                                     poison=list(d_copy.values()))
+    if do_mx:
+        poisoned["mxfp8"] = time_plan(torch, binding, p_mx, src_ptrs, ptr_mx, stream, reps=5,
+                                      poison=list(d_mx.values()))
+
     t_copy = [e[0].elapsed_time(e[1]) for e in evs] if do_copy else []
     t_mx = [e[2].elapsed_time(e[3]) for e in evs] if do_mx else []
     bytes_copy = i_copy["bytes_read"] + i_copy["bytes_written"]
@@ -542,8 +626,8 @@ def main():
         if c.get("kernel_source_sha256_16") == kernel_hash() and c.get("kernel") == dominant:
             traffic = c.get("traffic_bytes_per_launch")
 
-    # The MXFP8 kernel's own roofline (its plan takes two launches per
-    # execute; achieved is per execute, from the same HIP events).
+    # The MXFP8 kernel's own roofline (achieved per execute, from the same
+    # HIP events; the plan takes rs_plan_info.n_launches launches).
     roof_mx = None
     if do_mx:
         ach_mx = bytes_mx / (statistics.mean(t_mx) * 1e-3) / 1e9
@@ -576,9 +660,11 @@ def main():
                                "plus the BF16->MXFP8 install variant",
                    "variant": args.variant, "step_bytes": step_bytes},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),
-        "copy_ceiling_GBps": round(ceiling, 1) if ceiling else None,
+        "copy_ceiling_GBps": ceiling,
+        "copy_ceiling": ceil_info,
         "bf16": stats(t_copy, bytes_copy),
         "mxfp8": stats(t_mx, bytes_mx),
+        "poison_filled_ms_median": {k: round(v, 4) for k, v in poisoned.items()},
         "plan_us": plan_us,
         "execute_host_us": {k: {"first_call_with_upload": first_call_us[k],
                                 "p50": round(statistics.median(v), 1)}
@@ -591,7 +677,7 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
         "roofline_mxfp8": roof_mx,
-        "device": torch.cuda.get_device_name(0),
+        "device": device_info(torch),
     }
     del src, d_copy, d_mx
     torch.cuda.empty_cache()
@@ -599,9 +685,8 @@ def main():
         print("secondary workloads ...", file=sys.stderr, flush=True)
         out["secondary"] = secondary(torch, binding, stream)
         torch.cuda.empty_cache()
-    if not args.no_cpu_baseline:
-        print("cpu baseline ...", file=sys.stderr, flush=True)
-        out["cpu_baseline"], out["cpu_baseline_threads"] = cpu_baseline()
+    if cpu is not None:
+        out["cpu_baseline"], out["cpu_baseline_single_process"] = cpu
     print(json.dumps(out), flush=True)
     return 0
 

@@ -236,8 +236,20 @@ rs_status reshard_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int
  * execution surface on the stream like any HIP error. */
 rs_status reshard_execute(const rs_plan* plan, void* const* src_ptrs, void* const* dst_ptrs,
                           void* stream);
+/* Partial failure: a plan whose pointers exceed one launch's pointer pool
+ * runs as several launches (rs_plan_info.n_launches).  All argument checks
+ * come before the first launch; if the HIP runtime then refuses launch k,
+ * launches 0..k-1 stay enqueued and write their regions, the call returns
+ * RS_ERR_HIP naming launch k, and the destinations are only partly
+ * installed (execute again once the cause is fixed). */
 
-/* Fill *info.  Errors: RS_ERR_INVALID for NULL arguments. */
+/* Fill *info: the plan's pointer counts, region and work-unit counts per
+ * kernel, launches per execute, algorithmic bytes and planning time.  The
+ * per-receiver descriptor count and the bytes a refit moves are the figures
+ * the ModelExpress PR reports for its plans ("feat(refit): add ModelExpress
+ * Megatron-to-vLLM reshard path - #3632", "Performance measured on real model
+ * tensors": descriptors per receiver, wire bytes against engine bytes).
+ * Errors: RS_ERR_INVALID for NULL arguments. */
 rs_status reshard_plan_info(const rs_plan* plan, rs_plan_info* info);
 
 /* Copy region `index` (0 <= index < n_regions) into *out.
@@ -250,12 +262,19 @@ rs_status reshard_plan_region(const rs_plan* plan, uint64_t index, rs_region* ou
 rs_status reshard_shard_box(const rs_tensor_desc* desc, int64_t slot, int64_t* offsets,
                             int64_t* lengths);
 
-/* Free a plan and its device tables.  Every stream that executed it must
- * have been synchronised.  NULL is ignored. */
+/* Free a plan and its device tables.  A plan is built once and reused for
+ * every refit of the same layouts: the descriptor caching that the
+ * ModelExpress PR lists among its transport changes ("feat(refit): add
+ * ModelExpress Megatron-to-vLLM reshard path - #3632", "Performance measured
+ * on real model tensors"); destroy ends that reuse.  Every stream that
+ * executed the plan must have been synchronised.  NULL is ignored. */
 void reshard_plan_destroy(rs_plan* plan);
 
-/* Message of the last failing call on this thread ("" if none).  The string
- * stays valid until the next call on this thread. */
+/* Message of the last failing call on this thread ("" if none): one line
+ * per violation found, all of them, as the validation of "NCCL Reshard Refit
+ * (Experimental)", "Enabling It" reports every problem of a configuration in
+ * one error rather than the first only.  The string stays valid until the
+ * next call on this thread. */
 const char* reshard_last_error(void);
 
 #ifdef __cplusplus

@@ -126,23 +126,34 @@ def assemble(src_desc, esize, src_bufs):
     return G
 
 
-def reshard(src_desc, dst_desc, src_bufs, dst_bufs):
+def reshard(src_desc, dst_desc, src_bufs, dst_bufs, map_fn=None):
     """Write every destination shard through its view(s) into dst_bufs.
 
     dst_bufs[k] = {"buf": uint8 array, "view": ...} and, when
     dst_desc["quant"] == "mxfp8", also {"scale_buf": ..., "scale_view": ...}.
     The images are modified in place; bytes outside the views are left as
     they were given.
+
+    map_fn (default: the built-in map) applies the per-destination step to
+    every destination slot; a thread pool's map runs slots concurrently
+    (each slot writes only its own views).
     """
     if list(src_desc["shape"]) != list(dst_desc["shape"]):
         raise ValueError("global shapes differ")
     esize = ELEM_BYTES[src_desc["dtype"]]
     quant = dst_desc.get("quant")
     G = assemble(src_desc, esize, src_bufs)
-    for k, box in enumerate(layout.slot_boxes(dst_desc)):
-        ln = box[1]
-        if layout.box_volume(box) == 0:
-            continue
+
+    def one(kb):
+        _install(G, esize, quant, src_desc, dst_desc, kb[0], kb[1], dst_bufs)
+    list((map_fn or map)(one, enumerate(layout.slot_boxes(dst_desc))))
+
+
+def _install(G, esize, quant, src_desc, dst_desc, k, box, dst_bufs):
+    """Destination slot k: its box of G, quantised if asked, written through
+    its view(s)."""
+    ln = box[1]
+    if layout.box_volume(box) > 0:
         V = np.ascontiguousarray(G[box_slices(box)])
         if quant is None:
             if ELEM_BYTES[dst_desc["dtype"]] != esize:

@@ -1,14 +1,21 @@
 """GPU parity at the full layer sizes, in the launch configuration the
 benchmark times (default plan options, one execute on the current stream).
 
-The host oracle cannot assemble 7.5 GB tensors quickly, so here it checks
-sampled outputs one by one: for each sampled destination element (or MXFP8
-block) it finds, with its own box arithmetic, which source element(s) hold
-the value, reads them from the device, and computes the expected bytes.
-Properties checked over every byte: no poison left in any destination
-(poison 0xFF bytes form a bf16 NaN that N(0, 0.02) never produces, and that
-the MXFP8 encoder never emits for finite input), and the sum of all installed
-bf16 bit patterns equals the sum over the sources.
+Checks, per layer:
+* three whole destination slots of every tensor against the oracle, every
+  element (and for MXFP8 every scale byte): the oracle assembles the full
+  tensor on the host from the device's source shards and slices, and
+  quantises, those slots;
+* every destination slot, for the bf16 copies, against torch slicing of the
+  seeded global tensor regenerated on the device (position by position);
+* sampled destination elements (MXFP8: blocks) located one by one with the
+  oracle's own box arithmetic, and no poison byte left anywhere (0xFF bytes
+  form a bf16 NaN that N(0, 0.02) never produces and that the MXFP8 encoder
+  never emits for finite input);
+* the A -> B -> A round trip, every source byte.
+A 16-expert slice of the DeepSeek-V3-shaped layer (the same hidden and
+intermediate sizes, meshes and unit shapes) is compared with the oracle
+element by element in full.
 """
 
 import numpy as np
@@ -45,7 +52,8 @@ def dense_strides(lengths):
 def build(wl):
     """Device sources (cut from seeded device-generated globals with the
     oracle's boxes; one buffer per expert for split sources) and poisoned
-    destinations."""
+    destination buffers (every destination of these layers is a view into a
+    named buffer)."""
     dev = torch.device("cuda")
     src = []
     for t in wl["tensors"]:
@@ -64,44 +72,104 @@ def build(wl):
     for key, b in wl["buffers"].items():
         named[key] = torch.full((b["elems"] * synth.ELEM_BYTES[b["dtype"]],), POISON,
                                 dtype=torch.uint8, device=dev)
-    dst_ptrs, dst_bufs = [], []
+    dst_ptrs = []
     for t in wl["tensors"]:
         d = t["dst"]
-        boxes = olayout.slot_boxes(helpers.odesc(t, "dst"))
-        es = 1 if d.get("quant") == "mxfp8" else 2
-        el = []
-        for k, box in enumerate(boxes):
-            if d["slots"] is None:
-                el.append(torch.full((olayout.box_volume(box) * es,), POISON, dtype=torch.uint8,
-                                     device=dev))
-            else:
-                el.append(named[d["slots"][k]["buf"]])
-        dst_bufs.append(el)
-        dst_ptrs += [b.data_ptr() for b in el]
+        assert d["slots"] is not None
+        dst_ptrs += [named[e["buf"]].data_ptr() for e in d["slots"]]
         if d.get("quant") == "mxfp8":
-            sc = [named[d["scale_slots"][k]["buf"]] for k in range(len(boxes))]
-            dst_bufs.append(sc)
-            dst_ptrs += [b.data_ptr() for b in sc]
-    return src, named, dst_bufs, dst_ptrs
+            dst_ptrs += [named[e["buf"]].data_ptr() for e in d["scale_slots"]]
+    return src, named, dst_ptrs
 
 
 def run(wl):
-    src, named, dst_bufs, dst_ptrs = build(wl)
+    src, named, dst_ptrs = build(wl)
     plan = lh.plan_workload(wl)
     src_ptrs = [p.data_ptr() for shards in src for s in shards
                 for p in (s if isinstance(s, list) else [s])]
     binding.reshard_execute(plan, src_ptrs, dst_ptrs, torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
-    return plan, src, named, dst_bufs
+    return plan, src, named
 
 
-def chunked_sum16(t):
-    tot = 0
-    flat = t.view(torch.int16).view(-1)
-    step = 1 << 27
-    for i in range(0, flat.numel(), step):
-        tot += int((flat[i:i + step].to(torch.int32) & 0xFFFF).sum(dtype=torch.int64))
-    return tot
+WORKLOADS = {
+    "moe_128e": synth.moe_128e,
+    "moe_dsv3": synth.moe_dsv3,
+    "moe_dsv3_per_expert_src": lambda: synth.moe_dsv3(src_split=True),
+    "moe_dsv3_mxfp8": lambda: synth.moe_dsv3(quant="mxfp8"),
+}
+_RUNS = {}
+
+
+def layer_run(key):
+    """The layer relaid out once; later tests of the same layer reuse its
+    buffers (the previous layer's are released first)."""
+    if key not in _RUNS:
+        _RUNS.clear()
+        torch.cuda.empty_cache()
+        wl = WORKLOADS[key]()
+        gh.log("full size %s" % wl["name"])
+        plan, src, named = run(wl)
+        _RUNS[key] = (wl, src, named)
+    return _RUNS[key]
+
+
+def slot_tensor(named, entry, lengths, elem):
+    """The destination slot seen through its view (int16 elements for bf16,
+    bytes for MXFP8 codes and scales)."""
+    buf = named[entry["buf"]]
+    flat = buf.view(torch.int16) if elem == "bf16" else buf
+    base, strides = entry["view"]
+    return torch.as_strided(flat, size=list(lengths), stride=list(strides), storage_offset=base)
+
+
+def check_every_slot_on_device(wl, named):
+    """Every destination slot equals torch slicing of the seeded global
+    tensor, regenerated on the device, at the oracle's box."""
+    for t in wl["tensors"]:
+        G = synth.device_values(t, "cuda").view(torch.int16)
+        for k, (off, ln) in enumerate(olayout.slot_boxes(helpers.odesc(t, "dst"))):
+            want = G[tuple(slice(o, o + n) for o, n in zip(off, ln))]
+            got = slot_tensor(named, t["dst"]["slots"][k], ln, "bf16")
+            assert torch.equal(got, want), (wl["name"], t["name"], k)
+        del G
+        torch.cuda.empty_cache()
+
+
+def host_source_entries(shards):
+    """Oracle source entries (byte images) of one tensor's device shards."""
+    out = []
+    for s in shards:
+        if isinstance(s, list):
+            out.append({"parts": [p.cpu().numpy().view(np.uint8).reshape(-1) for p in s]})
+        else:
+            out.append({"buf": s.cpu().numpy().view(np.uint8).reshape(-1)})
+    return out
+
+
+def check_slots_against_oracle(wl, ti, src, named, slots):
+    """Whole destination slots of tensor ti against the oracle: the full
+    tensor assembled on the host from the device's source shards, each slot's
+    box sliced (and quantised for MXFP8), compared with every element (and
+    scale byte) the device installed."""
+    t = wl["tensors"][ti]
+    d = t["dst"]
+    G = ogolden.assemble(helpers.src_desc_for(t), 2, host_source_entries(src[ti]))
+    boxes = olayout.slot_boxes(helpers.odesc(t, "dst"))
+    for k in slots:
+        ln = boxes[k][1]
+        V = np.ascontiguousarray(G[ogolden.box_slices(boxes[k])])
+        if d.get("quant") == "mxfp8":
+            codes, scales = omx.quantize(V)
+            got = slot_tensor(named, d["slots"][k], ln, "u8").cpu().numpy()
+            np.testing.assert_array_equal(got, codes, err_msg="%s slot %d codes" % (t["name"], k))
+            sln = list(ln[:-1]) + [-(-ln[-1] // omx.BLOCK)]
+            got = slot_tensor(named, d["scale_slots"][k], sln, "u8").cpu().numpy()
+            np.testing.assert_array_equal(got, scales, err_msg="%s slot %d scales" % (t["name"], k))
+        else:
+            got = slot_tensor(named, d["slots"][k], ln, "bf16").cpu().numpy().view(np.uint16)
+            np.testing.assert_array_equal(got, V, err_msg="%s slot %d" % (t["name"], k))
+    del G
 
 
 def no_poison(buf, dtype):
@@ -168,42 +236,34 @@ def sampled_mx_check(wl, src, named, nblocks, rng):
             assert int(sbuf[so]) == int(scales[0, 0]), (t["name"], k, row, b)
 
 
-@pytest.mark.parametrize("which", ["moe_128e", "moe_dsv3", "moe_dsv3_per_expert_src"])
-def test_full_size_copy(which):
-    wl = synth.moe_dsv3(src_split=True) if which == "moe_dsv3_per_expert_src" else \
-        getattr(synth, which)()
-    gh.log("full size %s" % wl["name"])
-    plan, src, named, dst_bufs = run(wl)
+def three_slots(wl):
+    n = len(olayout.slot_boxes(helpers.odesc(wl["tensors"][0], "dst")))
+    return [0, n // 2 + 5, n - 1]
+
+
+@pytest.mark.parametrize("which", ["moe_128e", "moe_dsv3"])
+def test_full_size_copy_every_slot(which):
+    wl, src, named = layer_run(which)
     for key, buf in named.items():
         assert no_poison(buf, wl["buffers"][key]["dtype"]), key
-    src_sum = sum(chunked_sum16(p) for shards in src for s in shards
-                  for p in (s if isinstance(s, list) else [s]))
-    dst_sum = sum(chunked_sum16(b) for b in named.values())
-    assert src_sum == dst_sum
+    check_every_slot_on_device(wl, named)
     sampled_copy_check(wl, src, named, 3000, np.random.default_rng(1))
-    del src, named, dst_bufs
-    torch.cuda.empty_cache()
 
 
-def test_full_size_mxfp8():
-    wl = synth.moe_dsv3(quant="mxfp8")
-    gh.log("full size %s" % wl["name"])
-    plan, src, named, dst_bufs = run(wl)
-    for key, buf in named.items():
-        assert no_poison(buf, wl["buffers"][key]["dtype"]), key
-    sampled_mx_check(wl, src, named, 600, np.random.default_rng(2))
-    del src, named, dst_bufs
-    torch.cuda.empty_cache()
+@pytest.mark.parametrize("ti", [0, 1, 2], ids=["gate", "up", "down"])
+@pytest.mark.parametrize("which", ["moe_128e", "moe_dsv3"])
+def test_full_size_copy_slots_against_oracle(which, ti):
+    wl, src, named = layer_run(which)
+    check_slots_against_oracle(wl, ti, src, named, three_slots(wl))
 
 
-def test_full_size_round_trip():
-    """A -> B -> A on the DeepSeek-V3-shaped layer: EP16 sources to the
-    fused EP8 x TP8 destinations and back (the reverse plan reads through the
-    fused views); every source byte must come back (checked on the device,
-    all 22.5 GB)."""
-    wl = synth.moe_dsv3()
+@pytest.mark.parametrize("which", ["moe_128e", "moe_dsv3"])
+def test_full_size_round_trip(which):
+    """A -> B -> A: the sources to the fused EP x TP destinations and back
+    (the reverse plan reads through the fused views); every source byte
+    must come back (checked on the device)."""
+    wl, src, named = layer_run(which)
     gh.log("full size round trip %s" % wl["name"])
-    plan, src, named, dst_bufs = run(wl)
     back = synth.reverse(wl)
     bplan = lh.plan_workload(back)
     b_src_ptrs = []
@@ -216,8 +276,51 @@ def test_full_size_round_trip():
     for shards, outs in zip(src, out):
         for a, b in zip(shards, outs):
             assert torch.equal(a, b)
-    del src, named, dst_bufs, out
+    del out
+
+
+def test_full_size_copy_per_expert_sources():
+    wl, src, named = layer_run("moe_dsv3_per_expert_src")
+    for key, buf in named.items():
+        assert no_poison(buf, wl["buffers"][key]["dtype"]), key
+    check_every_slot_on_device(wl, named)
+    sampled_copy_check(wl, src, named, 3000, np.random.default_rng(1))
+    check_slots_against_oracle(wl, 2, src, named, [0, 63])
+
+
+def test_full_size_mxfp8_sampled():
+    wl, src, named = layer_run("moe_dsv3_mxfp8")
+    for key, buf in named.items():
+        assert no_poison(buf, wl["buffers"][key]["dtype"]), key
+    sampled_mx_check(wl, src, named, 600, np.random.default_rng(2))
+
+
+@pytest.mark.parametrize("ti", [0, 1, 2], ids=["gate", "up", "down"])
+def test_full_size_mxfp8_slots_against_oracle(ti):
+    wl, src, named = layer_run("moe_dsv3_mxfp8")
+    check_slots_against_oracle(wl, ti, src, named, three_slots(wl))
+
+
+def test_release_layer_buffers():
+    _RUNS.clear()
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("quant,ti", [(None, None), ("mxfp8", 0), ("mxfp8", 1), ("mxfp8", 2)],
+                         ids=["bf16", "mxfp8_gate", "mxfp8_up", "mxfp8_down"])
+def test_dsv3_sixteen_expert_slice_every_byte(quant, ti):
+    """16 experts of the DeepSeek-V3-shaped layer (hidden 7168, intermediate
+    2048, EP16 -> EP8 x TP8, fused w13): every destination pointer has the
+    full layer's shapes (7,168-element gate/up rows, 256-element down rows,
+    two source shards per destination), compared byte for byte with the
+    oracle, poison outside the views and guards included."""
+    wl = synth.moe_experts(16, 7168, 2048, 16, 8, 8, seed=5, quant=quant)
+    if ti is not None:
+        wl = dict(wl, tensors=[wl["tensors"][ti]])
+    gh.log("16-expert slice %s %s" % (wl["name"], [t["name"] for t in wl["tensors"]]))
+    globals_ = [synth.device_values(t, "cuda").view(torch.int16).cpu().numpy().view(np.uint16)
+                for t in wl["tensors"]]
+    gh.check_against_oracle(wl, globals_=globals_)
 
 
 def test_rows_past_2_31():

@@ -217,7 +217,8 @@ def test_moe_experts_mxfp8_misaligned(shape, shifts):
 
 
 @pytest.mark.parametrize("shape,inner", [([6, 40, 64], 64), ([3, 30, 200], 200), ([2, 8, 8200], 8200),
-                                         ([5, 3, 33], 33), ([7, 11, 8], 8), ([4, 9, 1000], 1000)])
+                                         ([5, 3, 33], 33), ([7, 11, 8], 8), ([4, 9, 1000], 1000),
+                                         ([2, 8, 7168], 7168), ([2, 8, 4104], 4104), ([3, 5, 2050], 2050)])
 @pytest.mark.parametrize("mesh,pl", [([2, 2], [0, -1]), ([4], [-1]), ([2, 3], [-1, 1])])
 def test_mxfp8_fanout_and_row_lengths(shape, inner, mesh, pl):
     """Replicated MXFP8 destinations (one read, up to four replicas written)
@@ -226,6 +227,22 @@ def test_mxfp8_fanout_and_row_lengths(shape, inner, mesh, pl):
     t = {"name": "w", "shape": shape, "dtype": "bf16", "src": synth.side([2], [0]),
          "dst": synth.side(mesh, pl, quant="mxfp8"), "values": {"kind": "normal", "std": 0.02, "seed": 21}}
     gh.check_against_oracle({"name": "mx_fan", "buffers": {}, "tensors": [t]})
+
+
+@pytest.mark.parametrize("as_source", [False, True])
+def test_permuted_rank_grid_fixture(as_source):
+    """The hand-written permuted rank grid (tests/golden/permuted_grid_2x2.txt)
+    as destination and as source."""
+    import test_oracle_layout as tl
+    wl = tl.grid_workload(as_source)
+    gh.check_against_oracle(wl)
+    if not as_source:
+        _, slots = tl.read_grid_fixture()
+        G, sources, named, per = helpers.golden_workload(wl)
+        _, _, dst_dev = gh.device_run(wl, sources, per)
+        for k, (_, ln, block) in slots.items():
+            got = dst_dev[k][1].host().view(np.uint32).reshape(ln)
+            np.testing.assert_array_equal(got, block.astype(np.uint32))
 
 
 @pytest.mark.parametrize("dst_mesh,dst_pl", [([2], [1]), ([2, 2], [0, -1]), ([3], [2])])

@@ -283,3 +283,58 @@ def test_parts_equal_stacked_buffer():
         e, t = divmod(k, 2)
         want = G[3 * e:3 * e + 3, :, 2 * t:2 * t + 2]
         np.testing.assert_array_equal(outs[0][k].view(np.uint32).reshape(3, 5, 2), want)
+
+
+def read_grid_fixture():
+    """The hand-written permuted rank grid (tests/golden/permuted_grid_2x2.txt)."""
+    with open(os.path.join(HERE, "golden", "permuted_grid_2x2.txt")) as f:
+        lines = [l.split() for l in f if l.strip() and not l.startswith("#")]
+    head = {l[0]: [int(x) for x in l[1:]] for l in lines[:4]}
+    slots = {}
+    i = 4
+    while i < len(lines):
+        l = lines[i]
+        k = int(l[1])
+        off = [int(l[3]), int(l[4])]
+        ln = [int(l[6]), int(l[7])]
+        block = np.array([[int(x) for x in lines[i + 1 + r]] for r in range(ln[0])])
+        slots[k] = (off, ln, block)
+        i += 1 + ln[0]
+    return head, slots
+
+
+def grid_workload(as_source=False):
+    head, _ = read_grid_fixture()
+    grid = synth.side(head["mesh"], head["placements"], slot_of_coord=head["grid"])
+    whole = synth.side([1], [-1])
+    t = {"name": "g", "shape": head["shape"], "dtype": "i32",
+         "src": grid if as_source else whole, "dst": whole if as_source else grid,
+         "values": {"kind": "index"}}
+    return {"name": "permuted_grid_%s" % ("src" if as_source else "dst"), "buffers": {},
+            "tensors": [t]}
+
+
+def test_permuted_rank_grid_boxes():
+    """Slot s of a layout whose mesh tensor holds rank s at coordinate c owns
+    the box of coordinate c (the fixture fixes the direction of the grid)."""
+    head, slots = read_grid_fixture()
+    desc = {"shape": head["shape"], "mesh": head["mesh"], "placements": head["placements"],
+            "slot_of_coord": head["grid"]}
+    boxes = layout.slot_boxes(desc)
+    for k, (off, ln, _) in slots.items():
+        assert boxes[k] == (off, ln), k
+
+
+def test_permuted_rank_grid_golden():
+    """Replicate -> the permuted grid: each slot's buffer holds its block."""
+    _, slots = read_grid_fixture()
+    wl = grid_workload()
+    G, _, _, per = helpers.golden_workload(wl)
+    for k, (_, ln, block) in slots.items():
+        got = per[0][k]["buf"].view(np.uint32).reshape(ln)
+        np.testing.assert_array_equal(got, block.astype(np.uint32))
+    # and back: the permuted grid as the source reassembles the index tensor
+    wl = grid_workload(as_source=True)
+    G, _, _, per = helpers.golden_workload(wl)
+    want = np.arange(24, dtype=np.uint32)
+    np.testing.assert_array_equal(per[0][0]["buf"].view(np.uint32), want)

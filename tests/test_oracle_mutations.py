@@ -98,3 +98,17 @@ def test_lost_sign_of_zero_is_caught(monkeypatch):
     zeros = [b for b in tm.read_blocks() if b["name"] == "zeros"][0]
     assert _fails(tm.test_hand_computed_blocks, zeros)
     assert _fails(tm.test_encode_vs_torch_float8, 0)
+
+
+def test_inverted_rank_grid_is_caught(monkeypatch):
+    """Reading the grid the wrong way round (entry c as the coordinate of
+    slot c, instead of the slot at coordinate c)."""
+    def inverted(desc):
+        coords = layout.mesh_coords(desc["mesh"])
+        soc = desc.get("slot_of_coord")
+        if soc is None:
+            return coords
+        return [coords[soc[s]] for s in range(len(coords))]
+    monkeypatch.setattr(layout, "slot_coords", inverted)
+    assert _fails(tl.test_permuted_rank_grid_boxes)
+    assert _fails(tl.test_permuted_rank_grid_golden)

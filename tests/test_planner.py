@@ -434,3 +434,16 @@ def test_interpreted_spread_layouts(name, unit_bytes):
 def test_interpreted_spread_random_layouts(seed):
     import spread_layouts as sl
     run_interpreted(sl.random_case(seed), unit_bytes=(8192, 16384, 32768)[seed % 3])
+
+
+def test_permuted_rank_grid_fixture():
+    """The library's shard boxes and interpreted plans on the hand-written
+    permuted rank grid (tests/golden/permuted_grid_2x2.txt), both ways."""
+    import test_oracle_layout as tl
+    head, slots = tl.read_grid_fixture()
+    sp = {"shape": head["shape"], "dtype": "i32", "mesh": head["mesh"],
+          "placements": head["placements"], "slot_of_coord": head["grid"]}
+    for k, (off, ln, _) in slots.items():
+        assert binding.reshard_shard_box(sp, k) == (off, ln)
+    for as_source in (False, True):
+        run_interpreted(tl.grid_workload(as_source))
