@@ -67,6 +67,11 @@ def parse():
     ap.add_argument("--plan-reps", type=int, default=1000, help="planner calls timed for plan_us")
     ap.add_argument("--ceiling-bytes", type=int, default=8 << 30,
                     help="size of the plain device copy timed as copy_ceiling_GBps")
+    ap.add_argument("--ceiling-torch-only", action="store_true",
+                    help="time only torch's copy for the ceiling (no launch of this library's kernels "
+                         "outside the workload, e.g. for counter runs)")
+    ap.add_argument("--poison-reps", type=int, default=5,
+                    help="poison-filled reps per variant after the timed steps (0: none)")
     ap.add_argument("--procs", type=int, default=1,
                     help="run the bench in this many fresh processes and report their median")
     return ap.parse_args()
@@ -179,7 +184,7 @@ def device_destinations(torch, binding, wl):
     return named, ptrs
 
 
-def copy_ceiling(torch, binding, nbytes, stream):
+def copy_ceiling(torch, binding, nbytes, stream, library=True):
     """Plain contiguous device-to-device copies of nbytes, GB/s of read +
     write: torch's copy_ (best of 6) and this library's own copy of the
     same bytes as one region (identity layout, median of 10).  The ceiling
@@ -198,22 +203,36 @@ def copy_ceiling(torch, binding, nbytes, stream):
             e1.record(stream)
             e1.synchronize()
             best = max(best, 2 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
-    t = {"name": "flat", "shape": [nbytes], "dtype": "u8", "src": synth.side([1], [-1]),
-         "dst": synth.side([1], [-1]), "values": {"kind": "index"}}
-    plan = binding.reshard_plan([spec(t, "src")], [spec(t, "dst")])
-    ms = time_plan(torch, binding, plan, [a.data_ptr()], [b.data_ptr()], stream)
-    plan.destroy()
-    lib = 2 * nbytes / (ms * 1e-3) / 1e9
+    lib = 0.0
+    if library:
+        t = {"name": "flat", "shape": [nbytes], "dtype": "u8", "src": synth.side([1], [-1]),
+             "dst": synth.side([1], [-1]), "values": {"kind": "index"}}
+        plan = binding.reshard_plan([spec(t, "src")], [spec(t, "dst")])
+        ms = time_plan(torch, binding, plan, [a.data_ptr()], [b.data_ptr()], stream)
+        plan.destroy()
+        lib = 2 * nbytes / (ms * 1e-3) / 1e9
     del a, b
     return {"GBps": round(max(best, lib), 1), "torch_copy_GBps": round(best, 1),
             "library_copy_GBps": round(lib, 1), "bytes_each_way": nbytes}
 
 
+_SWEEP = []
+
+
+def cache_sweep(torch):
+    """Reads 1 GiB (four times the 256 MB Infinity Cache): afterwards no cache
+    holds a destination line, clean or dirty, so a timed rep neither finds
+    its output cached nor pays for writing back a poison fill."""
+    if not _SWEEP:
+        _SWEEP.append(torch.ones(1 << 28, dtype=torch.float32, device="cuda"))
+    _SWEEP[0].sum()
+
+
 def time_plan(torch, binding, plan, src_ptrs, dst_ptrs, stream, reps=10, poison=()):
     """Median event-timed execute of a plan on `stream` (ms).  The buffers
     in `poison` are filled with 0xFF on the stream before every timed rep,
-    outside the timed events, so no rep finds the previous rep's output in a
-    cache."""
+    and the caches swept, outside the timed events, so no rep finds the
+    previous rep's output in a cache."""
     for _ in range(2):
         binding.reshard_execute(plan, src_ptrs, dst_ptrs, stream.cuda_stream)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -223,6 +242,7 @@ def time_plan(torch, binding, plan, src_ptrs, dst_ptrs, stream, reps=10, poison=
             with torch.cuda.stream(stream):
                 for t in poison:
                     t.fill_(0xFF)
+                cache_sweep(torch)
         a.record(stream)
         binding.reshard_execute(plan, src_ptrs, dst_ptrs, stream.cuda_stream)
         b.record(stream)
@@ -527,7 +547,8 @@ def main():
           file=sys.stderr, flush=True)
 
     stream = torch.cuda.Stream()
-    ceil_info = copy_ceiling(torch, binding, args.ceiling_bytes, stream) if args.ceiling_bytes else None
+    ceil_info = copy_ceiling(torch, binding, args.ceiling_bytes, stream,
+                             library=not args.ceiling_torch_only) if args.ceiling_bytes else None
     ceiling = ceil_info["GBps"] if ceil_info else None
     print("copy ceiling %.1f GB/s" % (ceiling or 0), file=sys.stderr, flush=True)
 
@@ -589,12 +610,12 @@ def main():
     # and outside its events: no rep can find the previous one's output in
     # a cache.
     poisoned = {}
-    if do_copy:
-        poisoned["bf16"] = time_plan(torch, binding, p_copy, src_ptrs, ptr_copy, stream, reps=5,
-                                     poison=list(d_copy.values()))
-    if do_mx:
-        poisoned["mxfp8"] = time_plan(torch, binding, p_mx, src_ptrs, ptr_mx, stream, reps=5,
-                                      poison=list(d_mx.values()))
+    if do_copy and args.poison_reps > 0:
+        poisoned["bf16"] = time_plan(torch, binding, p_copy, src_ptrs, ptr_copy, stream,
+                                     reps=args.poison_reps, poison=list(d_copy.values()))
+    if do_mx and args.poison_reps > 0:
+        poisoned["mxfp8"] = time_plan(torch, binding, p_mx, src_ptrs, ptr_mx, stream,
+                                      reps=args.poison_reps, poison=list(d_mx.values()))
 
     t_copy = [e[0].elapsed_time(e[1]) for e in evs] if do_copy else []
     t_mx = [e[2].elapsed_time(e[3]) for e in evs] if do_mx else []

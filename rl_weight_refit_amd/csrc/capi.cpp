@@ -196,7 +196,8 @@ rs_status execute(const rs_plan* plan, void* const* src_ptrs, void* const* dst_p
   char* base = nullptr;
   const rs_status ts = plan_tables(plan, dev, &base);
   if (ts != RS_OK) return ts;
-  for (const rs::Launch& L : d.launches) {
+  for (size_t li = 0; li < d.launches.size(); ++li) {
+    const rs::Launch& L = d.launches[li];
     rs::LaunchArgs args;
     std::memset(&args, 0, sizeof(args));
     args.regions = base + L.regions_off;
@@ -208,8 +209,12 @@ rs_status execute(const rs_plan* plan, void* const* src_ptrs, void* const* dst_p
       args.ptr[k] = (e & rs::kDstBit) ? dst_ptrs[e & ~rs::kDstBit] : src_ptrs[e];
     }
     he = rs::launch(L.bucket, L.n_units, args, static_cast<hipStream_t>(stream), dev);
-    if (he != hipSuccess)
-      return fail(RS_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(he) + "\n");
+    if (he != hipSuccess) {
+      std::ostringstream m;
+      m << "kernel launch " << li << " of " << d.launches.size() << ": " << hipGetErrorString(he)
+        << (li ? " (the earlier launches stay enqueued)" : "") << "\n";
+      return fail(RS_ERR_HIP, m.str());
+    }
   }
   return RS_OK;
 }

@@ -37,6 +37,9 @@
 //        code bytes per lane; the block scales are gathered in LDS and
 //        written by consecutive lanes at the end.  Units are taken in the
 //        same XCD turns as the bulk kernel's (6 % faster than dispatch order).
+//        The region's fields and pointers are read once at kernel entry, so
+//        no table read (a vector load whose wait would also wait for the
+//        stores issued before it) sits between a unit's stores.
 //
 // Fan-out: a region may name up to 16 destination replicas; the data is read
 // once and stored to each (the one-GPU analogue of serving every replica from
@@ -131,6 +134,28 @@ __device__ __forceinline__ uint32_t unit_of_block(uint32_t b, uint32_t n, uint32
   const uint32_t full = n / (8u * chunk) * (8u * chunk);
   if (b >= full) return b;
   return ((i / chunk) * 8u + x) * chunk + i % chunk;
+}
+
+// Pool indices of a region: the 16-bit fields from src_ptr on (source,
+// replica count, destinations, then for MXFP8 regions the scale
+// destinations), read as the aligned 32-bit words that hold them, so a
+// workgroup-uniform read is a scalar load.  A 16-bit read is a vector load,
+// and its wait (vmcnt counts loads and stores together on CDNA) would also
+// wait for every store the wave has issued.
+template <class Reg>
+__device__ __forceinline__ uint32_t pool_field(const Reg* R, uint32_t i) {
+  uint32_t w;
+  __builtin_memcpy(&w, reinterpret_cast<const char*>(&R->src_ptr) + 4u * (i >> 1), 4);
+  return (w >> ((i & 1u) << 4)) & 0xFFFFu;
+}
+template <class Reg>
+__device__ __forceinline__ uint32_t src_pool(const Reg* R) { return pool_field(R, 0); }
+template <class Reg>
+__device__ __forceinline__ uint32_t n_dst_of(const Reg* R) { return pool_field(R, 1); }
+template <class Reg>
+__device__ __forceinline__ uint32_t dst_pool(const Reg* R, uint32_t j) { return pool_field(R, 2 + j); }
+__device__ __forceinline__ uint32_t sc_pool(const MxRegion* R, uint32_t j) {
+  return pool_field(R, 2 + kMaxFan + j);
 }
 
 // Region of a work unit: the chunk table brackets it, a short binary search
@@ -252,7 +277,7 @@ __device__ __forceinline__ void bulk_short_rows(const LaunchArgs& a, const CopyR
       }
     }
     for (uint32_t j = 0; j < nd; ++j) {
-      char* d = kFan1 ? dp0 : static_cast<char*>(a.ptr[R->dst_ptr[j]]) + dst_off;
+      char* d = kFan1 ? dp0 : static_cast<char*>(a.ptr[dst_pool(R, j)]) + dst_off;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint32_t r = rb + u * step;
@@ -295,7 +320,7 @@ __device__ __forceinline__ void bulk_short_flat(const LaunchArgs& a, const CopyR
       if (f < nvec) x[k] = ld16(sp + uint64_t(r) * s0 + 16ull * v);
     }
     for (uint32_t j = 0; j < nd; ++j) {
-      char* d = static_cast<char*>(a.ptr[R->dst_ptr[kFan1 ? 0 : j]]) + dst_off;
+      char* d = static_cast<char*>(a.ptr[dst_pool(R, kFan1 ? 0 : j)]) + dst_off;
 #pragma unroll
       for (int k = 0; k < U; ++k)
         if (f0 + k * kThreads + tid < nvec) st16(d + o[k], x[k]);
@@ -338,7 +363,7 @@ __device__ __forceinline__ void bulk_spread_flat(const LaunchArgs& a, const Copy
       if (t < nvec) x[k] = ld16(sp + r * s0 + 16ull * v);
     }
     for (uint32_t jd = 0; jd < nd; ++jd) {
-      char* d = static_cast<char*>(a.ptr[R->dst_ptr[kFan1 ? 0 : jd]]) + dst_off;
+      char* d = static_cast<char*>(a.ptr[dst_pool(R, kFan1 ? 0 : jd)]) + dst_off;
 #pragma unroll
       for (int k = 0; k < U; ++k)
         if (t0 + k * kThreads + tid < nvec) st16(d + o[k], x[k]);
@@ -402,7 +427,7 @@ __device__ __forceinline__ void bulk_spread_rows(const LaunchArgs& a, const Copy
       }
     }
     for (uint32_t jd = 0; jd < nd; ++jd) {
-      char* d = static_cast<char*>(a.ptr[R->dst_ptr[kFan1 ? 0 : jd]]) + dst_off;
+      char* d = static_cast<char*>(a.ptr[dst_pool(R, kFan1 ? 0 : jd)]) + dst_off;
 #pragma unroll
       for (int k = 0; k < U; ++k)
         if (l0 + k * kWaves + wave < npu) st16(d + o[k], x[k]);
@@ -418,15 +443,15 @@ __device__ __forceinline__ void bulk_body(const LaunchArgs& a, const CopyRegion*
   const uint64_t d0 = R->dstr[0], d1 = R->dstr[1], d2 = R->dstr[2];
   const uint32_t e0 = R->e0, e1 = R->e1, rows = R->rows, inner = R->inner;
   const uint32_t rpu = R->rows_per_unit, ub = R->unit_begin, flags = R->flags;
-  const uint32_t nd = kFan1 ? 1u : R->n_dst;
+  const uint32_t nd = kFan1 ? 1u : n_dst_of(R);
   const uint32_t nouter = flags & kFlagOuterMask;
-  const char* sp = static_cast<const char*>(a.ptr[R->src_ptr]) + src_off;
-  char* dp0 = static_cast<char*>(a.ptr[R->dst_ptr[0]]) + dst_off;
+  const char* sp = static_cast<const char*>(a.ptr[src_pool(R)]) + src_off;
+  char* dp0 = static_cast<char*>(a.ptr[dst_pool(R, 0)]) + dst_off;
 
   uint32_t al = (flags >> 8) & 15u;
   al |= uint32_t(reinterpret_cast<uintptr_t>(sp) & 15u);
   for (uint32_t j = 0; j < nd; ++j)
-    al |= uint32_t((reinterpret_cast<uintptr_t>(a.ptr[R->dst_ptr[j]]) + dst_off) & 15u);
+    al |= uint32_t((reinterpret_cast<uintptr_t>(a.ptr[dst_pool(R, j)]) + dst_off) & 15u);
 
   const uint32_t r0 = (unit - ub) * rpu;
   const uint32_t r1 = min(r0 + rpu, rows);
@@ -463,7 +488,7 @@ __device__ __forceinline__ void bulk_body(const LaunchArgs& a, const CopyRegion*
         for (int k = 0; k < RS_UNROLL; ++k)
           if (v + k * kThreads < vpr) x[k] = ld16(s + 16ull * (v + k * kThreads));
         for (uint32_t j = 0; j < nd; ++j) {
-          char* d = (kFan1 ? dp0 : static_cast<char*>(a.ptr[R->dst_ptr[j]]) + dst_off) + dof;
+          char* d = (kFan1 ? dp0 : static_cast<char*>(a.ptr[dst_pool(R, j)]) + dst_off) + dof;
 #pragma unroll
           for (int k = 0; k < RS_UNROLL; ++k)
             if (v + k * kThreads < vpr) st16(d + 16ull * (v + k * kThreads), x[k]);
@@ -495,7 +520,7 @@ __device__ __forceinline__ void bulk_body(const LaunchArgs& a, const CopyRegion*
       const uint64_t so = row_off(r, e0, e1, nouter, s0, s1, s2);
       const uint64_t dof = row_off(r, e0, e1, nouter, d0, d1, d2);
       for (uint32_t j = 0; j < nd; ++j) {
-        char* d = static_cast<char*>(a.ptr[R->dst_ptr[j]]) + dst_off + dof;
+        char* d = static_cast<char*>(a.ptr[dst_pool(R, j)]) + dst_off + dof;
         wave_copy_span(d, sp + so, inner, lane);
       }
     }
@@ -506,7 +531,7 @@ __global__ __launch_bounds__(kThreads, RS_BULK_MIN_WAVES) void rs_bulk_kernel(La
   // One workgroup per work unit (looping workgroups measured slower).
   const uint32_t unit = unit_of_block<RS_XCD_MAP != 0>(blockIdx.x, gridDim.x, RS_XCD_CHUNK);
   const CopyRegion* R = find_region<CopyRegion>(a, unit);
-  if (R->n_dst == 1)
+  if (n_dst_of(R) == 1)
     bulk_body<true>(a, R, unit);
   else
     bulk_body<false>(a, R, unit);
@@ -538,14 +563,14 @@ __global__ __launch_bounds__(kThreads) void rs_thin_kernel(LaunchArgs a) {
   const uint64_t d0 = R->dstr[0], d1 = R->dstr[1], d2 = R->dstr[2];
   const uint32_t e0 = R->e0, e1 = R->e1, rows = R->rows, inner = R->inner;
   const uint32_t rpu = R->rows_per_unit, flags = R->flags;
-  const uint32_t nd = R->n_dst;
+  const uint32_t nd = n_dst_of(R);
   const uint32_t nouter = flags & kFlagOuterMask;
-  const char* sp = static_cast<const char*>(a.ptr[R->src_ptr]) + src_off;
+  const char* sp = static_cast<const char*>(a.ptr[src_pool(R)]) + src_off;
 
   uint32_t al = (flags >> 8) & 15u;
   al |= uint32_t(reinterpret_cast<uintptr_t>(sp) & 15u);
   for (uint32_t j = 0; j < nd; ++j)
-    al |= uint32_t((reinterpret_cast<uintptr_t>(a.ptr[R->dst_ptr[j]]) + dst_off) & 15u);
+    al |= uint32_t((reinterpret_cast<uintptr_t>(a.ptr[dst_pool(R, j)]) + dst_off) & 15u);
   const uint32_t g = low_granule(al);
   const uint32_t gpr = inner / g;
 
@@ -558,7 +583,7 @@ __global__ __launch_bounds__(kThreads) void rs_thin_kernel(LaunchArgs a) {
   if (flags & kFlagDstPacked) {
     // Gather strided source rows into LDS (congruent with the first
     // destination mod 16), then write the contiguous destination block.
-    const char* D0 = static_cast<const char*>(a.ptr[R->dst_ptr[0]]) + dst_off + uint64_t(r0) * inner;
+    const char* D0 = static_cast<const char*>(a.ptr[dst_pool(R, 0)]) + dst_off + uint64_t(r0) * inner;
     const uint32_t sh = uint32_t(reinterpret_cast<uintptr_t>(D0) & 15u);
     for (uint32_t f = tid; f < total; f += kThreads) {
       const uint32_t row = f / gpr;
@@ -568,7 +593,7 @@ __global__ __launch_bounds__(kThreads) void rs_thin_kernel(LaunchArgs a) {
     }
     __syncthreads();
     for (uint32_t j = 0; j < nd; ++j) {
-      char* Dj = static_cast<char*>(a.ptr[R->dst_ptr[j]]) + dst_off + uint64_t(r0) * inner;
+      char* Dj = static_cast<char*>(a.ptr[dst_pool(R, j)]) + dst_off + uint64_t(r0) * inner;
       if ((reinterpret_cast<uintptr_t>(Dj) & 15u) == sh)
         block_copy_congruent(Dj, tile + sh, nbytes, tid);
       else
@@ -585,7 +610,7 @@ __global__ __launch_bounds__(kThreads) void rs_thin_kernel(LaunchArgs a) {
       const uint32_t k = f - row * gpr;
       const uint64_t dof = row_off(r0 + row, e0, e1, nouter, d0, d1, d2);
       for (uint32_t j = 0; j < nd; ++j) {
-        char* d = static_cast<char*>(a.ptr[R->dst_ptr[j]]) + dst_off + dof + uint64_t(k) * g;
+        char* d = static_cast<char*>(a.ptr[dst_pool(R, j)]) + dst_off + dof + uint64_t(k) * g;
         copy_granule(d, tile + sh + row * inner + k * g, g);
       }
     }
@@ -597,7 +622,7 @@ __global__ __launch_bounds__(kThreads) void rs_thin_kernel(LaunchArgs a) {
       const uint64_t so = row_off(r0 + row, e0, e1, nouter, s0, s1, s2);
       const uint64_t dof = row_off(r0 + row, e0, e1, nouter, d0, d1, d2);
       for (uint32_t j = 0; j < nd; ++j) {
-        char* d = static_cast<char*>(a.ptr[R->dst_ptr[j]]) + dst_off + dof + uint64_t(k) * g;
+        char* d = static_cast<char*>(a.ptr[dst_pool(R, j)]) + dst_off + dof + uint64_t(k) * g;
         copy_granule(d, sp + so + uint64_t(k) * g, g);
       }
     }
@@ -810,22 +835,58 @@ __device__ __forceinline__ MxCodes mx_encode(u32x4 xa, u32x4 xb) {
 // elements, staged in LDS with row i at slot i << lg (one 16-byte slot per
 // 8-element group).  kOneRow: the unit is a single row, whose addresses are
 // uniform across the workgroup.
-template <bool kOneRow>
-__device__ __forceinline__ void mx_unit(const LaunchArgs& a, const MxRegion* R, uint32_t r0, uint32_t nr,
-                                        u32x4* stage, uint8_t* sc_stage) {
+// The fields of an MXFP8 region a work unit needs, read from the table once
+// at kernel entry, before any branch or store: a table read after a store is
+// a vector load (the compiler cannot rule out that the store changed the
+// table), and its wait would also wait for the stores already issued.
+struct MxFields {
+  uint64_t src_off, dst_off, sc_off;
+  uint64_t s0, s1, s2, d0, d1, d2, c0, c1, c2;
+  uint32_t e0, e1, inner, nouter, sc_inner, nd;
+  const char* sp;       // source buffer + src_off
+  char* dk;             // first destination's element and scale buffers
+  char* sk;
+};
+
+__device__ __forceinline__ MxFields mx_fields(const LaunchArgs& a, const MxRegion* R) {
+  MxFields f;
+  f.src_off = R->src_off;
+  f.dst_off = R->dst_off;
+  f.sc_off = R->sc_off;
+  f.s0 = R->sstr[0]; f.s1 = R->sstr[1]; f.s2 = R->sstr[2];
+  f.d0 = R->dstr[0]; f.d1 = R->dstr[1]; f.d2 = R->dstr[2];
+  f.c0 = R->scstr[0]; f.c1 = R->scstr[1]; f.c2 = R->scstr[2];
+  f.e0 = R->e0;
+  f.e1 = R->e1;
+  f.inner = R->inner;
+  f.nouter = R->flags & kFlagOuterMask;
+  f.sc_inner = R->sc_inner;
+  f.nd = n_dst_of(R);
+  f.sp = static_cast<const char*>(a.ptr[src_pool(R)]) + f.src_off;
+  f.dk = static_cast<char*>(a.ptr[dst_pool(R, 0)]);
+  f.sk = static_cast<char*>(a.ptr[sc_pool(R, 0)]);
+  return f;
+}
+
+template <bool kOneRow, bool kFan1>
+__device__ __forceinline__ void mx_unit(const LaunchArgs& a, const MxRegion* R, const MxFields& f, uint32_t r0,
+                                        uint32_t nr, u32x4* stage, uint8_t* sc_stage) {
   constexpr uint32_t K = kMxSlots / kMxThreads;
   const uint32_t tid = threadIdx.x;
-  const uint64_t s0 = R->sstr[0], s1 = R->sstr[1], s2 = R->sstr[2];
-  const uint64_t d0 = R->dstr[0], d1 = R->dstr[1], d2 = R->dstr[2];
-  const uint64_t c0 = R->scstr[0], c1 = R->scstr[1], c2 = R->scstr[2];
-  const uint32_t e0 = R->e0, e1 = R->e1, inner = R->inner;
-  const uint32_t nouter = R->flags & kFlagOuterMask;
-  const uint32_t sc_inner = R->sc_inner, nd = R->n_dst;
-  const uint32_t lg = mx_slot_shift(inner), Lp = 1u << lg;
-  const uint32_t ng = (inner + 7u) >> 3;
-  const char* sp = static_cast<const char*>(a.ptr[R->src_ptr]) + R->src_off;
+  const uint64_t s0 = f.s0, s1 = f.s1, s2 = f.s2;
+  const uint64_t d0 = f.d0, d1 = f.d1, d2 = f.d2;
+  const uint64_t c0 = f.c0, c1 = f.c1, c2 = f.c2;
+  const uint32_t e0 = f.e0, e1 = f.e1, inner = f.inner;
+  const uint32_t nouter = f.nouter;
+  const uint32_t sc_inner = f.sc_inner, nd = f.nd;
+  const uint64_t dst_off_r = f.dst_off, sc_off_r = f.sc_off;
+  const char* sp = f.sp;
+  char* const dk = f.dk;
+  char* const sk = f.sk;
   const uint64_t so1 = kOneRow ? row_off(r0, e0, e1, nouter, s0, s1, s2) : 0;
   const uint64_t do1 = kOneRow ? row_off(r0, e0, e1, nouter, d0, d1, d2) : 0;
+  const uint32_t lg = mx_slot_shift(inner), Lp = 1u << lg;
+  const uint32_t ng = (inner + 7u) >> 3;
 
   // Phase 1: every group of the unit into its LDS slot.  Whole, 16-byte
   // aligned groups load straight into LDS; a partial or misaligned group is
@@ -865,9 +926,9 @@ __device__ __forceinline__ void mx_unit(const LaunchArgs& a, const MxRegion* R, 
     const u32x4 xb = nvalid > 8 ? stage[s + 1] : u32x4{0u, 0u, 0u, 0u};
     const MxCodes c = mx_encode(xa, xb);
     if (nvalid > 0) {
-      const uint64_t doff = R->dst_off + (kOneRow ? do1 : row_off(r0 + rl, e0, e1, nouter, d0, d1, d2)) + col;
-      for (uint32_t j = 0; j < nd; ++j) {
-        char* d = static_cast<char*>(a.ptr[R->dst_ptr[j]]) + doff;
+      const uint64_t doff = dst_off_r + (kOneRow ? do1 : row_off(r0 + rl, e0, e1, nouter, d0, d1, d2)) + col;
+      for (uint32_t j = 0; j < (kFan1 ? 1u : nd); ++j) {
+        char* d = (kFan1 ? dk : static_cast<char*>(a.ptr[dst_pool(R, j)])) + doff;
         if (nvalid == 16 && (reinterpret_cast<uintptr_t>(d) & 15u) == 0) {
           __builtin_nontemporal_store(c.v, reinterpret_cast<u32x4*>(d));
         } else {
@@ -886,24 +947,35 @@ __device__ __forceinline__ void mx_unit(const LaunchArgs& a, const MxRegion* R, 
   for (uint32_t t = tid; t < kMxSlots / 4; t += kMxThreads) {
     const uint32_t rl = t >> (lg - 2), b = t & ((Lp >> 2) - 1u);
     if (rl < nr && b < nb) {
-      const uint64_t so = R->sc_off + row_off(r0 + rl, e0, e1, nouter, c0, c1, c2) + uint64_t(b) * sc_inner;
+      const uint64_t so = sc_off_r + row_off(r0 + rl, e0, e1, nouter, c0, c1, c2) + uint64_t(b) * sc_inner;
       const char v = char(sc_stage[t]);
-      for (uint32_t j = 0; j < nd; ++j) __builtin_nontemporal_store(v, static_cast<char*>(a.ptr[R->sc_ptr[j]]) + so);
+      for (uint32_t j = 0; j < (kFan1 ? 1u : nd); ++j)
+        __builtin_nontemporal_store(v, (kFan1 ? sk : static_cast<char*>(a.ptr[sc_pool(R, j)])) + so);
     }
   }
 }
 
+template <bool kOneRow>
+__device__ __forceinline__ void mx_unit_fan(const LaunchArgs& a, const MxRegion* R, const MxFields& f,
+                                            uint32_t r0, uint32_t nr, u32x4* stage, uint8_t* sc_stage) {
+  if (f.nd == 1)
+    mx_unit<kOneRow, true>(a, R, f, r0, nr, stage, sc_stage);
+  else
+    mx_unit<kOneRow, false>(a, R, f, r0, nr, stage, sc_stage);
+}
+
 __global__ __launch_bounds__(kMxThreads, RS_MX_MIN_WAVES) void rs_mx_kernel(LaunchArgs a) {
   __shared__ u32x4 stage[kMxSlots];
-  __shared__ uint8_t sc_stage[kMxSlots / 4];
+  __shared__ __attribute__((aligned(16))) uint8_t sc_stage[kMxSlots / 4];
   const uint32_t unit = unit_of_block<RS_MX_XCD_MAP != 0>(blockIdx.x, gridDim.x, RS_MX_XCD_CHUNK);
   const MxRegion* R = find_region<MxRegion>(a, unit);
   const uint32_t r0 = (unit - R->unit_begin) * R->rows_per_unit;
   const uint32_t nr = min(R->rows_per_unit, R->rows - r0);
+  const MxFields f = mx_fields(a, R);
   if (nr == 1)
-    mx_unit<true>(a, R, r0, nr, stage, sc_stage);
+    mx_unit_fan<true>(a, R, f, r0, nr, stage, sc_stage);
   else
-    mx_unit<false>(a, R, r0, nr, stage, sc_stage);
+    mx_unit_fan<false>(a, R, f, r0, nr, stage, sc_stage);
 }
 
 }  // namespace

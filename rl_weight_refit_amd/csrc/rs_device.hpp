@@ -3,6 +3,7 @@
 // compiles as ordinary C++.
 #pragma once
 
+#include <stddef.h>
 #include <stdint.h>
 
 namespace rs {
@@ -110,6 +111,14 @@ struct alignas(16) MxRegion {
   uint16_t sc_ptr[kMaxFan];
 };
 static_assert(sizeof(MxRegion) == 208, "MxRegion must stay 208 bytes");
+// The kernels read the 16-bit pool indices as the 32-bit words holding them:
+// src_ptr, n_dst, dst_ptr[] (and sc_ptr[]) follow one another from a
+// 4-byte-aligned src_ptr.
+static_assert(offsetof(CopyRegion, src_ptr) % 4 == 0 && offsetof(CopyRegion, n_dst) == offsetof(CopyRegion, src_ptr) + 2 &&
+              offsetof(CopyRegion, dst_ptr) == offsetof(CopyRegion, src_ptr) + 4, "CopyRegion pool index layout");
+static_assert(offsetof(MxRegion, src_ptr) % 4 == 0 && offsetof(MxRegion, n_dst) == offsetof(MxRegion, src_ptr) + 2 &&
+              offsetof(MxRegion, dst_ptr) == offsetof(MxRegion, src_ptr) + 4 &&
+              offsetof(MxRegion, sc_ptr) == offsetof(MxRegion, dst_ptr) + 2 * kMaxFan, "MxRegion pool index layout");
 
 // Kernel arguments of one launch.
 struct LaunchArgs {
