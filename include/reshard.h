@@ -243,6 +243,27 @@ rs_status reshard_execute(const rs_plan* plan, void* const* src_ptrs, void* cons
  * RS_ERR_HIP naming launch k, and the destinations are only partly
  * installed (execute again once the cause is fixed). */
 
+/* reshard_execute for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, checks, launches and results as
+ * reshard_execute, but the plan's region tables are not uploaded into an
+ * allocation of the plan: every call copies them (hipMemcpyAsync on
+ * `stream`, from the plan's host image) into a static device array of the
+ * library, RESHARD_TABLE_AREA_BYTES long, which each GPU holds from the
+ * library's load until the process ends.  The call allocates no device
+ * memory (no hipMalloc, no hipFree).
+ * Sharing: every call on a GPU uses that GPU's one area, which keeps the
+ * last call's tables.  Calls on one stream are ordered and safe; calls that
+ * overlap on one GPU (other streams, other threads, other plans) race for
+ * the area and may read each other's tables -- serialise them.
+ * Errors: those of reshard_execute, and RS_ERR_UNSUPPORTED, before anything
+ * is copied or launched, for a plan whose tables exceed the area
+ * (rs_plan_info gives n_regions; a region takes 128 bytes, an MXFP8 region
+ * 208, plus 4 bytes per 256 work units). */
+#define RESHARD_TABLE_AREA_BYTES (4u << 20)
+rs_status reshard_execute_no_alloc(const rs_plan* plan, void* const* src_ptrs,
+                                   void* const* dst_ptrs, void* stream);
+
 /* Fill *info: the plan's pointer counts, region and work-unit counts per
  * kernel, launches per execute, algorithmic bytes and planning time.  The
  * per-receiver descriptor count and the bytes a refit moves are the figures

@@ -92,6 +92,8 @@ def load():
     lib.reshard_plan.restype = c_i32
     lib.reshard_execute.argtypes = [P, ctypes.POINTER(P), ctypes.POINTER(P), P]
     lib.reshard_execute.restype = c_i32
+    lib.reshard_execute_no_alloc.argtypes = [P, ctypes.POINTER(P), ctypes.POINTER(P), P]
+    lib.reshard_execute_no_alloc.restype = c_i32
     lib.reshard_plan_info.argtypes = [P, ctypes.POINTER(PlanInfo)]
     lib.reshard_plan_info.restype = c_i32
     lib.reshard_plan_region.argtypes = [P, c_u64, ctypes.POINTER(Region)]
@@ -260,6 +262,18 @@ def reshard_execute(plan, src_ptrs, dst_ptrs, stream=None):
     s = _ptr_array(src_ptrs)
     d = _ptr_array(dst_ptrs)
     _check(load().reshard_execute(plan.handle, s, d, ctypes.c_void_p(stream or 0)))
+
+
+def reshard_execute_no_alloc(plan, src_ptrs, dst_ptrs, stream=None):
+    """reshard_execute without any device allocation: the plan's tables go
+    through the library's static per-GPU table area (calls that overlap on
+    one GPU race for it)."""
+    if len(src_ptrs) != plan.n_src_ptrs or len(dst_ptrs) != plan.n_dst_ptrs:
+        raise ValueError("the plan takes %d source and %d destination pointers, got %d and %d"
+                         % (plan.n_src_ptrs, plan.n_dst_ptrs, len(src_ptrs), len(dst_ptrs)))
+    s = _ptr_array(src_ptrs)
+    d = _ptr_array(dst_ptrs)
+    _check(load().reshard_execute_no_alloc(plan.handle, s, d, ctypes.c_void_p(stream or 0)))
 
 
 def reshard_shard_box(spec, slot):

@@ -17,6 +17,10 @@
 namespace rs {
 // Enqueues one launch of a bucket's kernel on `stream`, whose device is `dev`.
 hipError_t launch(uint32_t bucket, uint32_t grid, const LaunchArgs& args, hipStream_t stream, int dev);
+// Device address of the library's static table area on device `dev` (see
+// kernels.hip); looked up once per device.
+hipError_t table_area(int dev, char** out);
+extern const uint64_t kTableAreaBytes;
 }
 
 struct rs_plan {
@@ -107,7 +111,14 @@ rs_status plan_tables(const rs_plan* plan, int dev, char** base) {
   return st == RS_OK ? RS_OK : fail(st, msg);
 }
 
-rs_status execute(const rs_plan* plan, void* const* src_ptrs, void* const* dst_ptrs, void* stream) {
+// Where execute() finds the plan's device tables.
+enum class Tables {
+  kPlanOwned,   // uploaded once per device into an allocation the plan owns
+  kStaticArea,  // copied on every call into the library's static area (no allocation)
+};
+
+rs_status execute(const rs_plan* plan, void* const* src_ptrs, void* const* dst_ptrs, void* stream,
+                  Tables where) {
   if (!plan) return fail(RS_ERR_INVALID, "plan is NULL\n");
   const rs::PlanData& d = plan->d;
   std::ostringstream err;
@@ -153,6 +164,12 @@ rs_status execute(const rs_plan* plan, void* const* src_ptrs, void* const* dst_p
     }
   }
   if (nerr) return fail(RS_ERR_INVALID, err.str());
+  if (where == Tables::kStaticArea && d.image.size() > rs::kTableAreaBytes) {
+    err << "the plan's device tables take " << d.image.size() << " bytes, more than the "
+        << rs::kTableAreaBytes << "-byte static table area of reshard_execute_no_alloc "
+        << "(use reshard_execute)\n";
+    return fail(RS_ERR_UNSUPPORTED, err.str());
+  }
   if (d.launches.empty()) return RS_OK;
 
   // The kernels run on the stream's device, so the tables must live there.
@@ -194,8 +211,20 @@ rs_status execute(const rs_plan* plan, void* const* src_ptrs, void* const* dst_p
     if (nerr) return fail(RS_ERR_INVALID, err.str());
   }
   char* base = nullptr;
-  const rs_status ts = plan_tables(plan, dev, &base);
-  if (ts != RS_OK) return ts;
+  if (where == Tables::kPlanOwned) {
+    const rs_status ts = plan_tables(plan, dev, &base);
+    if (ts != RS_OK) return ts;
+  } else {
+    he = rs::table_area(dev, &base);
+    if (he != hipSuccess)
+      return fail(RS_ERR_HIP, std::string("address of the static table area: ") + hipGetErrorString(he) + "\n");
+    // Stream-ordered: earlier work on this stream (a previous call's
+    // kernels) has finished reading the area before the copy lands.
+    he = hipMemcpyAsync(base, d.image.data(), d.image.size(), hipMemcpyHostToDevice,
+                        static_cast<hipStream_t>(stream));
+    if (he != hipSuccess)
+      return fail(RS_ERR_HIP, std::string("copy of the plan tables: ") + hipGetErrorString(he) + "\n");
+  }
   for (size_t li = 0; li < d.launches.size(); ++li) {
     const rs::Launch& L = d.launches[li];
     rs::LaunchArgs args;
@@ -227,7 +256,17 @@ rs_status reshard_execute(const rs_plan* plan, void* const* src_ptrs, void* cons
                           void* stream) {
   g_error.clear();
   try {
-    return execute(plan, src_ptrs, dst_ptrs, stream);
+    return execute(plan, src_ptrs, dst_ptrs, stream, Tables::kPlanOwned);
+  } catch (const std::bad_alloc&) {
+    return fail(RS_ERR_ALLOC, "host allocation failed\n");
+  }
+}
+
+rs_status reshard_execute_no_alloc(const rs_plan* plan, void* const* src_ptrs, void* const* dst_ptrs,
+                                   void* stream) {
+  g_error.clear();
+  try {
+    return execute(plan, src_ptrs, dst_ptrs, stream, Tables::kStaticArea);
   } catch (const std::bad_alloc&) {
     return fail(RS_ERR_ALLOC, "host allocation failed\n");
   }

@@ -50,6 +50,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "rs_device.hpp"
 
@@ -1007,6 +1008,43 @@ size_t bulk_lds_pad(int dev) {
   if (pad > per_wg) pad = per_wg;
   if (dev >= 0 && dev < kMaxDevices) cache[dev].store(pad + 1, std::memory_order_relaxed);
   return size_t(pad);
+}
+
+// Static table area of reshard_execute_no_alloc: a plan's region and chunk
+// tables are copied here on every such call instead of into an allocation
+// the plan owns.  Each device holds its own copy of the array from the
+// library's load until the process ends.  `scratch` is a host-side stand-in
+// in host code: its device address comes from hipGetSymbolAddress, looked
+// up once per device with that device current, and only that address is
+// handed to copies and kernels.
+extern const uint64_t kTableAreaBytes = uint64_t(4) << 20;
+__device__ __align__(256) char scratch[uint64_t(4) << 20];
+
+hipError_t table_area(int dev, char** out) {
+  static std::atomic<char*> addr[kMaxDevices];
+  static std::mutex mu;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  char* p = addr[dev].load(std::memory_order_acquire);
+  if (p) {
+    *out = p;
+    return hipSuccess;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  p = addr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess) return e;
+    p = static_cast<char*>(a);
+    addr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
 }
 
 hipError_t launch(uint32_t bucket, uint32_t grid, const LaunchArgs& args, hipStream_t stream, int dev) {
