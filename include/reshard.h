@@ -194,6 +194,17 @@ typedef struct rs_region {
   uint64_t ext[3];
   uint64_t src_stride[3], dst_stride[3], scale_stride[3];
   uint64_t scale_inner_stride;   /* MXFP8 only: bytes between consecutive block scales */
+  /* Second source piece (MXFP8 only).  A 32-element block whose values two
+   * source shards hold (their boundary falls inside the block) is installed
+   * by a region one block wide: columns [0, split) of each row come from
+   * src_index as above, columns [split, inner) from src2_index at src2_off
+   * + sum_k ik * src2_stride[k], column split first.  split == inner for
+   * every one-source region. */
+  uint64_t split;
+  uint32_t src2_index;
+  uint32_t reserved0;
+  uint64_t src2_off;
+  uint64_t src2_stride[3];
 } rs_region;
 
 /* Plan n_tensors tensor pairs (for example gate, up and down of one layer)
@@ -205,8 +216,9 @@ typedef struct rs_region {
  * the first (cf. the single error listing every violation of
  * "NCCL Reshard Refit (Experimental)", "Enabling It").
  * Errors: RS_ERR_INVALID, RS_ERR_MISMATCH, RS_ERR_UNSUPPORTED (for example an
- * MXFP8 block that would span two source shards, or a non-contiguous last
- * dim on an MXFP8 tensor), RS_ERR_ALLOC. */
+ * MXFP8 block whose 32 values come from more than two source shards, i.e.
+ * source shards narrower than a block along the last dim, or a
+ * non-contiguous last dim on an MXFP8 tensor), RS_ERR_ALLOC. */
 rs_status reshard_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32_t n_tensors,
                        const rs_plan_opts* opts, rs_plan** out);
 

@@ -65,7 +65,9 @@ class Region(ctypes.Structure):
                 ("dst_index", c_u32 * RS_MAX_FANOUT), ("scale_index", c_u32 * RS_MAX_FANOUT),
                 ("src_off", c_u64), ("dst_off", c_u64), ("scale_off", c_u64), ("inner", c_u64),
                 ("ext", c_u64 * 3), ("src_stride", c_u64 * 3), ("dst_stride", c_u64 * 3),
-                ("scale_stride", c_u64 * 3), ("scale_inner_stride", c_u64)]
+                ("scale_stride", c_u64 * 3), ("scale_inner_stride", c_u64),
+                ("split", c_u64), ("src2_index", c_u32), ("reserved0", c_u32), ("src2_off", c_u64),
+                ("src2_stride", c_u64 * 3)]
 
 
 class ReshardError(RuntimeError):
@@ -208,7 +210,9 @@ class Plan:
                 "src_off": r.src_off, "dst_off": r.dst_off, "scale_off": r.scale_off,
                 "inner": r.inner, "ext": list(r.ext), "src_stride": list(r.src_stride),
                 "dst_stride": list(r.dst_stride), "scale_stride": list(r.scale_stride),
-                "scale_inner_stride": r.scale_inner_stride}
+                "scale_inner_stride": r.scale_inner_stride, "split": r.split,
+                "src2_index": r.src2_index, "src2_off": r.src2_off,
+                "src2_stride": list(r.src2_stride)}
 
     def regions(self):
         return [self.region(i) for i in range(self.info()["n_regions"])]

@@ -843,10 +843,12 @@ __device__ __forceinline__ MxCodes mx_encode(u32x4 xa, u32x4 xb) {
 struct MxFields {
   uint64_t src_off, dst_off, sc_off;
   uint64_t s0, s1, s2, d0, d1, d2, c0, c1, c2;
-  uint32_t e0, e1, inner, nouter, sc_inner, nd;
+  uint32_t e0, e1, inner, nouter, sc_inner, nd, split;
   const char* sp;       // source buffer + src_off
   char* dk;             // first destination's element and scale buffers
   char* sk;
+  const char* sp2;      // two-piece regions: second source + src2_off, and its strides
+  uint64_t t0, t1, t2;
 };
 
 __device__ __forceinline__ MxFields mx_fields(const LaunchArgs& a, const MxRegion* R) {
@@ -866,10 +868,19 @@ __device__ __forceinline__ MxFields mx_fields(const LaunchArgs& a, const MxRegio
   f.sp = static_cast<const char*>(a.ptr[src_pool(R)]) + f.src_off;
   f.dk = static_cast<char*>(a.ptr[dst_pool(R, 0)]);
   f.sk = static_cast<char*>(a.ptr[sc_pool(R, 0)]);
+  f.split = R->split;
+  f.sp2 = nullptr;
+  f.t0 = f.t1 = f.t2 = 0;
+  if (f.split < f.inner) {
+    f.sp2 = static_cast<const char*>(a.ptr[pool_field(R, 2 + 2 * kMaxFan)]) + R->src2_off;
+    f.t0 = R->sstr2[0];
+    f.t1 = R->sstr2[1];
+    f.t2 = R->sstr2[2];
+  }
   return f;
 }
 
-template <bool kOneRow, bool kFan1>
+template <bool kOneRow, bool kFan1, bool kTwo = false>
 __device__ __forceinline__ void mx_unit(const LaunchArgs& a, const MxRegion* R, const MxFields& f, uint32_t r0,
                                         uint32_t nr, u32x4* stage, uint8_t* sc_stage) {
   constexpr uint32_t K = kMxSlots / kMxThreads;
@@ -896,7 +907,21 @@ __device__ __forceinline__ void mx_unit(const LaunchArgs& a, const MxRegion* R, 
   for (uint32_t k = 0; k < K; ++k) {
     const uint32_t s = k * kMxThreads + tid;
     const uint32_t rl = s >> lg, g = s & (Lp - 1u);
-    if (rl < nr && g < ng) {
+    if (kTwo && rl < nr && g < ng) {
+      // Two pieces: each element from the piece that holds its column.
+      const char* p1 = sp + row_off(r0 + rl, e0, e1, nouter, s0, s1, s2);
+      const char* p2 = f.sp2 + row_off(r0 + rl, e0, e1, nouter, f.t0, f.t1, f.t2);
+      uint32_t w[4] = {0, 0, 0, 0};
+      for (uint32_t i = 0; i < 8; ++i) {
+        const uint32_t c = g * 8u + i;
+        if (c < inner) {
+          const uint16_t v = c < f.split ? *reinterpret_cast<const uint16_t*>(p1 + 2u * c)
+                                         : *reinterpret_cast<const uint16_t*>(p2 + 2u * (c - f.split));
+          w[i >> 1] |= uint32_t(v) << (16 * (i & 1));
+        }
+      }
+      stage[s] = u32x4{w[0], w[1], w[2], w[3]};
+    } else if (rl < nr && g < ng) {
       const char* p = sp + (kOneRow ? so1 : row_off(r0 + rl, e0, e1, nouter, s0, s1, s2)) +
                       uint64_t(g) * 16u;
       if (g * 8u + 8u <= inner && (reinterpret_cast<uintptr_t>(p) & 15u) == 0) {
@@ -959,7 +984,9 @@ __device__ __forceinline__ void mx_unit(const LaunchArgs& a, const MxRegion* R, 
 template <bool kOneRow>
 __device__ __forceinline__ void mx_unit_fan(const LaunchArgs& a, const MxRegion* R, const MxFields& f,
                                             uint32_t r0, uint32_t nr, u32x4* stage, uint8_t* sc_stage) {
-  if (f.nd == 1)
+  if (f.split < f.inner)
+    mx_unit<kOneRow, false, true>(a, R, f, r0, nr, stage, sc_stage);
+  else if (f.nd == 1)
     mx_unit<kOneRow, true>(a, R, f, r0, nr, stage, sc_stage);
   else
     mx_unit<kOneRow, false>(a, R, f, r0, nr, stage, sc_stage);

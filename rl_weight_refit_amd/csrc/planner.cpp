@@ -374,6 +374,7 @@ bool same_view(const rs_view& a, const rs_view& b, int ndim) {
 // A region before it is split to fit the kernels.
 struct Dim {
   uint64_t ext, ss, ds, sc;  // extent; byte strides on src, dst, scale sides
+  uint64_t ss2 = 0;          // source stride of a two-piece MXFP8 region's second piece
 };
 
 // Outer dims, outermost first (fixed capacity: tensor rank + one split).
@@ -400,6 +401,17 @@ struct Raw {
   uint64_t inner;                 // bytes (copy) or elements (mx)
   uint64_t sc_inner;
   Dims outer;
+  // MXFP8 only.  A block that two source shards share is installed by a
+  // region with two pieces: columns [0, split) come from the first source
+  // (src_index, src_off, outer ss), columns [split, inner) from the second
+  // (src2_index, src2_off, outer ss2).  split == inner: one piece.
+  uint64_t split = 0;
+  uint32_t src2_index = 0;
+  uint64_t src2_off = 0;
+  // While planning: destination-local first column and the offsets of
+  // column 0 of these rows (elements, scale bytes), to group the pieces of
+  // one row box before cutting them into regions.
+  uint64_t c0 = 0, kloc = 0, drow = 0, srow = 0;
 };
 
 uint64_t rows_of(const Dims& o) {
@@ -415,11 +427,13 @@ void merge_outer(Dims& o, bool with_scale) {
     if (d.ext == 1) continue;
     if (!m.empty()) {
       Dim& p = m.back();  // p outer, d inner
-      if (p.ss == d.ext * d.ss && p.ds == d.ext * d.ds && (!with_scale || p.sc == d.ext * d.sc)) {
+      if (p.ss == d.ext * d.ss && p.ds == d.ext * d.ds && (!with_scale || p.sc == d.ext * d.sc) &&
+          p.ss2 == d.ext * d.ss2) {
         p.ext *= d.ext;
         p.ss = d.ss;
         p.ds = d.ds;
         p.sc = d.sc;
+        p.ss2 = d.ss2;
         continue;
       }
     }
@@ -439,6 +453,96 @@ struct Opts {
   uint64_t thin = 128;
 };
 
+// Same destinations and rows (the pieces of one MXFP8 row box).
+bool same_row_box(const Raw& a, const Raw& b) {
+  if (a.tensor != b.tensor || a.n_dst != b.n_dst || a.drow != b.drow || a.srow != b.srow ||
+      a.outer.n != b.outer.n || a.kloc != b.kloc)
+    return false;
+  for (uint32_t j = 0; j < a.n_dst; ++j)
+    if (a.dst_index[j] != b.dst_index[j] || a.sc_index[j] != b.sc_index[j]) return false;
+  for (int i = 0; i < a.outer.n; ++i)
+    if (a.outer.d[i].ext != b.outer.d[i].ext || a.outer.d[i].ds != b.outer.d[i].ds ||
+        a.outer.d[i].sc != b.outer.d[i].sc)
+      return false;
+  return true;
+}
+
+// Columns [c, c + n) of piece p as a one-source region (c block-aligned,
+// n whole blocks or up to the row end).
+Raw mx_part(const Raw& p, uint64_t c, uint64_t n) {
+  Raw r = p;
+  r.src_off = p.src_off + (c - p.c0) * 2;
+  r.dst_off = p.drow + c;
+  r.sc_off = p.srow + (c / kMxBlock) * p.sc_inner;
+  r.inner = n;
+  r.split = n;
+  merge_outer(r.outer, true);
+  return r;
+}
+
+void cut_mx_pieces(std::vector<Raw>& raws, Errors& E) {
+  std::vector<size_t> mx;
+  for (size_t i = 0; i < raws.size(); ++i)
+    if (raws[i].mx) mx.push_back(i);
+  if (mx.empty()) return;
+  // Pieces of one row box are created consecutively (columns innermost),
+  // but sort to be independent of that order.
+  std::stable_sort(mx.begin(), mx.end(), [&](size_t x, size_t y) {
+    const Raw& a = raws[x];
+    const Raw& b = raws[y];
+    if (a.tensor != b.tensor) return a.tensor < b.tensor;
+    if (a.dst_index[0] != b.dst_index[0]) return a.dst_index[0] < b.dst_index[0];
+    if (a.drow != b.drow) return a.drow < b.drow;
+    if (a.srow != b.srow) return a.srow < b.srow;
+    return a.c0 < b.c0;
+  });
+  std::vector<Raw> out;
+  out.reserve(raws.size());
+  for (size_t i = 0; i < raws.size(); ++i)
+    if (!raws[i].mx) out.push_back(std::move(raws[i]));
+  size_t g = 0;
+  while (g < mx.size()) {
+    size_t e = g + 1;
+    while (e < mx.size() && same_row_box(raws[mx[g]], raws[mx[e]])) ++e;
+    const uint64_t K = raws[mx[g]].kloc;
+    for (size_t i = g; i < e; ++i) {
+      const Raw& p = raws[mx[i]];
+      const uint64_t a = p.c0, b = p.c0 + p.inner;
+      if (i > g && a % kMxBlock != 0) {
+        // The block holding column a starts in the previous piece.
+        const Raw& q = raws[mx[i - 1]];
+        const uint64_t B = a - a % kMxBlock, Eb = std::min<uint64_t>(B + kMxBlock, K);
+        if (q.c0 > B || b < Eb || q.c0 + q.inner != a) {
+          E.add(&E.unsupported, "tensor ", p.tensor, ": MXFP8 block at columns ", B, "..", Eb,
+                " of a destination shard takes values from more than two source shards "
+                "(source shards narrower than a 32-element block along the last dim)");
+          continue;
+        }
+        Raw r = q;
+        r.src_off = q.src_off + (B - q.c0) * 2;
+        r.src2_index = p.src_index;
+        r.src2_off = p.src_off;
+        r.split = a - B;
+        r.inner = Eb - B;
+        r.dst_off = q.drow + B;
+        r.sc_off = q.srow + (B / kMxBlock) * q.sc_inner;
+        for (int k = 0; k < r.outer.n; ++k) r.outer.d[k].ss2 = p.outer.d[k].ss;
+        merge_outer(r.outer, true);
+        out.push_back(std::move(r));
+      }
+      // Whole blocks of this piece alone (the last block may be short).
+      const uint64_t lo = (a + kMxBlock - 1) / kMxBlock * kMxBlock;
+      const uint64_t hi = b == K ? b : b - b % kMxBlock;
+      if (hi > lo) out.push_back(mx_part(p, lo, hi - lo));
+    }
+    if (raws[mx[g]].c0 != 0 || raws[mx[e - 1]].c0 + raws[mx[e - 1]].inner != K)
+      E.add(&E.invalid, "internal: MXFP8 pieces of tensor ", raws[mx[g]].tensor,
+            " do not tile the destination row");
+    g = e;
+  }
+  raws.swap(out);
+}
+
 // Splits a raw region until the kernels can take it: at most 3 outer dims,
 // rows < 2^31, every extent < 2^32, and (copy) inner <= unit bytes.
 void finalize(Raw r, const Opts& o, std::vector<Raw>& out) {  // r by value: it is modified
@@ -450,12 +554,14 @@ void finalize(Raw r, const Opts& o, std::vector<Raw>& out) {  // r by value: it 
     if (rem) {
       Raw tail = r;
       tail.inner = rem;
+      tail.split = rem;   // one piece (two-piece regions are one block wide)
       tail.src_off += q * C * 2;
       tail.dst_off += q * C;
       tail.sc_off += q * sc_step;
       finalize(tail, o, out);
     }
     r.inner = C;
+    r.split = C;
     r.outer.push_back({q, 2 * C, C, sc_step});
     merge_outer(r.outer, true);
   }
@@ -487,6 +593,7 @@ void finalize(Raw r, const Opts& o, std::vector<Raw>& out) {  // r by value: it 
         Raw s = r;
         s.outer = rest;
         s.src_off += i * top.ss;
+        s.src2_off += i * top.ss2;
         s.dst_off += i * top.ds;
         s.sc_off += i * top.sc;
         finalize(std::move(s), o, out);
@@ -498,9 +605,10 @@ void finalize(Raw r, const Opts& o, std::vector<Raw>& out) {  // r by value: it 
         const uint64_t n = part ? top.ext - h : h;
         const uint64_t first = part ? h : 0;
         s.outer.n = 0;
-        s.outer.push_back(Dim{n, top.ss, top.ds, top.sc});
+        s.outer.push_back(Dim{n, top.ss, top.ds, top.sc, top.ss2});
         for (const Dim& x : rest) s.outer.push_back(x);
         s.src_off += first * top.ss;
+        s.src2_off += first * top.ss2;
         s.dst_off += first * top.ds;
         s.sc_off += first * top.sc;
         finalize(std::move(s), o, out);
@@ -522,11 +630,12 @@ struct Final {
 
 // Fills the fields shared by the public and device views.
 void outer_fields(const Dims& o, uint64_t ext[3], uint64_t ss[3], uint64_t ds[3],
-                  uint64_t sc[3]) {
+                  uint64_t sc[3], uint64_t* ss2 = nullptr) {
   // Device convention: index 0 is the innermost outer dim.
   for (int k = 0; k < 3; ++k) {
     ext[k] = 1;
     ss[k] = ds[k] = sc[k] = 0;
+    if (ss2) ss2[k] = 0;
   }
   const int n = int(o.size());
   for (int k = 0; k < n; ++k) {
@@ -535,6 +644,7 @@ void outer_fields(const Dims& o, uint64_t ext[3], uint64_t ss[3], uint64_t ds[3]
     ss[k] = d.ss;
     ds[k] = d.ds;
     sc[k] = d.sc;
+    if (ss2) ss2[k] = d.ss2;
   }
 }
 
@@ -846,28 +956,28 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
             const rs_view& cv = B.scale_views[ds0];
             const int last = nd - 1;
             const int64_t c0 = st[last] - db[last].start;
-            const int64_t kloc = db[last].len;
-            const int64_t c1 = c0 + ln[last];
-            if (c0 % kMxBlock != 0 || (c1 % kMxBlock != 0 && c1 != kloc)) {
-              E.add(&E.unsupported, "tensor ", t, ": an MXFP8 block of destination slot ", ds0,
-                    " would span two source shards or parts (columns ", c0, "..", c1,
-                    " of its last dim); block-aligned splits are required");
-            }
             if ((sv.strides[last] != 1 && ln[last] > 1) || (dv.strides[last] != 1 && ln[last] > 1))
               E.add(&E.unsupported, "tensor ", t,
                     ": MXFP8 install needs a contiguous last dim on both sides");
             for (int dd = B.split ? 1 : 0; dd < last; ++dd)
               sco += (st[dd] - db[dd].start) * cv.strides[dd];
-            sco += cv.base + (c0 / kMxBlock) * cv.strides[last];
+            sco += cv.base;
+            // One piece of a destination row box: columns [c0, c0 + inner)
+            // from one source shard.  Pieces are cut into regions below,
+            // once all pieces of the row box are known.
             r.src_off = uint64_t(so) * 2;
             r.dst_off = uint64_t(dof);
-            r.sc_off = uint64_t(sco);
+            r.sc_off = 0;
             r.inner = uint64_t(ln[last]);
+            r.split = r.inner;
             r.sc_inner = uint64_t(cv.strides[last]);
+            r.c0 = uint64_t(c0);
+            r.kloc = uint64_t(db[last].len);
+            r.drow = uint64_t(dof - c0);
+            r.srow = uint64_t(sco);
             for (int dd = 0; dd < last; ++dd)
               r.outer.push_back({uint64_t(ln[dd]), uint64_t(sv.strides[dd]) * 2,
                                  uint64_t(dv.strides[dd]), uint64_t(cv.strides[dd])});
-            merge_outer(r.outer, true);
           }
           raws.push_back(std::move(r));
         }
@@ -877,6 +987,19 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
       if (dd < 0) break;
     }
   }
+  if (E.status() != RS_OK) {
+    err = E.text.str();
+    return E.status();
+  }
+
+  // ---- MXFP8 row boxes: pieces -> regions ----------------------------------
+  // The pieces of one destination row box (same tensor, destinations,
+  // rows) tile its columns [0, kloc) in source-shard order.  Blocks inside
+  // one piece become one-source regions; a block that two pieces share (a
+  // source shard boundary off the 32-column grid) becomes a two-piece
+  // region one block wide, whose kernel work unit gathers the block's
+  // values from both sources before taking its amax.
+  cut_mx_pieces(raws, E);
   if (E.status() != RS_OK) {
     err = E.text.str();
     return E.status();
@@ -985,9 +1108,10 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
       uint64_t units = 0;
       while (i < list.size()) {
         const Final* f = list[i];
-        uint32_t need[1 + 2 * kMaxFan];
+        uint32_t need[2 + 2 * kMaxFan];
         int nneed = 0;
         need[nneed++] = f->rp->src_index;
+        if (f->rp->mx && f->rp->split < f->rp->inner) need[nneed++] = f->rp->src2_index;
         for (uint32_t j = 0; j < f->rp->n_dst; ++j) {
           need[nneed++] = f->rp->dst_index[j] | kDstBit;
           if (f->rp->mx) need[nneed++] = f->rp->sc_index[j] | kDstBit;
@@ -1063,8 +1187,8 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
       for (size_t k = 0; k < batch.size(); ++k) {
         const Final& f = *batch[k];
         const Raw& r = *f.rp;
-        uint64_t ext[3], ss[3], ds[3], sc[3];
-        outer_fields(r.outer, ext, ss, ds, sc);
+        uint64_t ext[3], ss[3], ds[3], sc[3], ss2[3];
+        outer_fields(r.outer, ext, ss, ds, sc, ss2);
         uint8_t* dstp = out.image.data() + L.regions_off + rsz * k;
         if (bucket == kMx) {
           MxRegion m;
@@ -1076,6 +1200,12 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
             m.sstr[q] = ss[q];
             m.dstr[q] = ds[q];
             m.scstr[q] = sc[q];
+          }
+          m.split = uint32_t(r.split);
+          if (r.split < r.inner) {
+            m.src2_ptr = pool(r.src2_index);
+            m.src2_off = r.src2_off;
+            for (int q = 0; q < 3; ++q) m.sstr2[q] = ss2[q];
           }
           m.e0 = uint32_t(ext[0]);
           m.e1 = uint32_t(ext[1]);
@@ -1200,6 +1330,12 @@ rs_status region_info(const PlanData& d, uint64_t index, rs_region* out) {
         out->scale_stride[q] = m.scstr[q];
       }
       out->scale_inner_stride = m.sc_inner;
+      out->split = m.split;
+      if (m.split < m.inner) {
+        out->src2_index = user(m.src2_ptr);
+        out->src2_off = m.src2_off;
+        for (int q = 0; q < 3; ++q) out->src2_stride[q] = m.sstr2[q];
+      }
     } else {
       CopyRegion c;
       std::memcpy(&c, d.image.data() + L.regions_off + k * sizeof(CopyRegion), sizeof(c));
@@ -1209,6 +1345,7 @@ rs_status region_info(const PlanData& d, uint64_t index, rs_region* out) {
       out->src_off = c.src_off;
       out->dst_off = c.dst_off;
       out->inner = c.inner;
+      out->split = c.inner;
       const uint32_t nouter = c.flags & kFlagOuterMask;
       const uint64_t e2 = (nouter >= 3) ? uint64_t(c.rows) / (uint64_t(c.e0) * c.e1) : 1;
       const uint64_t ext[3] = {nouter >= 1 ? c.e0 : 1u, nouter >= 2 ? c.e1 : 1u, e2};

@@ -88,7 +88,8 @@ struct alignas(16) CopyRegion {
 static_assert(sizeof(CopyRegion) == 128, "CopyRegion must stay 128 bytes");
 
 // An MXFP8 install region: rows x inner bf16 elements (inner along the
-// destination's last dim, starting on a 32-element block boundary).  Element
+// destination's last dim, starting on a 32-element block boundary), from
+// one source or, for a block two source shards share, from two pieces.  Element
 // bytes go to dst, block scales to scale (one byte per block,
 // sc_inner bytes apart).
 struct alignas(16) MxRegion {
@@ -109,8 +110,17 @@ struct alignas(16) MxRegion {
   uint16_t n_dst;
   uint16_t dst_ptr[kMaxFan];
   uint16_t sc_ptr[kMaxFan];
+  // Two-piece regions (one block wide, where a source shard boundary falls
+  // inside a 32-element block): columns [split, inner) of row r come from
+  // src2_ptr at src2_off + row offset by sstr2, column split first.
+  // split == inner: one piece.
+  uint16_t src2_ptr;
+  uint16_t pad0;
+  uint32_t split;
+  uint64_t src2_off;
+  uint64_t sstr2[3];
 };
-static_assert(sizeof(MxRegion) == 208, "MxRegion must stay 208 bytes");
+static_assert(sizeof(MxRegion) == 240, "MxRegion must stay 240 bytes");
 // The kernels read the 16-bit pool indices as the 32-bit words holding them:
 // src_ptr, n_dst, dst_ptr[] (and sc_ptr[]) follow one another from a
 // 4-byte-aligned src_ptr.
@@ -118,7 +128,9 @@ static_assert(offsetof(CopyRegion, src_ptr) % 4 == 0 && offsetof(CopyRegion, n_d
               offsetof(CopyRegion, dst_ptr) == offsetof(CopyRegion, src_ptr) + 4, "CopyRegion pool index layout");
 static_assert(offsetof(MxRegion, src_ptr) % 4 == 0 && offsetof(MxRegion, n_dst) == offsetof(MxRegion, src_ptr) + 2 &&
               offsetof(MxRegion, dst_ptr) == offsetof(MxRegion, src_ptr) + 4 &&
-              offsetof(MxRegion, sc_ptr) == offsetof(MxRegion, dst_ptr) + 2 * kMaxFan, "MxRegion pool index layout");
+              offsetof(MxRegion, sc_ptr) == offsetof(MxRegion, dst_ptr) + 2 * kMaxFan &&
+              offsetof(MxRegion, src2_ptr) == offsetof(MxRegion, sc_ptr) + 2 * kMaxFan,
+              "MxRegion pool index layout");
 
 // Kernel arguments of one launch.
 struct LaunchArgs {

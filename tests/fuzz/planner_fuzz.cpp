@@ -29,6 +29,7 @@ namespace {
 uint64_t g_bucket_regions[4] = {};   // regions replayed, per bucket
 uint64_t g_valid_rejected = 0;       // uncorrupted cases the planner declined (e.g. MXFP8 blocks across sources)
 uint64_t g_sibling_groups = 0;       // thin sibling groups checked
+uint64_t g_two_piece = 0;            // MXFP8 regions with two source pieces replayed
 
 struct Rng {
   uint64_t s;
@@ -352,13 +353,23 @@ bool run_case(Rng& g, uint64_t c, bool corrupt) {
     ++g_bucket_regions[R.bucket];
     const bool isq = R.bucket == 3;
     const uint64_t rows = R.ext[0] * R.ext[1] * R.ext[2];
-    const uint64_t rd = isq ? 2 * R.inner : R.inner;
+    const bool two = isq && R.split < R.inner;
+    if (R.split > R.inner || (!isq && R.split != R.inner)) die("bad split", c);
+    if (two && (R.inner > 32 || R.src2_index >= sbuf.size())) die("bad two-piece region", c);
+    if (two) ++g_two_piece;
+    const uint64_t rd = isq ? 2 * R.split : R.inner;
     const uint64_t nb = isq ? (R.inner + 31) / 32 : 0;
     for (uint64_t r = 0; r < rows; ++r) {
       const uint64_t i0 = r % R.ext[0], i1 = (r / R.ext[0]) % R.ext[1], i2 = r / (R.ext[0] * R.ext[1]);
       const uint64_t so = R.src_off + i0 * R.src_stride[0] + i1 * R.src_stride[1] + i2 * R.src_stride[2];
       const Buf& sb = sbuf[R.src_index];
       if (so + rd > sb.bytes.size()) die("region reads past its source buffer", c);
+      if (two) {
+        const uint64_t so2 = R.src2_off + i0 * R.src2_stride[0] + i1 * R.src2_stride[1] +
+                             i2 * R.src2_stride[2];
+        if (so2 + 2 * (R.inner - R.split) > sbuf[R.src2_index].bytes.size())
+          die("region reads past its second source buffer", c);
+      }
       for (uint32_t j = 0; j < R.n_dst; ++j) {
         if (R.dst_index[j] >= dbuf.size()) die("bad destination index", c);
         Buf& db = dbuf[R.dst_index[j]];
@@ -449,8 +460,8 @@ int main(int argc, char** argv) {
   std::printf("cases %" PRIu64 ": planned and replayed %" PRIu64 ", rejected %" PRIu64
               " (%" PRIu64 " of them uncorrupted, unsupported), corrupted but accepted %" PRIu64
               "; regions replayed: bulk %" PRIu64 ", thin %" PRIu64 ", tiny %" PRIu64 ", mxfp8 %" PRIu64
-              "; thin sibling groups %" PRIu64 "\n",
+              "; thin sibling groups %" PRIu64 "; two-piece MXFP8 regions %" PRIu64 "\n",
               cases, planned, rejected, g_valid_rejected, corrupt_ok, g_bucket_regions[0],
-              g_bucket_regions[1], g_bucket_regions[2], g_bucket_regions[3], g_sibling_groups);
+              g_bucket_regions[1], g_bucket_regions[2], g_bucket_regions[3], g_sibling_groups, g_two_piece);
   return 0;
 }

@@ -76,8 +76,16 @@ def interpret(plan, src_flat, dst_flat, count=None):
                 if count is not None:
                     np.add.at(count[j], idx_d.reshape(-1), 1)
         else:
-            idx_s = so[:, None] + np.arange(2 * inner)[None, :]
-            bits = src[idx_s].reshape(len(so), inner, 2).copy().view(np.uint16)[..., 0]
+            # Columns [0, split) from the source, [split, inner) from the
+            # second piece (a block two source shards share).
+            split = int(r["split"])
+            idx_s = so[:, None] + np.arange(2 * split)[None, :]
+            raw = src[idx_s]
+            if split < inner:
+                so2 = _row_offsets(r["ext"], r["src2_stride"]) + r["src2_off"]
+                idx2 = so2[:, None] + np.arange(2 * (inner - split))[None, :]
+                raw = np.concatenate([raw, src_flat[r["src2_index"]][idx2]], axis=1)
+            bits = raw.reshape(len(so), inner, 2).copy().view(np.uint16)[..., 0]
             codes, scales = omx.quantize(bits)
             co = _row_offsets(r["ext"], r["scale_stride"]) + r["scale_off"]
             nb = scales.shape[1]

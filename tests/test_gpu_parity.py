@@ -383,3 +383,39 @@ def test_fp8_blockwise_dsv3_shape_32_experts():
     2048, 128 x 128 blocks), EP16 -> EP8 x TP8."""
     gh.log("fp8 dsv3 32 experts")
     gh.check_against_oracle(synth.fp8_moe_experts(32, 7168, 2048, 16, 8, 8, seed=4))
+
+
+@pytest.mark.parametrize("shifts", [(0, 0), (2, 1)])
+@pytest.mark.parametrize("i", range(9))
+def test_mxfp8_blocks_from_two_sources(i, shifts):
+    """MXFP8 blocks that straddle a source shard boundary along the last dim
+    (TP3 over 2,048, 257 = 129 + 128, both sides cutting the last dim, rows
+    longer than a unit), gathered from two sources in one work unit; also
+    with sources on 2-byte and destinations on odd byte boundaries."""
+    import test_planner as tp
+    gh.check_against_oracle(tp.mx_split_workload(i), src_shift=shifts[0], dst_shift=shifts[1])
+
+
+@pytest.mark.parametrize("seed", range(0, 40, 3))
+def test_mxfp8_random_last_dim_splits(seed):
+    import test_planner as tp
+    rng = np.random.default_rng(seed)
+    nd = int(rng.integers(2, 4))
+    shape = [int(rng.integers(1, 6)) for _ in range(nd - 1)] + [int(rng.integers(33, 700))]
+    parts = int(rng.integers(2, max(3, min(8, shape[-1] // 32) + 1)))
+    smesh, spl = ([parts], [nd - 1]) if rng.integers(2) else ([2, parts], [0, nd - 1])
+    dmesh, dpl = [[1], [-1]] if rng.integers(2) else [[2], [int(rng.integers(0, nd))]]
+    t = {"name": "w", "shape": shape, "dtype": "bf16", "src": synth.side(smesh, spl),
+         "dst": synth.side(dmesh, dpl, quant="mxfp8"), "values": {"kind": "normal", "std": 0.02, "seed": seed}}
+    gh.check_against_oracle({"name": "mx_rand_%d" % seed, "buffers": {}, "tensors": [t]})
+
+
+def test_mxfp8_two_source_blocks_replicated():
+    """Two-piece regions with replicated destinations (one read, four
+    element and scale replicas written)."""
+    t = {"name": "w", "shape": [6, 2048], "dtype": "bf16", "src": synth.side([3], [1]),
+         "dst": synth.side([2, 2], [0, -1], quant="mxfp8"),
+         "values": {"kind": "normal", "std": 0.02, "seed": 77}}
+    plan = gh.check_against_oracle({"name": "mx_two_rep", "buffers": {}, "tensors": [t]})
+    two = [r for r in plan.regions() if r["split"] < r["inner"]]
+    assert two and all(len(r["dst_index"]) == 2 for r in two)

@@ -312,12 +312,70 @@ def test_view_reaching_past_the_64_bit_range_is_rejected():
     assert e.value.status == 1 and "views[0]" in str(e.value)
 
 
-def test_mxfp8_block_spanning_sources_is_unsupported():
-    src = {"shape": [4, 100], "dtype": "bf16", "mesh": [2], "placements": [1]}
+def test_mxfp8_block_from_three_sources_is_unsupported():
+    """Source shards of 13 columns put three of them inside one 32-element
+    block; a region gathers a block from at most two."""
+    src = {"shape": [4, 100], "dtype": "bf16", "mesh": [8], "placements": [1]}
     dst = {"shape": [4, 100], "dtype": "u8", "mesh": [1], "placements": [-1], "quant": "mxfp8"}
     with pytest.raises(binding.ReshardError) as e:
         binding.reshard_plan([src], [dst])
-    assert e.value.status == 3 and "span" in str(e.value)
+    assert e.value.status == 3 and "more than two source shards" in str(e.value)
+
+
+# MXFP8 destinations whose 32-element blocks straddle a source shard
+# boundary along the last dim: (shape, source mesh, placements, destination
+# mesh, placements).
+MX_SPLIT_LAYOUTS = [
+    ([4, 2048], [3], [1], [1], [-1]),            # TP3 over 2,048: boundaries at 683 and 1,366
+    ([4, 2048], [3], [1], [2], [0]),
+    ([7, 51, 257], [2], [2], [2], [0]),          # 129 + 128
+    ([7, 51, 257], [2, 3], [0, 2], [4], [1]),    # 86 + 86 + 85
+    ([6, 100], [2], [1], [1], [-1]),             # 50 + 50
+    ([3, 5, 1000], [7], [2], [2], [1]),          # 143 per shard
+    ([2, 3, 7168], [3], [2], [2, 2], [0, 1]),    # 2,390 per shard, rows longer than one unit
+    ([4, 300], [3], [1], [2], [1]),              # both sides cut the last dim
+    ([5, 96], [3], [-1], [3], [1]),              # aligned cuts only (32 per shard)
+]
+
+
+def mx_split_workload(i, fanout_mesh=None):
+    shape, sm, sp, dm, dp = MX_SPLIT_LAYOUTS[i]
+    t = {"name": "w", "shape": shape, "dtype": "bf16", "src": synth.side(sm, sp),
+         "dst": synth.side(dm, dp, quant="mxfp8"), "values": {"kind": "normal", "std": 0.02, "seed": 40 + i}}
+    return {"name": "mx_split_%d" % i, "buffers": {}, "tensors": [t]}
+
+
+@pytest.mark.parametrize("i", range(len(MX_SPLIT_LAYOUTS)))
+def test_interpreted_mxfp8_blocks_from_two_sources(i):
+    """Blocks gathered from two source shards: the plan's regions, replayed
+    on the host, equal the oracle's MXFP8 bytes; straddling blocks come as
+    two-piece regions one block wide."""
+    wl = mx_split_workload(i)
+    plan, dst_flat, count = run_interpreted(wl)
+    two = [r for r in plan.regions() if r["split"] < r["inner"]]
+    straddles = i != len(MX_SPLIT_LAYOUTS) - 1
+    assert bool(two) == straddles
+    for r in two:
+        assert r["inner"] <= 32 and 0 < r["split"] < r["inner"]
+    for c in counts_by_buffer(dst_flat, count).values():
+        assert c.max() <= 1
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_interpreted_mxfp8_random_last_dim_splits(seed):
+    """Random MXFP8 layouts whose source meshes cut the last dim off the
+    block grid (rows 1-3 dims, last extents 33-700, source shards at least
+    32 wide), replayed on the host against the oracle."""
+    rng = np.random.default_rng(seed)
+    nd = int(rng.integers(2, 4))
+    shape = [int(rng.integers(1, 6)) for _ in range(nd - 1)] + [int(rng.integers(33, 700))]
+    parts = int(rng.integers(2, max(3, min(8, shape[-1] // 32) + 1)))
+    smesh, spl = ([parts], [nd - 1]) if rng.integers(2) else ([2, parts], [0, nd - 1])
+    dmesh, dpl = [[1], [-1]] if rng.integers(2) else [[2], [int(rng.integers(0, nd))]]
+    t = {"name": "w", "shape": shape, "dtype": "bf16", "src": synth.side(smesh, spl),
+         "dst": synth.side(dmesh, dpl, quant="mxfp8"), "values": {"kind": "normal", "std": 0.02, "seed": seed}}
+    wl = {"name": "mx_rand_%d" % seed, "buffers": {}, "tensors": [t]}
+    run_interpreted(wl)
 
 
 def test_execute_rejects_null_pointer_before_launch():

@@ -42,5 +42,7 @@ def test_planner_fuzz_sanitized(fuzz_exe, seed):
                        env=env)
     assert r.returncode == 0, (r.stdout[-4000:] + r.stderr[-4000:])
     assert "planned and replayed" in r.stdout
-    groups = int(r.stdout.split("thin sibling groups")[1].split()[0])
+    groups = int(r.stdout.split("thin sibling groups")[1].split()[0].rstrip(";"))
     assert groups > 0, r.stdout
+    two = int(r.stdout.split("two-piece MXFP8 regions")[1].split()[0])
+    assert two > 0, r.stdout
