@@ -23,9 +23,13 @@
 //        column shard): rows are gathered through an LDS tile so the side
 //        that is contiguous across rows is written (or read) with 16-byte
 //        vectors.  Sibling regions (same source rows, different columns)
-//        take their units member-fastest, in short XCD turns, so the
-//        workgroups reading one block of source rows run together on one
-//        XCD and share its lines instead of each fetching them from HBM.
+//        whose destinations are packed are loaded whole by a kernel of
+//        their own: one workgroup reads a block of the group's source rows
+//        once (direct-to-LDS 16-byte loads when the block is contiguous and
+//        aligned) and writes every member's rows from LDS with 16-byte
+//        stores.  Other siblings take their units member-fastest, in short
+//        XCD turns, so the workgroups reading one block of source rows run
+//        together on one XCD and share its lines.
 //  tiny  regions of at most a few hundred bytes: one lane per region, a
 //        wave-level prefix sum of their granule counts, then all 64 lanes
 //        share the wave's granules.
@@ -59,6 +63,7 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ uint64_t row_off(uint32_t r, uint32_t e0, uint32_t e1, uint32_t nouter,
                                             uint64_t s0, uint64_t s1, uint64_t s2) {
@@ -106,6 +111,15 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) {
 #endif
 #ifndef RS_XCD_CHUNK
 #define RS_XCD_CHUNK 4096   // units per XCD turn (0: one contiguous eighth per XCD)
+#endif
+#ifndef RS_THIN_GROUP_DMA
+#define RS_THIN_GROUP_DMA 1    // group-loaded thin units: aligned blocks go straight into LDS
+#endif
+#ifndef RS_THIN_LDS_AUX
+#define RS_THIN_LDS_AUX 2      // cache policy of those direct-to-LDS loads (2: non-temporal)
+#endif
+#ifndef RS_THIN_GROUP_BATCH
+#define RS_THIN_GROUP_BATCH 1  // group-loaded thin units: a lane's loads all in flight before LDS writes
 #endif
 #ifndef RS_THIN_XCD_CHUNK
 #define RS_THIN_XCD_CHUNK 16  // thin kernel: units per XCD turn (0: dispatch order)
@@ -542,6 +556,161 @@ __global__ __launch_bounds__(kThreads, RS_BULK_MIN_WAVES) void rs_bulk_kernel(La
 // thin (LDS-staged)
 // ---------------------------------------------------------------------------
 
+// Packed destination rows of one member of a group loaded whole: output
+// byte q of the member's rows [r0, r1) is LDS byte row * S + cm + col of
+// the staged span (row = q / inner, col = q % inner).  G: the granule the
+// LDS side allows (a divisor of inner, cm and S); 16-byte stores where the
+// destination is 16-byte aligned, granules for the rest.
+template <int G>
+__device__ __forceinline__ void group_store(char* D, const char* lds, uint32_t cm, uint32_t S, uint32_t inner,
+                                           uint32_t nbytes, uint32_t tid) {
+  uint32_t head = 0;
+  if ((reinterpret_cast<uintptr_t>(D) & 15u) == 0) {
+    const uint32_t nvec = nbytes >> 4;
+    for (uint32_t v = tid; v < nvec; v += kThreads) {
+      uint32_t row = (16u * v) / inner;
+      uint32_t col = 16u * v - row * inner;
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int k = 0; k < 16 / G; ++k) {
+        const char* p = lds + row * S + cm + col;
+        if (G == 16) {
+          const u32x4 t = *reinterpret_cast<const u32x4*>(p);
+          w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
+        } else if (G == 8) {
+          const u32x2 t = *reinterpret_cast<const u32x2*>(p);
+          w[2 * k] = t.x;
+          w[2 * k + 1] = t.y;
+        } else if (G == 4) {
+          w[k] = *reinterpret_cast<const uint32_t*>(p);
+        } else if (G == 2) {
+          w[k >> 1] |= uint32_t(*reinterpret_cast<const uint16_t*>(p)) << (16 * (k & 1));
+        } else {
+          w[k >> 2] |= uint32_t(*reinterpret_cast<const uint8_t*>(p)) << (8 * (k & 3));
+        }
+        col += G;
+        if (col >= inner) {
+          col -= inner;
+          ++row;
+        }
+      }
+      st16(D + 16u * v, u32x4{w[0], w[1], w[2], w[3]});
+    }
+    head = nvec << 4;
+  }
+  // The rest (a tail, or everything for a misaligned destination) by
+  // granules as wide as both sides allow.
+  const uint32_t g = low_granule(uint32_t(G) | uint32_t(reinterpret_cast<uintptr_t>(D) & 15u));
+  for (uint32_t q = head + tid * g; q < nbytes; q += kThreads * g) {
+    const uint32_t row = q / inner, col = q - row * inner;
+    copy_granule(D + q, lds + row * S + cm + col, g);
+  }
+}
+
+// One unit of a sibling group loaded whole (kFlagGroupLoad; R is the
+// group's first member, the members follow it in the table): rows
+// [r0, r1) of the group's column span go into LDS once -- 16-byte vectors
+// when consecutive rows of the span are contiguous in the source -- and
+// every member writes its packed destination rows from there.
+__device__ __forceinline__ void thin_group_unit(const LaunchArgs& a, const CopyRegion* R, uint32_t ul, char* tile) {
+  const uint32_t tid = threadIdx.x;
+  const uint32_t gm = (R->flags >> 16) & 255u;
+  const uint32_t rows = R->rows, rpu = R->rows_per_unit;
+  const uint32_t e0 = R->e0, e1 = R->e1, nouter = R->flags & kFlagOuterMask;
+  const uint64_t s0 = R->sstr[0], s1 = R->sstr[1], s2 = R->sstr[2];
+  uint64_t lo = R->src_off, hi = R->src_off + R->inner;
+  for (uint32_t m = 1; m < gm; ++m) {
+    lo = min(lo, R[m].src_off);
+    hi = max(hi, R[m].src_off + R[m].inner);
+  }
+  const uint32_t S = uint32_t(hi - lo);
+  const char* base = static_cast<const char*>(a.ptr[src_pool(R)]) + lo;
+  const uint32_t r0 = ul * rpu, r1 = min(r0 + rpu, rows), T = r1 - r0;
+  uint32_t sh = 0;
+  if (nouter <= 1 && s0 == S) {
+    // One contiguous block: byte head, then 16-byte vectors with all of a
+    // lane's loads in flight before any LDS write, then a byte tail.
+    const char* src = base + uint64_t(r0) * S;
+    sh = uint32_t(reinterpret_cast<uintptr_t>(src) & 15u);
+    const uint32_t n = T * S;
+#if RS_THIN_GROUP_DMA
+    if (sh == 0 && (n & 15u) == 0) {
+      // Aligned block: straight into LDS with direct-to-LDS 16-byte loads
+      // (no registers; every load of the unit in flight at once).
+      constexpr uint32_t kB = (kGroupTile / 16 + kThreads - 1) / kThreads;
+      const uint32_t nv = n >> 4;
+#pragma unroll
+      for (uint32_t k = 0; k < kB; ++k) {
+        const uint32_t v = k * kThreads + tid;
+        if (v < nv)
+          __builtin_amdgcn_global_load_lds(src + 16u * v,
+                                           (lds_void*)(tile + 16u * (k * kThreads + (tid & ~63u))), 16, 0,
+                                           RS_THIN_LDS_AUX);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+    } else
+#endif
+    {
+#if RS_THIN_GROUP_BATCH
+    uint32_t h = (16u - sh) & 15u;
+    if (h > n) h = n;
+    if (tid < h) tile[sh + tid] = src[tid];
+    const uint32_t nv = (n - h) >> 4;
+    const u32x4* sv = reinterpret_cast<const u32x4*>(src + h);
+    u32x4* dv = reinterpret_cast<u32x4*>(tile + sh + h);
+    constexpr uint32_t kB = (kGroupTile / 16 + kThreads - 1) / kThreads;
+    u32x4 x[kB];
+#pragma unroll
+    for (uint32_t k = 0; k < kB; ++k)
+      if (k * kThreads + tid < nv) x[k] = ld16(sv + k * kThreads + tid);
+#pragma unroll
+    for (uint32_t k = 0; k < kB; ++k)
+      if (k * kThreads + tid < nv) dv[k * kThreads + tid] = x[k];
+    const uint32_t done = h + (nv << 4);
+    if (tid < n - done) tile[sh + done + tid] = src[done + tid];
+#else
+    block_copy_congruent(tile + sh, src, n, tid);
+#endif
+    }
+  } else {
+    uint32_t al = uint32_t(reinterpret_cast<uintptr_t>(base) & 15u) | S | uint32_t(s0 & 15u);
+    if (nouter >= 2) al |= uint32_t(s1 & 15u);
+    if (nouter >= 3) al |= uint32_t(s2 & 15u);
+    const uint32_t g = low_granule(al), gpr = S / g, total = T * gpr;
+    for (uint32_t f = tid; f < total; f += kThreads) {
+      const uint32_t row = f / gpr, k = f - row * gpr;
+      copy_granule(tile + row * S + k * g, base + row_off(r0 + row, e0, e1, nouter, s0, s1, s2) + k * g, g);
+    }
+  }
+  __syncthreads();
+  const char* lds = tile + sh;
+  for (uint32_t m = 0; m < gm; ++m) {
+    const CopyRegion* M = R + m;
+    const uint32_t cm = uint32_t(M->src_off - lo), inner = M->inner, nd = n_dst_of(M);
+    const uint32_t nbytes = T * inner;
+    const uint32_t G = low_granule((sh + cm) | S | inner);
+    for (uint32_t j = 0; j < nd; ++j) {
+      char* D = static_cast<char*>(a.ptr[dst_pool(M, j)]) + M->dst_off + uint64_t(r0) * inner;
+      switch (G) {
+        case 16: group_store<16>(D, lds, cm, S, inner, nbytes, tid); break;
+        case 8: group_store<8>(D, lds, cm, S, inner, nbytes, tid); break;
+        case 4: group_store<4>(D, lds, cm, S, inner, nbytes, tid); break;
+        case 2: group_store<2>(D, lds, cm, S, inner, nbytes, tid); break;
+        default: group_store<1>(D, lds, cm, S, inner, nbytes, tid); break;
+      }
+    }
+  }
+}
+
+// Thin sibling groups loaded whole (launches of their own: this path needs
+// more registers than the thin kernel's others).
+__global__ __launch_bounds__(kThreads) void rs_thin_group_kernel(LaunchArgs a) {
+  __shared__ __attribute__((aligned(16))) char tile[kGroupTile + 16];
+  const uint32_t unit = unit_of_block<RS_THIN_XCD_CHUNK != 0>(blockIdx.x, gridDim.x, RS_THIN_XCD_CHUNK);
+  const CopyRegion* R = find_region<CopyRegion>(a, unit);
+  thin_group_unit(a, R, unit - R->unit_begin, tile);
+}
+
 __global__ __launch_bounds__(kThreads) void rs_thin_kernel(LaunchArgs a) {
   __shared__ __attribute__((aligned(16))) char tile[kThinTile + 16];
   const uint32_t tid = threadIdx.x;
@@ -796,7 +965,6 @@ __device__ __forceinline__ uint32_t e4m3x4(uint32_t w0, uint32_t w1, uint32_t m0
 #define RS_MX_LDS_AUX 2    // cache policy of the direct-to-LDS loads (2: non-temporal)
 #endif
 
-typedef __attribute__((address_space(3))) void lds_void;
 
 // Block codes of one lane's two adjacent 8-element groups xa, xb (bf16
 // pairs, 16 elements, half a block; zeros past the row end).  The two lanes
@@ -1081,6 +1249,9 @@ hipError_t launch(uint32_t bucket, uint32_t grid, const LaunchArgs& args, hipStr
       hipLaunchKernelGGL(rs_bulk_kernel, dim3(grid), dim3(kThreads), bulk_lds_pad(dev), stream, args);
       break;
     case kThin: hipLaunchKernelGGL(rs_thin_kernel, dim3(grid), dim3(kThreads), 0, stream, args); break;
+    case kThinGroup:
+      hipLaunchKernelGGL(rs_thin_group_kernel, dim3(grid), dim3(kThreads), 0, stream, args);
+      break;
     case kTiny: hipLaunchKernelGGL(rs_tiny_kernel, dim3(grid), dim3(kThreads), 0, stream, args); break;
     case kMx: hipLaunchKernelGGL(rs_mx_kernel, dim3(grid), dim3(kMxThreads), 0, stream, args); break;
     default: return hipErrorInvalidValue;

@@ -445,6 +445,9 @@ void merge_outer(Dims& o, bool with_scale) {
 #ifndef RS_THIN_SIBLINGS
 #define RS_THIN_SIBLINGS 1   // group thin regions that read the same source rows
 #endif
+#ifndef RS_THIN_GROUP_LOAD
+#define RS_THIN_GROUP_LOAD 1 // load short-span sibling groups whole (one workgroup per row block)
+#endif
 
 struct Opts {
   bool fanout = true;
@@ -1096,10 +1099,60 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
                     4 * ((bytes_read / o.unit) >> kChunkShift) + 4096);
   uint64_t nreg_bucket[kBuckets] = {}, nunit_bucket[kBuckets] = {};
   std::vector<int32_t> pool_src(n_src_ptrs, -1), pool_dst(n_dst_ptrs, -1);
-  for (uint32_t bucket = 0; bucket < kBuckets; ++bucket) {
+  // Thin sibling groups (consecutive thin regions reading the same source
+  // rows at different columns) and which of them are loaded whole: every
+  // member writes packed rows and the group's column span is short.  Those
+  // run in launches of their own, with a kernel of their own.
+  auto same_rows = [](const Final& x, const Final& y) {
+    if (x.rp->src_index != y.rp->src_index || x.rows != y.rows || x.units != y.units ||
+        x.rows_per_unit != y.rows_per_unit || x.rp->outer.size() != y.rp->outer.size() ||
+        x.rp->outer.size() == 0)
+      return false;
+    uint64_t xe[3], xs[3], xd[3], xc[3], ye[3], ys[3], yd[3], yc[3];
+    outer_fields(x.rp->outer, xe, xs, xd, xc);
+    outer_fields(y.rp->outer, ye, ys, yd, yc);
+    for (int q = 0; q < 3; ++q)
+      if (xe[q] != ye[q] || xs[q] != ys[q]) return false;
+    const uint64_t a = x.rp->src_off, b = y.rp->src_off;
+    return (a > b ? a - b : b - a) < xs[0];
+  };
+  std::vector<uint32_t> group_of(fin.size(), 0);  // 1 + group number, 0: none
+  std::vector<uint8_t> whole(fin.size(), 0);
+  if (RS_THIN_SIBLINGS) {
+    std::vector<size_t> thin;
+    for (size_t q = 0; q < fin.size(); ++q)
+      if (fin[q].bucket == kThin) thin.push_back(q);
+    size_t k = 0;
+    uint32_t ng = 0;
+    while (k < thin.size()) {
+      size_t e = k + 1;
+      while (e < thin.size() && e - k < 255 && same_rows(fin[thin[k]], fin[thin[e]])) ++e;
+      if (e - k >= 2) {
+        ++ng;
+        bool packed_all = true;
+        uint64_t lo = ~uint64_t(0), hi = 0;
+        for (size_t q = k; q < e; ++q) {
+          const Final& f = fin[thin[q]];
+          group_of[thin[q]] = ng;
+          packed_all &= (f.flags & kFlagDstPacked) != 0;
+          lo = std::min(lo, f.rp->src_off);
+          hi = std::max(hi, f.rp->src_off + f.rp->inner);
+        }
+        if (RS_THIN_GROUP_LOAD && packed_all && hi - lo <= kGroupSpanMax)
+          for (size_t q = k; q < e; ++q) whole[thin[q]] = 1;
+      }
+      k = e;
+    }
+  }
+
+  // Launch passes: one per bucket, then the thin groups loaded whole.
+  for (uint32_t pass = 0; pass <= kBuckets; ++pass) {
+    const uint32_t bucket = pass < kBuckets ? pass : uint32_t(kThin);
+    const uint32_t kernel = pass < kBuckets ? pass : uint32_t(kThinGroup);
     std::vector<const Final*> list;
-    for (const Final& f : fin)
-      if (f.bucket == bucket) list.push_back(&f);
+    for (size_t q = 0; q < fin.size(); ++q)
+      if (fin[q].bucket == bucket && (bucket != kThin || whole[q] == (pass == kBuckets)))
+        list.push_back(&fin[q]);
     size_t i = 0;
     while (i < list.size()) {
       // Greedy group: regions in order while their pointers fit the pool.
@@ -1145,7 +1198,7 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
         return uint16_t((k & kDstBit) ? pool_dst[k & ~kDstBit] : pool_src[k]);
       };
       Launch L;
-      L.bucket = bucket;
+      L.bucket = kernel;
       L.n_regions = uint32_t(batch.size());
       L.pool = members;
       align_up(out.image, 256);
@@ -1161,26 +1214,47 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
       // share the fetched lines.  Flags bits 16-23 hold the group size,
       // bits 24-31 the member index.
       std::vector<uint32_t> sib(batch.size(), 0);
-      if (RS_THIN_SIBLINGS && bucket == kThin) {
-        auto same_rows = [](const Final& x, const Final& y) {
-          if (x.rp->src_index != y.rp->src_index || x.rows != y.rows || x.units != y.units ||
-              x.rows_per_unit != y.rows_per_unit || x.rp->outer.size() != y.rp->outer.size() ||
-              x.rp->outer.size() == 0)
-            return false;
-          uint64_t xe[3], xs[3], xd[3], xc[3], ye[3], ys[3], yd[3], yc[3];
-          outer_fields(x.rp->outer, xe, xs, xd, xc);
-          outer_fields(y.rp->outer, ye, ys, yd, yc);
-          for (int q = 0; q < 3; ++q)
-            if (xe[q] != ye[q] || xs[q] != ys[q]) return false;
-          const uint64_t a = x.rp->src_off, b = y.rp->src_off;
-          return (a > b ? a - b : b - a) < xs[0];
-        };
+      std::vector<uint32_t> units_k(batch.size()), rpu_k(batch.size());
+      for (size_t k = 0; k < batch.size(); ++k) {
+        units_k[k] = batch[k]->units;
+        rpu_k[k] = batch[k]->rows_per_unit;
+      }
+      if (bucket == kThin) {
+        // Sibling groups of this launch: consecutive members of one group
+        // (a group cut by the pointer pool continues in the next launch as
+        // a group of its own).  Flags bits 16-23 hold the group size, bits
+        // 24-31 the member index.
         size_t k = 0;
         while (k < batch.size()) {
+          const uint32_t gid = group_of[size_t(batch[k] - fin.data())];
           size_t e = k + 1;
-          while (e < batch.size() && e - k < 255 && same_rows(*batch[k], *batch[e])) ++e;
-          if (e - k >= 2)
+          while (gid && e < batch.size() && group_of[size_t(batch[e] - fin.data())] == gid) ++e;
+          if (e - k >= 2) {
             for (size_t q = k; q < e; ++q) sib[q] = (uint32_t(e - k) << 16) | (uint32_t(q - k) << 24);
+            if (kernel == kThinGroup) {
+              // The group's units belong to its first member: each unit
+              // moves rows_per_unit rows of every member.
+              uint64_t lo = ~uint64_t(0), hi = 0;
+              for (size_t q = k; q < e; ++q) {
+                lo = std::min(lo, batch[q]->rp->src_off);
+                hi = std::max(hi, batch[q]->rp->src_off + batch[q]->rp->inner);
+              }
+              const uint64_t rows = batch[k]->rows;
+              const uint64_t rpu = std::min<uint64_t>(std::max<uint64_t>(1, kGroupTile / (hi - lo)), rows);
+              for (size_t q = k; q < e; ++q) {
+                sib[q] |= kFlagGroupLoad;
+                rpu_k[q] = uint32_t(rpu);
+                units_k[q] = q == k ? uint32_t((rows + rpu - 1) / rpu) : 0;
+              }
+            }
+          } else if (kernel == kThinGroup) {
+            // A lone member left by a pool cut: a group of one.
+            sib[k] = kFlagGroupLoad | (1u << 16);
+            const uint64_t rows = batch[k]->rows;
+            const uint64_t rpu = std::min<uint64_t>(std::max<uint64_t>(1, kGroupTile / batch[k]->rp->inner), rows);
+            rpu_k[k] = uint32_t(rpu);
+            units_k[k] = uint32_t((rows + rpu - 1) / rpu);
+          }
           k = e;
         }
       }
@@ -1237,7 +1311,7 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
           c.e1 = uint32_t(ext[1]);
           c.rows = uint32_t(f.rows);
           c.inner = uint32_t(r.inner);
-          c.rows_per_unit = f.rows_per_unit;
+          c.rows_per_unit = rpu_k[k];
           c.unit_begin = ub;
           c.flags = f.flags | (uint32_t(al & 15) << 8) | sib[k];
           c.src_ptr = pool(r.src_index);
@@ -1248,10 +1322,10 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
         if (bucket != kTiny) {
           // Chunk table: the region of every (1 << kChunkShift)-th unit.
           const uint64_t first = (uint64_t(ub) + (1u << kChunkShift) - 1) >> kChunkShift;
-          for (uint64_t c = first; (c << kChunkShift) < uint64_t(ub) + f.units; ++c)
+          for (uint64_t c = first; (c << kChunkShift) < uint64_t(ub) + units_k[k]; ++c)
             unit_region.push_back(uint32_t(k));
         }
-        ub += f.units;
+        ub += units_k[k];
 
         out.region_tensor.push_back(r.tensor);
       }
@@ -1305,7 +1379,7 @@ rs_status region_info(const PlanData& d, uint64_t index, rs_region* out) {
     const uint64_t k = index - base;
     std::memset(out, 0, sizeof(*out));
     out->tensor = d.region_tensor[index];
-    out->bucket = L.bucket;
+    out->bucket = L.bucket == kThinGroup ? uint32_t(kThin) : L.bucket;
     auto user = [&](uint16_t slot) { return L.pool[slot] & ~kDstBit; };
     if (L.bucket == kMx) {
       MxRegion m;

@@ -56,13 +56,29 @@ constexpr uint32_t mx_slot_shift(uint32_t inner) {
 }
 
 enum Bucket : uint32_t { kBulk = 0, kThin = 1, kTiny = 2, kMx = 3, kBuckets = 4 };
+// Launch kind of thin sibling groups loaded whole (reported as thin regions;
+// a kernel of their own, so the thin kernel keeps its register budget).
+constexpr uint32_t kThinGroup = kBuckets;
 
 // Region flags.
 enum : uint32_t {
   kFlagOuterMask = 3u,      // number of outer dims (0..3)
   kFlagSrcPacked = 1u << 2, // consecutive rows are contiguous on the source side
   kFlagDstPacked = 1u << 3, // ... on the destination side
+  // Thin sibling group loaded whole: the group's units belong to its first
+  // member (the others have none); a unit copies rows of the group's column
+  // span [min src_off, max src_off + inner) into LDS once and writes every
+  // member's (packed) destination rows from there.
+  kFlagGroupLoad = 1u << 4,
 };
+// Largest column span of a sibling group loaded whole, and the LDS tile a
+// unit of such a group fills (rows x span bytes).
+constexpr uint32_t kGroupSpanMax = 4096;
+#ifndef RS_GROUP_TILE
+#define RS_GROUP_TILE 16384
+#endif
+constexpr uint32_t kGroupTile = RS_GROUP_TILE;
+static_assert(kGroupTile >= kGroupSpanMax && (kGroupTile & 15u) == 0, "group tile holds whole spans");
 
 // A copy region: rows x inner bytes.  Row r = i0 + e0*(i1 + e1*i2) starts at
 // src_off + i0*sstr[0] + i1*sstr[1] + i2*sstr[2] (same on the destination

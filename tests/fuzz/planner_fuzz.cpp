@@ -30,6 +30,7 @@ uint64_t g_bucket_regions[4] = {};   // regions replayed, per bucket
 uint64_t g_valid_rejected = 0;       // uncorrupted cases the planner declined (e.g. MXFP8 blocks across sources)
 uint64_t g_sibling_groups = 0;       // thin sibling groups checked
 uint64_t g_two_piece = 0;            // MXFP8 regions with two source pieces replayed
+uint64_t g_group_loads = 0;          // thin sibling groups loaded whole
 
 struct Rng {
   uint64_t s;
@@ -312,17 +313,36 @@ bool run_case(Rng& g, uint64_t c, bool corrupt) {
     std::vector<std::vector<uint8_t>> seen(L.n_regions);
     for (uint32_t k = 0; k < L.n_regions; ++k) {
       const uint32_t nu = (regs[k].rows + regs[k].rows_per_unit - 1) / regs[k].rows_per_unit;
-      seen[k].assign(nu, 0);
       const uint32_t gm = (regs[k].flags >> 16) & 255u, m = regs[k].flags >> 24;
-      if (L.bucket != rs::kThin && gm) die("sibling group outside the thin bucket", c);
-      if (gm == 1 || (gm && m >= gm) || (!gm && m)) die("bad sibling group fields", c);
+      const bool whole = (regs[k].flags & rs::kFlagGroupLoad) != 0;
+      // A group loaded whole: its first member takes all of the group's
+      // units (rows_per_unit rows of every member each), the others none.
+      seen[k].assign(whole && m ? 0 : nu, 0);
+      if (L.bucket != rs::kThin && L.bucket != rs::kThinGroup && gm) die("sibling group outside the thin bucket", c);
+      if ((gm == 1 && !whole) || (gm && m >= gm) || (!gm && m)) die("bad sibling group fields", c);
+      if (whole != (L.bucket == rs::kThinGroup)) die("group-load flag outside its launch kind", c);
+      if (whole && !gm) die("group-load flag outside a sibling group", c);
       if (gm && (k < m || k - m + gm > L.n_regions)) die("sibling group leaves its launch", c);
       if (gm && m == 0) ++g_sibling_groups;
+      if (whole && m == 0) ++g_group_loads;
       if (gm) {
         const rs::CopyRegion& h = regs[k - m];
+        const uint32_t want_ub = whole ? h.unit_begin + (m ? nu : 0) : h.unit_begin + m * nu;
         if (((h.flags >> 16) & 255u) != gm || (h.flags >> 24) != 0 || h.rows != regs[k].rows ||
-            h.rows_per_unit != regs[k].rows_per_unit || h.unit_begin + m * nu != regs[k].unit_begin)
+            h.rows_per_unit != regs[k].rows_per_unit || want_ub != regs[k].unit_begin ||
+            ((h.flags ^ regs[k].flags) & rs::kFlagGroupLoad))
           die("sibling group members differ", c);
+        if (whole) {
+          // The group's column span fits the thin kernel's LDS tile.
+          uint64_t lo = ~uint64_t(0), hi = 0;
+          for (uint32_t q = 0; q < gm; ++q) {
+            lo = std::min<uint64_t>(lo, regs[k - m + q].src_off);
+            hi = std::max<uint64_t>(hi, regs[k - m + q].src_off + regs[k - m + q].inner);
+            if (!(regs[k - m + q].flags & rs::kFlagDstPacked)) die("group-load member not packed", c);
+          }
+          if (hi - lo > rs::kGroupSpanMax || uint64_t(h.rows_per_unit) * (hi - lo) > rs::kGroupTile)
+            die("group-load span exceeds the LDS tile", c);
+        }
       }
     }
     for (uint32_t u = 0; u < L.n_units; ++u) {
@@ -330,7 +350,7 @@ bool run_case(Rng& g, uint64_t c, bool corrupt) {
       while (k + 1 < L.n_regions && regs[k + 1].unit_begin <= u) ++k;
       uint32_t ul = u - regs[k].unit_begin;
       const uint32_t gm = (regs[k].flags >> 16) & 255u;
-      if (gm > 1) {
+      if (gm > 1 && !(regs[k].flags & rs::kFlagGroupLoad)) {
         const uint32_t m = regs[k].flags >> 24;
         const uint32_t nu = (regs[k].rows + regs[k].rows_per_unit - 1) / regs[k].rows_per_unit;
         const uint32_t local = ul + m * nu;
@@ -460,8 +480,8 @@ int main(int argc, char** argv) {
   std::printf("cases %" PRIu64 ": planned and replayed %" PRIu64 ", rejected %" PRIu64
               " (%" PRIu64 " of them uncorrupted, unsupported), corrupted but accepted %" PRIu64
               "; regions replayed: bulk %" PRIu64 ", thin %" PRIu64 ", tiny %" PRIu64 ", mxfp8 %" PRIu64
-              "; thin sibling groups %" PRIu64 "; two-piece MXFP8 regions %" PRIu64 "\n",
+              "; thin sibling groups %" PRIu64 " (loaded whole %" PRIu64 "); two-piece MXFP8 regions %" PRIu64 "\n",
               cases, planned, rejected, g_valid_rejected, corrupt_ok, g_bucket_regions[0],
-              g_bucket_regions[1], g_bucket_regions[2], g_bucket_regions[3], g_sibling_groups, g_two_piece);
+              g_bucket_regions[1], g_bucket_regions[2], g_bucket_regions[3], g_sibling_groups, g_group_loads, g_two_piece);
   return 0;
 }

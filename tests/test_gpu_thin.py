@@ -2,6 +2,9 @@
 oracle, byte for byte: column slabs whose regions read the same source rows
 (groups of 2 to 8 members, several work units each, a partial last unit),
 uneven column splits (members of different widths are not grouped),
+groups loaded whole by one workgroup per row block (contiguous spans, spans
+narrower than the source row, wide spans, several units with a ragged
+tail, replicas without fan-out),
 destination replicas, three-dim tensors with several outer dims, and
 shifted buffers."""
 
@@ -37,6 +40,11 @@ CASES = {
     "cols_2_replicated_3": ([30000, 16], "bf16", ([2], [0]), ([2, 3], [1, -1])),
     "three_dim_outer_dims": ([6, 9000, 8], "f32", ([2], [1]), ([2, 4], [0, 2])),
     "u8_narrow_columns": ([100000, 12], "u8", ([1], [-1]), ([6], [1])),
+    # groups loaded whole: one workgroup reads each block of source rows once
+    "whole_many_units_ragged": ([262144 + 77, 8], "i32", ([2], [0]), ([4], [1])),
+    "whole_partial_span_u8": ([70000, 10], "u8", ([2], [0]), ([3], [1])),
+    "whole_wide_span_bf16": ([20000, 96], "bf16", ([2], [0]), ([16], [1])),
+    "whole_f64_pairs": ([30000, 4], "f64", ([3], [0]), ([2], [1])),
 }
 
 
@@ -50,4 +58,16 @@ def test_thin_sibling_groups(name):
 @pytest.mark.parametrize("shifts", [(4, 0), (0, 8), (3, 5)])
 def test_thin_sibling_groups_shifted(shifts):
     gh.check_against_oracle(_slabs(*CASES["rows_2_to_cols_4"]), src_shift=shifts[0],
+                            dst_shift=shifts[1])
+
+
+def test_thin_group_replicas_without_fanout():
+    """Replicated column slabs planned without fan-out: members of one group
+    read the same columns for different replicas."""
+    gh.check_against_oracle(_slabs([40000, 8], "i32", ([2], [0]), ([4, 2], [1, -1])), fanout=False)
+
+
+@pytest.mark.parametrize("shifts", [(2, 0), (0, 3), (1, 7)])
+def test_thin_group_partial_span_shifted(shifts):
+    gh.check_against_oracle(_slabs(*CASES["whole_partial_span_u8"]), src_shift=shifts[0],
                             dst_shift=shifts[1])

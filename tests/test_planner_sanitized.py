@@ -44,5 +44,7 @@ def test_planner_fuzz_sanitized(fuzz_exe, seed):
     assert "planned and replayed" in r.stdout
     groups = int(r.stdout.split("thin sibling groups")[1].split()[0].rstrip(";"))
     assert groups > 0, r.stdout
+    whole = int(r.stdout.split("loaded whole")[1].split()[0].rstrip(");"))
+    assert whole > 0, r.stdout
     two = int(r.stdout.split("two-piece MXFP8 regions")[1].split()[0])
     assert two > 0, r.stdout
