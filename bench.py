@@ -347,6 +347,24 @@ def secondary(torch, binding, stream):
                            "regions": info["regions"]}
         out[key] = slab
         del srcs, dsts
+    # A large uneven bf16 layout: TP3 -> TP2 over an odd last dim (2,049),
+    # so regions start at source/destination offsets that differ modulo 16
+    # (the misaligned path: funnel-shifted 16-byte loads, aligned stores).
+    t = {"name": "w", "shape": [16, 8193, 2049], "dtype": "bf16", "src": synth.side([3], [2]),
+         "dst": synth.side([2], [2]), "values": {"kind": "normal", "std": 0.02, "seed": 9}}
+    wl = {"name": "uneven_tp3_to_tp2", "buffers": {}, "tensors": [t]}
+    src = device_sources(torch, binding, wl)
+    sp = [x.data_ptr() for tt in src for x in tt]
+    named, dp = device_destinations(torch, binding, wl)
+    plan = plan_of(binding, wl)
+    info = plan.info()
+    ms = time_plan(torch, binding, plan, sp, dp, stream, poison=list(named.values()))
+    nb = info["bytes_read"] + info["bytes_written"]
+    out["uneven_bf16_16x8193x2049_tp3_to_tp2"] = {"ms": round(ms, 4), "GBps": round(nb / ms / 1e6, 1),
+                                                  "bytes": nb, "regions": info["regions"]}
+    plan.destroy()
+    del src, named
+    torch.cuda.empty_cache()
     # Execution time of the uneven layouts (fp32 / bf16 [1000,3000] and
     # [7,513,257], meshes [3] / [2,3] -> [7] / [4,2]); small, cache-resident.
     ex = []

@@ -15,8 +15,9 @@
 //        the vectors of short rows are numbered across the unit so every lane
 //        loads its share in one batch (sub-wave lane groups per row when rows
 //        have several outer dims).  Misaligned regions: each wave copies one
-//        row at the widest granule the source/destination co-alignment
-//        allows, with byte head and tail.
+//        row; once the destination is 16-byte aligned, its 16-byte stores
+//        take bytes from two aligned 16-byte source loads joined by byte
+//        funnel shifts (edges at the widest granule the co-alignment allows).
 //        Launched so that at most five workgroups share a CU (see
 //        bulk_lds_pad): fewer streams concurrently per CU copy faster.
 //  thin  runs shorter than the thin threshold (e.g. the 8-byte rows of a
@@ -240,6 +241,23 @@ __device__ void wave_copy_span(char* d, const char* s, uint64_t n, uint32_t lane
   if (lane < n - done) d[done + lane] = s[done + lane];
 }
 
+// Bytes r .. r + 15 of the 32-byte concatenation A | B (r uniform, < 16).
+template <int Q>
+__device__ __forceinline__ u32x4 funnel_q(u32x4 A, u32x4 B, uint32_t t) {
+  const uint32_t c[8] = {A.x, A.y, A.z, A.w, B.x, B.y, B.z, B.w};
+  return u32x4{__builtin_amdgcn_alignbyte(c[Q + 1], c[Q], t), __builtin_amdgcn_alignbyte(c[Q + 2], c[Q + 1], t),
+               __builtin_amdgcn_alignbyte(c[Q + 3], c[Q + 2], t), __builtin_amdgcn_alignbyte(c[Q + 4], c[Q + 3], t)};
+}
+__device__ __forceinline__ u32x4 funnel16(u32x4 A, u32x4 B, uint32_t r) {
+  const uint32_t t = r & 3u;
+  switch (r >> 2) {
+    case 0: return funnel_q<0>(A, B, t);
+    case 1: return funnel_q<1>(A, B, t);
+    case 2: return funnel_q<2>(A, B, t);
+    default: return funnel_q<3>(A, B, t);
+  }
+}
+
 // The workgroup copies n bytes between two ranges congruent modulo 16.
 __device__ __forceinline__ void block_copy_congruent(char* d, const char* s, uint32_t n, uint32_t tid) {
   uint32_t h = uint32_t((16u - (reinterpret_cast<uintptr_t>(d) & 15u)) & 15u);
@@ -450,6 +468,112 @@ __device__ __forceinline__ void bulk_spread_rows(const LaunchArgs& a, const Copy
   }
 }
 
+// Rows of a misaligned region (source and destination differ modulo 16)
+// into one destination, rows [r0, r1) of n bytes.  Per row, once the
+// destination is 16-byte aligned (hd bytes in), output vector v is bytes
+// r .. r + 15 of the aligned 16-byte source lines L(v) and L(v) + 16 (r =
+// the source's offset in its line, 0 when the row is co-aligned), joined by
+// byte funnel shifts; only vectors whose lines lie inside the row are done
+// so, so no load leaves the row.  The unit's (row, vector) pairs are
+// numbered flat, so every lane has several loads in flight; the row edges
+// (under 32 bytes at the head, 48 at the tail) are one byte per item, loaded
+// in the same batches, before any store.
+struct MisRow {
+  const char* s;
+  char* d;
+  uint32_t hd, r;
+  int lo, hi;        // vectors lo .. hi (none when hi < lo)
+  uint32_t b0, b1;   // edges: bytes [0, b0) and [b1, n)
+};
+
+__device__ __forceinline__ MisRow mis_row(const char* s, char* d, uint32_t n) {
+  MisRow m;
+  m.s = s;
+  m.d = d;
+  m.hd = uint32_t((16u - (reinterpret_cast<uintptr_t>(d) & 15u)) & 15u);
+  m.r = uint32_t((reinterpret_cast<uintptr_t>(s) + m.hd) & 15u);
+  if (m.r == 0) {
+    m.lo = 0;
+    m.hi = n >= m.hd + 16u ? int((n - m.hd) >> 4) - 1 : -1;
+  } else {
+    m.lo = m.hd >= m.r ? 0 : 1;
+    m.hi = n + m.r >= m.hd + 32u ? int((n + m.r - m.hd - 32u) >> 4) : -1;
+  }
+  m.b0 = min(n, m.hd + 16u * uint32_t(m.lo));
+  m.b1 = m.hi >= m.lo ? m.hd + 16u * uint32_t(m.hi + 1) : m.b0;
+  return m;
+}
+
+__device__ __forceinline__ void bulk_misaligned_rows(const char* sp, char* dp, uint32_t r0, uint32_t r1,
+                                                     uint32_t n, uint32_t e0, uint32_t e1, uint32_t nouter,
+                                                     uint64_t s0, uint64_t s1, uint64_t s2,
+                                                     uint64_t d0, uint64_t d1, uint64_t d2) {
+  constexpr int U = 4;          // vector items per lane per batch
+  constexpr int UE = 4;         // edge bytes per lane per batch
+  constexpr uint32_t kEdge = 80;  // edge slots per row: head 0-31, tail 32-79
+  const uint32_t tid = threadIdx.x;
+  const uint32_t nvr = (n + 15u) >> 4;   // vector slots per row
+  const uint32_t rows = r1 - r0;
+  const uint32_t total = rows * nvr, te = rows * kEdge;
+  const uint64_t magic = ((uint64_t(1) << 32) + nvr - 1) / nvr;
+  // Batches: a lane's vector loads and edge-byte loads are all issued
+  // before its stores.
+  const uint32_t nbv = (total + U * kThreads - 1) / (U * kThreads);
+  const uint32_t nbe = (te + UE * kThreads - 1) / (UE * kThreads);
+  const uint32_t nbat = max(nbv, nbe);
+  for (uint32_t bt = 0; bt < nbat; ++bt) {
+    u32x4 A[U], B[U];
+    char* dv[U];
+    uint32_t rr[U];
+    bool ok[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const uint32_t f = (bt * U + k) * kThreads + tid;
+      ok[k] = false;
+      rr[k] = 0;
+      dv[k] = nullptr;
+      if (f < total) {
+        const uint32_t i = uint32_t((uint64_t(f) * magic) >> 32);
+        const int v = int(f - i * nvr);
+        const MisRow m = mis_row(sp + row_off(r0 + i, e0, e1, nouter, s0, s1, s2),
+                                 dp + row_off(r0 + i, e0, e1, nouter, d0, d1, d2), n);
+        if (v >= m.lo && v <= m.hi) {
+          const char* line = m.s + m.hd - m.r + 16u * uint32_t(v);
+          A[k] = *reinterpret_cast<const u32x4*>(line);
+          if (m.r) B[k] = *reinterpret_cast<const u32x4*>(line + 16u);
+          ok[k] = true;
+          rr[k] = m.r;
+          dv[k] = m.d + m.hd + 16u * uint32_t(v);
+        }
+      }
+    }
+    char eb[UE];
+    char* ed[UE];
+#pragma unroll
+    for (int k = 0; k < UE; ++k) {
+      const uint32_t f = (bt * UE + k) * kThreads + tid;
+      ed[k] = nullptr;
+      eb[k] = 0;
+      if (f < te) {
+        const uint32_t i = f / kEdge, e = f - i * kEdge;
+        const MisRow m = mis_row(sp + row_off(r0 + i, e0, e1, nouter, s0, s1, s2),
+                                 dp + row_off(r0 + i, e0, e1, nouter, d0, d1, d2), n);
+        const uint32_t pos = e < 32u ? e : m.b1 + (e - 32u);
+        if (e < 32u ? pos < m.b0 : pos < n) {
+          eb[k] = m.s[pos];
+          ed[k] = m.d + pos;
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k)
+      if (ok[k]) st16(dv[k], rr[k] ? funnel16(A[k], B[k], rr[k]) : A[k]);
+#pragma unroll
+    for (int k = 0; k < UE; ++k)
+      if (ed[k]) *ed[k] = eb[k];
+  }
+}
+
 template <bool kFan1>
 __device__ __forceinline__ void bulk_body(const LaunchArgs& a, const CopyRegion* R, uint32_t unit) {
   const uint32_t tid = threadIdx.x;
@@ -529,15 +653,11 @@ __device__ __forceinline__ void bulk_body(const LaunchArgs& a, const CopyRegion*
       bulk_short_rows<kFan1, 1>(a, R, sp, dp0, dst_off, r0, r1, vpr, L, e0, e1, nouter,
                                 s0, s1, s2, d0, d1, d2, nd);
   } else {
-    // Misaligned: one row per wave at the co-alignment granule.
-    const uint32_t lane = tid & 63u, wave = tid >> 6;
-    for (uint32_t r = r0 + wave; r < r1; r += 4) {
-      const uint64_t so = row_off(r, e0, e1, nouter, s0, s1, s2);
-      const uint64_t dof = row_off(r, e0, e1, nouter, d0, d1, d2);
-      for (uint32_t j = 0; j < nd; ++j) {
-        char* d = static_cast<char*>(a.ptr[dst_pool(R, j)]) + dst_off + dof;
-        wave_copy_span(d, sp + so, inner, lane);
-      }
+    // Misaligned: funnel-shifted 16-byte vectors numbered across the unit,
+    // once per destination (each replica may sit at its own alignment).
+    for (uint32_t j = 0; j < nd; ++j) {
+      char* dp = kFan1 ? dp0 : static_cast<char*>(a.ptr[dst_pool(R, j)]) + dst_off;
+      bulk_misaligned_rows(sp, dp, r0, r1, inner, e0, e1, nouter, s0, s1, s2, d0, d1, d2);
     }
   }
 }

@@ -445,6 +445,9 @@ void merge_outer(Dims& o, bool with_scale) {
 #ifndef RS_THIN_SIBLINGS
 #define RS_THIN_SIBLINGS 1   // group thin regions that read the same source rows
 #endif
+#ifndef RS_FANOUT_UNIT_SHIFT
+#define RS_FANOUT_UNIT_SHIFT 0  // bulk units of regions with several destinations: unit_bytes >> this
+#endif
 #ifndef RS_THIN_GROUP_LOAD
 #define RS_THIN_GROUP_LOAD 1 // load short-span sibling groups whole (one workgroup per row block)
 #endif
@@ -568,17 +571,18 @@ void finalize(Raw r, const Opts& o, std::vector<Raw>& out) {  // r by value: it 
     r.outer.push_back({q, 2 * C, C, sc_step});
     merge_outer(r.outer, true);
   }
-  if (!r.mx && r.inner > o.unit) {
-    const uint64_t q = r.inner / o.unit, rem = r.inner % o.unit;
+  const uint64_t unit = r.n_dst > 1 ? o.unit >> RS_FANOUT_UNIT_SHIFT : o.unit;
+  if (!r.mx && r.inner > unit) {
+    const uint64_t q = r.inner / unit, rem = r.inner % unit;
     if (rem) {
       Raw tail = r;
       tail.inner = rem;
-      tail.src_off += q * o.unit;
-      tail.dst_off += q * o.unit;
+      tail.src_off += q * unit;
+      tail.dst_off += q * unit;
       finalize(std::move(tail), o, out);
     }
-    r.inner = o.unit;
-    r.outer.push_back({q, o.unit, o.unit, 0});
+    r.inner = unit;
+    r.outer.push_back({q, unit, unit, 0});
     merge_outer(r.outer, false);
   }
   const uint64_t rows = rows_of(r.outer);
@@ -1050,7 +1054,7 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
         rpu = std::max<uint64_t>(1, kThinTile / r.inner);
       } else {
         f.bucket = kBulk;
-        rpu = std::max<uint64_t>(1, o.unit / r.inner);
+        rpu = std::max<uint64_t>(1, (nd > 1 ? o.unit >> RS_FANOUT_UNIT_SHIFT : o.unit) / r.inner);
         // Whole spread pieces per unit, where that keeps at least half of it.
         const uint64_t m = kSpreadPiece / std::gcd<uint64_t>(r.inner, kSpreadPiece);
         if (kSpread > 1 && rpu >= m) rpu -= rpu % m;

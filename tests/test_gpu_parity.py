@@ -419,3 +419,31 @@ def test_mxfp8_two_source_blocks_replicated():
     plan = gh.check_against_oracle({"name": "mx_two_rep", "buffers": {}, "tensors": [t]})
     two = [r for r in plan.regions() if r["split"] < r["inner"]]
     assert two and all(len(r["dst_index"]) == 2 for r in two)
+
+
+MISALIGNED_LONG = {
+    # TP3 -> TP2 over an odd bf16 width: rows of 683 / 342 / 341 elements at
+    # source and destination offsets that differ modulo 16
+    "bf16_tp3_to_tp2_2049": ([6, 300, 2049], "bf16", ([3], [2]), ([2], [2])),
+    "bf16_rows_to_cols_4097": ([40, 4097], "bf16", ([3], [0]), ([3], [1])),
+    "u8_odd_widths": ([33, 3001], "u8", ([7], [1]), ([2, 2], [1, -1])),
+    "f32_tp5_to_tp3": ([64, 1001], "f32", ([5], [1]), ([3], [1])),
+}
+
+
+@pytest.mark.parametrize("shifts", [(0, 0), (2, 0), (0, 6), (10, 4), (1, 3)])
+@pytest.mark.parametrize("name", sorted(MISALIGNED_LONG))
+def test_misaligned_long_rows(name, shifts):
+    """Rows whose source and destination differ modulo 16 (odd splits, and
+    buffers shifted by a few bytes): 16-byte stores fed by funnel-shifted
+    pairs of aligned loads, edges by granules."""
+    shape, dtype, src, dst = MISALIGNED_LONG[name]
+    if dtype != "u8" and (shifts[0] % 2 or shifts[1] % 2):
+        shifts = (shifts[0] & ~1, shifts[1] & ~1)
+    if dtype == "f32":
+        shifts = (shifts[0] & ~3, shifts[1] & ~3)
+    vals = {"kind": "uniform", "seed": 5} if dtype in ("f32", "bf16") else {"kind": "index"}
+    t = {"name": "w", "shape": shape, "dtype": dtype, "src": synth.side(*src), "dst": synth.side(*dst),
+         "values": vals}
+    gh.check_against_oracle({"name": "mis_" + name, "buffers": {}, "tensors": [t]},
+                            src_shift=shifts[0], dst_shift=shifts[1], tiny_bytes=0, thin_bytes=1)
