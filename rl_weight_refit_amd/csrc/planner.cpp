@@ -1154,6 +1154,7 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
     const uint32_t bucket = pass < kBuckets ? pass : uint32_t(kThin);
     const uint32_t kernel = pass < kBuckets ? pass : uint32_t(kThinGroup);
     std::vector<const Final*> list;
+    list.reserve(fin.size());
     for (size_t q = 0; q < fin.size(); ++q)
       if (fin[q].bucket == bucket && (bucket != kThin || whole[q] == (pass == kBuckets)))
         list.push_back(&fin[q]);
@@ -1162,6 +1163,8 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
       // Greedy group: regions in order while their pointers fit the pool.
       std::vector<uint32_t> members;    // pool slot -> caller pointer index (| kDstBit)
       std::vector<const Final*> batch;
+      members.reserve(kPool);
+      batch.reserve(list.size() - i);
       uint64_t units = 0;
       while (i < list.size()) {
         const Final* f = list[i];
@@ -1211,6 +1214,7 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
       out.image.resize(out.image.size() + rsz * batch.size(), 0);
       uint32_t ub = 0;
       std::vector<uint32_t> unit_region;
+      unit_region.reserve(2 + (units >> kChunkShift));
       // Thin sibling groups: consecutive thin regions that read the same
       // source rows (same source buffer, outer dims and row count, column
       // offsets within one source row) take their units interleaved in the
