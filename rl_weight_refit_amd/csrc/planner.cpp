@@ -29,6 +29,7 @@
 
 #include <algorithm>
 #include <chrono>
+#include <cstdlib>
 #include <cstring>
 #include <numeric>
 #include <sstream>
@@ -374,14 +375,22 @@ bool same_view(const rs_view& a, const rs_view& b, int ndim) {
 // A region before it is split to fit the kernels.
 struct Dim {
   uint64_t ext, ss, ds, sc;  // extent; byte strides on src, dst, scale sides
-  uint64_t ss2 = 0;          // source stride of a two-piece MXFP8 region's second piece
+  uint64_t ss2;              // source stride of a two-piece MXFP8 region's second piece (0: none)
 };
 
-// Outer dims, outermost first (fixed capacity: tensor rank + one split).
-struct Dims {
-  Dim d[RS_MAX_DIMS + 1];
+// Outer dims, outermost first.  A region keeps at most 3 outer dims plus
+// one that finalize adds while cutting long rows (regions are peeled to that
+// when they are built); WideDims holds the up to rank + 1 dims of a region
+// being built.
+template <int Cap>
+struct DimsT {
+  Dim d[Cap];
   int n = 0;
-  void push_back(const Dim& x) { d[n++] = x; }
+  DimsT() {}  // entries past n stay unset
+  void push_back(const Dim& x) {
+    if (n == Cap) std::abort();  // unreachable: regions are peeled before they grow past Cap
+    d[n++] = x;
+  }
   void pop_back() { --n; }
   Dim& back() { return d[n - 1]; }
   Dim& front() { return d[0]; }
@@ -390,8 +399,14 @@ struct Dims {
   const Dim* begin() const { return d; }
   const Dim* end() const { return d + n; }
 };
+using Dims = DimsT<4>;
+using WideDims = DimsT<RS_MAX_DIMS + 1>;
 
 struct Raw {
+  // Fields without initializers are set where a region is built; a Raw is
+  // a few hundred bytes, so value-initializing each one would cost more
+  // than the planning it takes part in.
+  Raw() {}
   uint32_t tensor;
   bool mx;
   uint32_t src_index;
@@ -421,8 +436,9 @@ uint64_t rows_of(const Dims& o) {
 }
 
 // Merge mergeable adjacent outer dims; drop extent-1 dims.
-void merge_outer(Dims& o, bool with_scale) {
-  Dims m;
+template <int Cap>
+void merge_outer(DimsT<Cap>& o, bool with_scale) {
+  DimsT<Cap> m;
   for (const Dim& d : o) {
     if (d.ext == 1) continue;
     if (!m.empty()) {
@@ -626,6 +642,44 @@ void finalize(Raw r, const Opts& o, std::vector<Raw>& out) {  // r by value: it 
   out.push_back(std::move(r));
 }
 
+// True when finalize would keep r exactly as it is (the common case), so
+// the caller can use it in place instead of copying it.
+bool final_as_is(const Raw& r, const Opts& o) {
+  if (r.mx && r.inner > kMxBatchElems) return false;
+  if (!r.mx && r.inner > (r.n_dst > 1 ? o.unit >> RS_FANOUT_UNIT_SHIFT : o.unit)) return false;
+  const uint64_t rows = rows_of(r.outer);
+  if (rows == 0 || r.inner == 0 || rows > kMaxRows || r.outer.size() > 3) return false;
+  for (const Dim& d : r.outer)
+    if (d.ext > 0xFFFFFFFFull) return false;
+  return true;
+}
+
+// finalize without copying r where that is possible: returns true when r
+// itself (possibly cut to unit-sized rows in place) is final and comes
+// after the pieces appended to out; false when out holds all of r's pieces.
+bool finalize_at(Raw& r, const Opts& o, std::vector<Raw>& out) {
+  if (final_as_is(r, o)) return true;
+  const uint64_t unit = r.n_dst > 1 ? o.unit >> RS_FANOUT_UNIT_SHIFT : o.unit;
+  if (!r.mx && r.inner > unit && r.outer.size() < 3) {
+    const uint64_t q = r.inner / unit, rem = r.inner % unit;
+    if (rem) {
+      Raw tail = r;
+      tail.inner = rem;
+      tail.src_off += q * unit;
+      tail.dst_off += q * unit;
+      finalize(std::move(tail), o, out);
+    }
+    r.inner = unit;
+    r.outer.push_back({q, unit, unit, 0});
+    merge_outer(r.outer, false);
+    if (final_as_is(r, o)) return true;
+    finalize(r, o, out);
+    return false;
+  }
+  finalize(r, o, out);
+  return false;
+}
+
 struct Final {
   const Raw* rp;
   uint32_t bucket;
@@ -688,6 +742,43 @@ rs_status shard_box(const rs_tensor_desc* d, int64_t slot, int64_t* off, int64_t
     len[i] = b[i].len;
   }
   return RS_OK;
+}
+
+// Gives the region just built (raws.back()) the outer dims w.  A region
+// with more than 3 is replaced by one region per index of its outermost
+// dims (as finalize would peel it), so a Raw never holds more than 3 dims
+// from here on.
+void peel_into(std::vector<Raw>& raws, const Raw& proto, const WideDims& w, int k) {
+  if (w.n - k <= 3) {
+    Raw& r = raws.emplace_back(proto);
+    r.outer.n = 0;
+    for (int i = k; i < w.n; ++i) r.outer.push_back(w.d[i]);
+    return;
+  }
+  const Dim& top = w.d[k];
+  for (uint64_t i = 0; i < top.ext; ++i) {
+    Raw s = proto;
+    s.src_off += i * top.ss;
+    s.dst_off += i * top.ds;
+    if (s.mx) {  // MXFP8 pieces: row offsets on the element and scale sides
+      s.drow += i * top.ds;
+      s.srow += i * top.sc;
+    } else {
+      s.sc_off += i * top.sc;
+    }
+    peel_into(raws, s, w, k + 1);
+  }
+}
+void set_outer(std::vector<Raw>& raws, const WideDims& w) {
+  Raw& r = raws.back();
+  if (w.n <= 3) {
+    r.outer.n = 0;
+    for (int i = 0; i < w.n; ++i) r.outer.push_back(w.d[i]);
+    return;
+  }
+  const Raw proto = r;
+  raws.pop_back();
+  peel_into(raws, proto, w, 0);
 }
 
 rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32_t n,
@@ -842,6 +933,7 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
     std::vector<uint8_t> done;
     std::vector<size_t> grp;
     std::vector<Raw> raws, split;
+    std::vector<uint32_t> cut;
   };
   thread_local Scratch scratch;
   std::vector<Target>& targets = scratch.targets;
@@ -923,7 +1015,7 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
             ln[0] = 1;
           }
           const int64_t s0 = st[0] - sb[0].start, d0 = st[0] - db[0].start;
-          Raw r;
+          Raw& r = raws.emplace_back();  // built in place: a Raw is a few hundred bytes
           r.tensor = t;
           r.mx = mx;
           r.src_index = uint32_t(src_base[t] + (A.split ? A.ptr_base[ss] + s0 : ss));
@@ -946,7 +1038,7 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
             r.sc_inner = 0;
             // Element size folds into the innermost run; runs grow while both
             // sides stay contiguous.
-            Dims keep;
+            WideDims keep;
             for (int dd = 0; dd < nd; ++dd)
               if (ln[dd] != 1)
                 keep.push_back({uint64_t(ln[dd]), uint64_t(sv.strides[dd]) * es,
@@ -957,8 +1049,8 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
               keep.pop_back();
             }
             r.inner = run;
-            r.outer = keep;
-            merge_outer(r.outer, false);
+            merge_outer(keep, false);
+            set_outer(raws, keep);
           } else {
             const rs_view& cv = B.scale_views[ds0];
             const int last = nd - 1;
@@ -982,11 +1074,15 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
             r.kloc = uint64_t(db[last].len);
             r.drow = uint64_t(dof - c0);
             r.srow = uint64_t(sco);
+            // Extent-1 dims dropped, nothing merged: the pieces of one row
+            // box (same rows, other sources) must keep the same dims.
+            WideDims w;
             for (int dd = 0; dd < last; ++dd)
-              r.outer.push_back({uint64_t(ln[dd]), uint64_t(sv.strides[dd]) * 2,
-                                 uint64_t(dv.strides[dd]), uint64_t(cv.strides[dd])});
+              if (ln[dd] != 1)
+                w.push_back({uint64_t(ln[dd]), uint64_t(sv.strides[dd]) * 2,
+                             uint64_t(dv.strides[dd]), uint64_t(cv.strides[dd])});
+            set_outer(raws, w);
           }
-          raws.push_back(std::move(r));
         }
       }
       int dd = nd - 1;
@@ -1014,15 +1110,22 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
 
   // ---- step 4: split, bucket, size work units ------------------------------
   std::vector<Raw>& split = scratch.split;
+  std::vector<uint32_t>& cut = scratch.cut;
   split.clear();
-  for (Raw& r : raws) finalize(r, o, split);
-  raws.clear();
+  cut.resize(raws.size());
+  // Regions the kernels take as they are (or once cut to unit-sized rows)
+  // stay in raws; the pieces of the others go to `split`.  cut[i]: end of
+  // raw i's pieces in split, top bit set when raws[i] itself follows them.
+  for (size_t i = 0; i < raws.size(); ++i) {
+    const bool kept = finalize_at(raws[i], o, split);
+    cut[i] = uint32_t(split.size()) | (kept ? 0x80000000u : 0u);
+  }
 
   thread_local std::vector<Final> fin;
   fin.clear();
-  fin.reserve(split.size());
+  fin.reserve(raws.size() + split.size());
   uint64_t bytes_read = 0, bytes_written = 0, bytes_nofan = 0;
-  for (const Raw& r : split) {
+  auto add_final = [&](const Raw& r) {
     Final f;
     f.rp = &r;
     f.rows = rows_of(r.outer);
@@ -1092,6 +1195,10 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
       }
     }
     fin.push_back(f);
+  };
+  for (size_t i = 0, sp = 0; i < raws.size(); ++i) {
+    for (; sp < (cut[i] & 0x7FFFFFFFu); ++sp) add_final(split[sp]);
+    if (cut[i] >> 31) add_final(raws[i]);
   }
 
   // ---- device image: per bucket, launch groups bounded by the pointer pool --

@@ -139,3 +139,59 @@ def golden_workload(workload, poison=0xA5, globals_=None):
 def local_arrays(tensor, G, side_name):
     desc = src_desc_for(tensor) if side_name == "src" else odesc(tensor, side_name)
     return [np.ascontiguousarray(G[ogolden.box_slices(b)]) for b in olayout.slot_boxes(desc)]
+
+
+def high_rank_case(seed, mx=False):
+    """A rank 4-6 tensor over tiny meshes whose slots (either side, at
+    random) are padded views into shared buffers, so outer dims do not merge
+    and regions keep more than three of them (the planner peels those).
+    MXFP8 destinations keep the last dim contiguous; their scale views are
+    padded the same way."""
+    rng = np.random.Generator(np.random.PCG64(77_000 + seed))
+    ndim = int(rng.integers(4, 7))
+    shape = [int(rng.integers(1, 5)) if rng.random() < 0.3 else int(rng.integers(2, 4))
+             for _ in range(ndim)]
+    if mx:
+        shape[-1] = int(rng.integers(20, 90))
+    dtype = "bf16" if mx else ["i32", "bf16", "u8"][int(rng.integers(3))]
+    buffers = {}
+    sides = {}
+    for name in ("src", "dst"):
+        mesh = synth.TINY_MESHES[int(rng.integers(len(synth.TINY_MESHES)))]
+        # MXFP8: sources are not cut along the last dim (blocks from several
+        # sources are covered by tests of their own)
+        top = ndim - 1 if (mx and name == "src") else ndim
+        pl = [int(rng.integers(-1, top)) for _ in mesh]
+        sd = synth.side(mesh, pl)
+        quant = "mxfp8" if (mx and name == "dst") else None
+        sd["quant"] = quant
+        if rng.random() < 0.8:
+            desc = {"shape": shape, "dtype": dtype, "mesh": mesh, "placements": pl,
+                    "slot_of_coord": None, "quant": quant}
+            slots, sslots = [], []
+            for k, (_, ln) in enumerate(olayout.slot_boxes(desc)):
+                for kind, last in (("e", ln[-1]), ("s", -(-ln[-1] // 32))):
+                    if kind == "s" and not quant:
+                        continue
+                    dims = list(ln[:-1]) + [last]
+                    pad = [int(rng.integers(1, 3)) for _ in dims]
+                    pad[-1] = 0 if mx else pad[-1]   # MXFP8: contiguous last dim
+                    st, acc = [], 1
+                    for n, p in zip(reversed(dims), reversed(pad)):
+                        st.append(acc)
+                        acc *= max(n + p, 1)
+                    st = list(reversed(st))
+                    base = int(rng.integers(0, 5))
+                    key = "%s%s%d" % (name, kind, k)
+                    bdt = "u8" if (quant or kind == "s") else dtype
+                    buffers[key] = {"dtype": bdt, "elems": base + acc}
+                    (slots if kind == "e" else sslots).append({"buf": key, "view": (base, st)})
+            sd["slots"] = slots
+            if quant:
+                sd["scale_slots"] = sslots
+        sides[name] = sd
+    return {"name": "high_rank_%d" % seed, "buffers": buffers,
+            "tensors": [{"name": "t", "shape": shape, "dtype": dtype, "src": sides["src"],
+                         "dst": sides["dst"],
+                         "values": {"kind": "normal", "std": 1.0, "seed": seed} if mx
+                         else {"kind": "index"}}]}

@@ -505,3 +505,44 @@ def test_permuted_rank_grid_fixture():
         assert binding.reshard_shard_box(sp, k) == (off, ln)
     for as_source in (False, True):
         run_interpreted(tl.grid_workload(as_source))
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_interpreted_high_rank(seed):
+    """Ranks 4-6 with padded views: regions with more than three outer dims
+    are peeled into regions the kernels take; bytes match the oracle and
+    every destination byte is written once."""
+    wl = helpers.high_rank_case(seed)
+    plan, dst_flat, count = run_interpreted(wl)
+    for c in counts_by_buffer(dst_flat, count).values():
+        assert c.max(initial=0) <= 1
+    for r in plan.regions():
+        assert len([e for e in r["ext"] if e > 1]) <= 3
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_interpreted_high_rank_mxfp8(seed):
+    run_interpreted(helpers.high_rank_case(seed, mx=True))
+
+
+def _box_pairs(t):
+    """Overlapping (distinct source box, destination slot) pairs."""
+    sb = {tuple(map(tuple, b)) for b in olayout.slot_boxes(helpers.src_desc_for(t))}
+    n = 0
+    for so, sl in sb:
+        for do, dl in olayout.slot_boxes(helpers.odesc(t, "dst")):
+            n += all(max(a, c) < min(a + b, c + d) for a, b, c, d in zip(so, sl, do, dl))
+    return n
+
+
+@pytest.mark.parametrize("mx", [False, True])
+def test_high_rank_cases_peel(mx):
+    """The high-rank cases reach regions with more than three outer dims
+    (so the peel is exercised): planned without fan-out, a plan with more
+    regions than overlapping box pairs has peeled some."""
+    peeled = 0
+    for seed in range(40 if mx else 60):
+        wl = helpers.high_rank_case(seed, mx=mx)
+        plan = lh.plan_workload(wl, fanout=False)
+        peeled += plan.info()["n_regions"] > _box_pairs(wl["tensors"][0])
+    assert peeled >= 10
