@@ -2,8 +2,8 @@
 byte for byte, on every workload family at sizes the oracle finishes in
 seconds: the pages' worked example, 200 tiny random layouts, the 500 uneven
 layouts with their A -> B -> A round trips, fused dense and MoE layers
-(ragged variants included), the MXFP8 install, misaligned pointers and every
-kernel bucket forced on its own.  Destinations start poisoned, with guard
+(ragged variants included), the MXFP8 install, misaligned pointers, rank 4-6
+layouts with padded views, and every kernel bucket forced on its own.  Destinations start poisoned, with guard
 bytes after each buffer; sources must come back unchanged.
 """
 
@@ -447,3 +447,17 @@ def test_misaligned_long_rows(name, shifts):
          "values": vals}
     gh.check_against_oracle({"name": "mis_" + name, "buffers": {}, "tensors": [t]},
                             src_shift=shifts[0], dst_shift=shifts[1], tiny_bytes=0, thin_bytes=1)
+
+
+@pytest.mark.parametrize("seed", range(0, 60, 3))
+def test_high_rank_layouts(seed):
+    """Ranks 4-6 with padded views (regions with more than three outer dims
+    are peeled by the planner)."""
+    gh.log("high rank %d" % seed)
+    gh.check_against_oracle(helpers.high_rank_case(seed))
+
+
+@pytest.mark.parametrize("seed", range(0, 40, 2))
+def test_high_rank_mxfp8(seed):
+    gh.log("high rank mxfp8 %d" % seed)
+    gh.check_against_oracle(helpers.high_rank_case(seed, mx=True))
