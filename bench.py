@@ -250,6 +250,21 @@ def time_plan(torch, binding, plan, src_ptrs, dst_ptrs, stream, reps=10, poison=
     return statistics.median(a.elapsed_time(b) for a, b in evs)
 
 
+def time_back_to_back(torch, binding, plan, src_ptrs, dst_ptrs, stream, reps=20):
+    """Mean time of `reps` executes enqueued back to back between two events
+    (ms): the steady state, where every execute also pays for the write-backs
+    the previous one left in the caches."""
+    for _ in range(2):
+        binding.reshard_execute(plan, src_ptrs, dst_ptrs, stream.cuda_stream)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        binding.reshard_execute(plan, src_ptrs, dst_ptrs, stream.cuda_stream)
+    b.record(stream)
+    stream.synchronize()
+    return a.elapsed_time(b) / reps
+
+
 def secondary(torch, binding, stream):
     """Other layer-sized layouts and the kernels' special paths, measured
     after the timed region (not part of `value`)."""
@@ -263,11 +278,13 @@ def secondary(torch, binding, stream):
         plan = plan_of(binding, wl)
         info = plan.info()
         ms = time_plan(torch, binding, plan, sp, dp, stream, poison=list(named.values()))
+        bb = time_back_to_back(torch, binding, plan, sp, dp, stream)
         nb = info["bytes_read"] + info["bytes_written"]
         nbf = info["bytes_read_no_fanout"] + info["bytes_written"]
         out[name] = {"ms": round(ms, 4), "GBps": round(nb / ms / 1e6, 1), "bytes": nb,
                      "bytes_no_fanout": nbf, "GBps_no_fanout_credit": round(nbf / ms / 1e6, 1),
-                     "regions": info["n_regions"]}
+                     "regions": info["n_regions"], "ms_back_to_back": round(bb, 4),
+                     "GBps_back_to_back": round(nb / bb / 1e6, 1)}
         del src, named
     # The DSV3 layer with every source expert in a buffer of its own (no
     # stacking copy on the training side): 768 source pointers.
@@ -345,6 +362,10 @@ def secondary(torch, binding, stream):
             nb = info["bytes_read"] + info["bytes_written"]
             slab[label] = {"ms": round(ms, 4), "GBps": round(nb / ms / 1e6, 1),
                            "regions": info["regions"]}
+            if label == "lds_thin_kernel":
+                bb = time_back_to_back(torch, binding, plan, sp, dp, stream)
+                slab[label].update(ms_back_to_back=round(bb, 4),
+                                   GBps_back_to_back=round(nb / bb / 1e6, 1))
         out[key] = slab
         del srcs, dsts
     # A large uneven bf16 layout: TP3 -> TP2 over an odd last dim (2,049),
