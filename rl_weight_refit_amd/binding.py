@@ -15,6 +15,7 @@ A side description is a dict:
   scale_of of the same plan).
 """
 
+import array
 import ctypes
 import os
 
@@ -251,10 +252,14 @@ def reshard_plan(src_specs, dst_specs, fanout=True, unit_bytes=16384, tiny_bytes
 
 
 def _ptr_array(ptrs):
-    arr = (ctypes.c_void_p * max(len(ptrs), 1))()
-    for i, p in enumerate(ptrs):
-        arr[i] = int(p) if p else None
-    return arr
+    """(keep-alive buffer, void** view) of a pointer list (None or 0 = NULL)."""
+    try:
+        buf = array.array("Q", ptrs)
+    except TypeError:
+        buf = array.array("Q", [int(p) if p else 0 for p in ptrs])
+    if not buf:
+        buf = array.array("Q", [0])
+    return buf, ctypes.cast(buf.buffer_info()[0], ctypes.POINTER(ctypes.c_void_p))
 
 
 def reshard_execute(plan, src_ptrs, dst_ptrs, stream=None):
@@ -263,8 +268,8 @@ def reshard_execute(plan, src_ptrs, dst_ptrs, stream=None):
     if len(src_ptrs) != plan.n_src_ptrs or len(dst_ptrs) != plan.n_dst_ptrs:
         raise ValueError("the plan takes %d source and %d destination pointers, got %d and %d"
                          % (plan.n_src_ptrs, plan.n_dst_ptrs, len(src_ptrs), len(dst_ptrs)))
-    s = _ptr_array(src_ptrs)
-    d = _ptr_array(dst_ptrs)
+    s_keep, s = _ptr_array(src_ptrs)
+    d_keep, d = _ptr_array(dst_ptrs)
     _check(load().reshard_execute(plan.handle, s, d, ctypes.c_void_p(stream or 0)))
 
 
@@ -275,8 +280,8 @@ def reshard_execute_no_alloc(plan, src_ptrs, dst_ptrs, stream=None):
     if len(src_ptrs) != plan.n_src_ptrs or len(dst_ptrs) != plan.n_dst_ptrs:
         raise ValueError("the plan takes %d source and %d destination pointers, got %d and %d"
                          % (plan.n_src_ptrs, plan.n_dst_ptrs, len(src_ptrs), len(dst_ptrs)))
-    s = _ptr_array(src_ptrs)
-    d = _ptr_array(dst_ptrs)
+    s_keep, s = _ptr_array(src_ptrs)
+    d_keep, d = _ptr_array(dst_ptrs)
     _check(load().reshard_execute_no_alloc(plan.handle, s, d, ctypes.c_void_p(stream or 0)))
 
 
