@@ -195,3 +195,80 @@ def high_rank_case(seed, mx=False):
                          "dst": sides["dst"],
                          "values": {"kind": "normal", "std": 1.0, "seed": seed} if mx
                          else {"kind": "index"}}]}
+
+
+def random_plan_case(seed):
+    """A seeded random plan: 1 to 3 tensors in one plan (so launches share
+    the pointer pool and several buckets run in one execute), ranks 1-4,
+    u8 / bf16 / i32 / f64, 4 KB to 3 MB each, meshes of 1-2 dims with 1-4
+    slots per dim, Shard / Replicate placements, sides held as padded views
+    into shared buffers at random, a fifth of the tensors installed as MXFP8;
+    random planning options (fan-out, unit, tiny and thin thresholds) and
+    pointer offsets.  Returns (workload, plan options, (src_shift,
+    dst_shift))."""
+    rng = np.random.Generator(np.random.PCG64(90_000 + seed))
+    buffers, tensors = {}, []
+    any_mx = False
+    for ti in range(int(rng.integers(1, 4))):
+        mx = rng.random() < 0.2
+        ndim = int(rng.integers(2 if mx else 1, 5))
+        dtype = "bf16" if mx else ["u8", "bf16", "i32", "f64"][int(rng.integers(4))]
+        es = synth.ELEM_BYTES[dtype]
+        last_bytes = int(rng.choice([2, 8, 24, 64, 130, 512, 1030, 4096, 9000, 20000]))
+        last = max(1, last_bytes // es)
+        if mx:
+            last = max(last, int(rng.integers(20, 300)))
+        total = int(rng.integers(4096, 3 << 20)) // es
+        rest = max(1, total // last)
+        shape = [last]
+        for _ in range(ndim - 2):
+            k = int(rng.integers(1, 6))
+            shape.insert(0, k)
+            rest = max(1, rest // k)
+        if ndim >= 2:
+            shape.insert(0, rest)
+        sides = {}
+        for name in ("src", "dst"):
+            mesh = [int(rng.integers(1, 5)) for _ in range(int(rng.integers(1, 3)))]
+            top = ndim - 1 if (mx and name == "src") else ndim
+            pl = [int(rng.integers(-1, top)) for _ in mesh]
+            quant = "mxfp8" if (mx and name == "dst") else None
+            sd = synth.side(mesh, pl, quant=quant)
+            if rng.random() < 0.3:
+                desc = {"shape": shape, "dtype": "u8" if quant else dtype, "mesh": mesh,
+                        "placements": pl, "slot_of_coord": None, "quant": quant}
+                slots, sslots = [], []
+                for k, (_, ln) in enumerate(olayout.slot_boxes(desc)):
+                    for kind, lastn in (("e", ln[-1]), ("s", -(-ln[-1] // 32))):
+                        if kind == "s" and not quant:
+                            continue
+                        dims = list(ln[:-1]) + [lastn]
+                        pad = [int(rng.integers(0, 3)) for _ in dims]
+                        if mx:
+                            pad[-1] = 0
+                        st, acc = [], 1
+                        for n, p in zip(reversed(dims), reversed(pad)):
+                            st.append(acc)
+                            acc *= max(n + p, 1)
+                        st = list(reversed(st))
+                        base = int(rng.integers(0, 9))
+                        key = "t%d%s%s%d" % (ti, name, kind, k)
+                        buffers[key] = {"dtype": "u8" if (quant or kind == "s") else dtype,
+                                        "elems": base + acc}
+                        (slots if kind == "e" else sslots).append({"buf": key, "view": (base, st)})
+                sd["slots"] = slots
+                if quant:
+                    sd["scale_slots"] = sslots
+            sides[name] = sd
+        any_mx |= mx
+        vals = {"kind": "normal", "std": 1.0, "seed": seed * 10 + ti} if dtype == "bf16" else \
+            {"kind": "index"}
+        tensors.append({"name": "t%d" % ti, "shape": shape, "dtype": dtype, "src": sides["src"],
+                        "dst": sides["dst"], "values": vals})
+    opts = {"fanout": bool(rng.random() < 0.8),
+            "unit_bytes": int(rng.choice([4096, 8192, 16384, 65536])),
+            "tiny_bytes": int(rng.choice([0, 256, 1024, 4096])),
+            "thin_bytes": int(rng.choice([1, 64, 128, 512, 2048]))}
+    shifts = [int(rng.choice([0, 0, 2, 6, 8, 10])) for _ in range(2)]
+    return ({"name": "random_plan_%d" % seed, "buffers": buffers, "tensors": tensors}, opts,
+            tuple(shifts))

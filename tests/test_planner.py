@@ -546,3 +546,13 @@ def test_high_rank_cases_peel(mx):
         plan = lh.plan_workload(wl, fanout=False)
         peeled += plan.info()["n_regions"] > _box_pairs(wl["tensors"][0])
     assert peeled >= 10
+
+
+@pytest.mark.parametrize("seed", range(0, 150, 3))
+def test_interpreted_random_plans(seed):
+    """Random multi-tensor plans with random options (helpers.random_plan_case),
+    interpreted on the host against the oracle."""
+    wl, opts, _ = helpers.random_plan_case(seed)
+    plan, dst_flat, count = run_interpreted(wl, **opts)
+    for c in counts_by_buffer(dst_flat, count).values():
+        assert c.max(initial=0) <= 1
