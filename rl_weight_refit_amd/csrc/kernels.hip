@@ -119,6 +119,16 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) {
 #ifndef RS_THIN_LDS_AUX
 #define RS_THIN_LDS_AUX 2      // cache policy of those direct-to-LDS loads (2: non-temporal)
 #endif
+#ifndef RS_MIS_LDS
+#define RS_MIS_LDS 1           // bulk kernel: misaligned rows staged through LDS where they fit
+#endif
+#ifndef RS_MIS_LDS_AUX
+#define RS_MIS_LDS_AUX 2       // cache policy of those direct-to-LDS loads (2: non-temporal)
+#endif
+// Static LDS of the bulk kernel for misaligned rows: a 16 KiB unit of rows of
+// at least 512 bytes needs at most 16384 + 31 * 32 bytes (a row slot is
+// ceil(row / 16) + 1 lines: at most 31 bytes beyond the row's own).
+constexpr uint32_t kMisTile = RS_MIS_LDS ? 17408u : 16u;
 #ifndef RS_THIN_GROUP_BATCH
 #define RS_THIN_GROUP_BATCH 1  // group-loaded thin units: a lane's loads all in flight before LDS writes
 #endif
@@ -574,8 +584,112 @@ __device__ __forceinline__ void bulk_misaligned_rows(const char* sp, char* dp, u
   }
 }
 
+// Misaligned rows staged through LDS (rows of at least kMisMinRow bytes
+// whose unit fits the bulk kernel's kMisTile staging area; replicas at one
+// alignment).  Row i of the unit takes LDS slot i (lm 16-byte lines): row
+// byte x at slot byte h_i + x, h_i = source address mod 16.  Source lines
+// wholly inside a row cover its bytes [f0, f1); the row's 16-byte-aligned
+// destination blocks inside that span cover [e0, e1).
+//   Phase 1: the whole lines go straight into LDS with direct-to-LDS
+//   16-byte loads, and the bytes of the partial first and last lines
+//   ([0, f0) and [f1, n), under 16 each) into registers, all before one
+//   wait, so no load leaves the row.
+//   Phase 2, per destination: each block is two aligned LDS reads joined by
+//   a funnel shift and one 16-byte store; the edge bytes [0, e0) and
+//   [e1, n) come from the registers or, inside [f0, f1), from LDS.
+constexpr uint32_t kMisMinRow = 512;
+constexpr int kMisEdge = 4;   // edge bytes per lane and source: 32 per row, rows * 32 <= kMisEdge * kThreads
+
+struct MisSpan {
+  uint32_t h, f0, f1, e0, e1;
+};
+__device__ __forceinline__ MisSpan mis_span(const char* src, const char* dst, uint32_t n) {
+  MisSpan m;
+  m.h = uint32_t(reinterpret_cast<uintptr_t>(src) & 15u);
+  m.f0 = (16u - m.h) & 15u;
+  m.f1 = n >= m.f0 + 16u ? m.f0 + ((n - m.f0) & ~15u) : m.f0;
+  const uint32_t y0 = (16u - uint32_t(reinterpret_cast<uintptr_t>(dst) & 15u)) & 15u;  // first block start
+  m.e0 = m.f0 + ((y0 - m.f0) & 15u);
+  m.e1 = m.f1 >= m.e0 + 16u ? m.e0 + ((m.f1 - m.e0) & ~15u) : m.e0;
+  return m;
+}
+
 template <bool kFan1>
-__device__ __forceinline__ void bulk_body(const LaunchArgs& a, const CopyRegion* R, uint32_t unit) {
+__device__ __forceinline__ void bulk_misaligned_lds(const LaunchArgs& a, const CopyRegion* R, const char* sp,
+                                                    char* dp0, uint64_t dst_off, uint32_t r0, uint32_t rows,
+                                                    uint32_t n, uint32_t lm, uint32_t e0, uint32_t e1,
+                                                    uint32_t nouter, uint64_t s0, uint64_t s1, uint64_t s2,
+                                                    uint64_t d0, uint64_t d1, uint64_t d2, uint32_t nd,
+                                                    char* lds) {
+  const uint32_t tid = threadIdx.x;
+  // Phase 1: partial-line bytes into registers (edge slot e < 16: row byte
+  // e; e >= 16: row byte f1 + e - 16), whole lines into LDS.
+  char eb[kMisEdge];
+#pragma unroll
+  for (int k = 0; k < kMisEdge; ++k) {
+    const uint32_t f = uint32_t(k) * kThreads + tid;
+    eb[k] = 0;
+    if (f < rows * 32u) {
+      const uint32_t i = f >> 5, e = f & 31u;
+      const char* src = sp + row_off(r0 + i, e0, e1, nouter, s0, s1, s2);
+      const uint32_t h = uint32_t(reinterpret_cast<uintptr_t>(src) & 15u), f0 = (16u - h) & 15u;
+      const uint32_t f1 = n >= f0 + 16u ? f0 + ((n - f0) & ~15u) : f0;
+      const uint32_t pos = e < 16u ? e : f1 + (e - 16u);
+      if (e < 16u ? pos < f0 : pos < n) eb[k] = src[pos];
+    }
+  }
+  const uint32_t slots = rows * lm;
+  const uint64_t mag = ((uint64_t(1) << 32) + lm - 1) / lm;   // exact: slots * lm < 2^32
+  for (uint32_t f0 = 0; f0 < slots; f0 += kThreads) {
+    const uint32_t f = f0 + tid;
+    if (f < slots) {
+      const uint32_t i = uint32_t((uint64_t(f) * mag) >> 32), j = f - i * lm;
+      const char* src = sp + row_off(r0 + i, e0, e1, nouter, s0, s1, s2);
+      const int x0 = int(16u * j) - int(reinterpret_cast<uintptr_t>(src) & 15u);   // row byte at line j
+      if (x0 >= 0 && uint32_t(x0) + 16u <= n)
+        __builtin_amdgcn_global_load_lds(src + x0, (lds_void*)(lds + 16u * (f0 + (tid & ~63u))), 16, 0,
+                                         RS_MIS_LDS_AUX);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  // Phase 2.
+  const uint32_t mb = (n + 15u) / 16u + 1u;   // aligned destination blocks a row can touch
+  const uint32_t blocks = rows * mb;
+  const uint64_t magb = ((uint64_t(1) << 32) + mb - 1) / mb;
+  for (uint32_t jd = 0; jd < nd; ++jd) {
+    char* dp = kFan1 ? dp0 : static_cast<char*>(a.ptr[dst_pool(R, jd)]) + dst_off;
+    for (uint32_t f = tid; f < blocks; f += kThreads) {
+      const uint32_t i = uint32_t((uint64_t(f) * magb) >> 32), b = f - i * mb;
+      char* dst = dp + row_off(r0 + i, e0, e1, nouter, d0, d1, d2);
+      const MisSpan m = mis_span(sp + row_off(r0 + i, e0, e1, nouter, s0, s1, s2), dst, n);
+      const uint32_t y = m.e0 + 16u * b;   // row byte at the start of block b
+      if (y + 16u > m.e1) continue;
+      const uint32_t o = 16u * i * lm + m.h + y, o0 = o & ~15u, sh = o & 15u;
+      const u32x4 A = *reinterpret_cast<const u32x4*>(lds + o0);
+      st16(dst + y, sh ? funnel16(A, *reinterpret_cast<const u32x4*>(lds + o0 + 16u), sh) : A);
+    }
+#pragma unroll
+    for (int k = 0; k < kMisEdge; ++k) {
+      const uint32_t f = uint32_t(k) * kThreads + tid;
+      if (f < rows * 32u) {
+        const uint32_t i = f >> 5, e = f & 31u;
+        char* dst = dp + row_off(r0 + i, e0, e1, nouter, d0, d1, d2);
+        const MisSpan m = mis_span(sp + row_off(r0 + i, e0, e1, nouter, s0, s1, s2), dst, n);
+        // from the registers: [0, f0) and [f1, n)
+        const uint32_t pr = e < 16u ? e : m.f1 + (e - 16u);
+        if (e < 16u ? pr < m.f0 : pr < n) dst[pr] = eb[k];
+        // from LDS: [f0, e0) and [e1, f1)
+        const uint32_t pl = e < 16u ? m.f0 + e : m.e1 + (e - 16u);
+        if (e < 16u ? pl < m.e0 : pl < m.f1) dst[pl] = lds[16u * i * lm + m.h + pl];
+      }
+    }
+  }
+}
+
+template <bool kFan1>
+__device__ __forceinline__ void bulk_body(const LaunchArgs& a, const CopyRegion* R, uint32_t unit,
+                                          char* mis_tile) {
   const uint32_t tid = threadIdx.x;
   const uint64_t src_off = R->src_off, dst_off = R->dst_off;
   const uint64_t s0 = R->sstr[0], s1 = R->sstr[1], s2 = R->sstr[2];
@@ -653,6 +767,21 @@ __device__ __forceinline__ void bulk_body(const LaunchArgs& a, const CopyRegion*
       bulk_short_rows<kFan1, 1>(a, R, sp, dp0, dst_off, r0, r1, vpr, L, e0, e1, nouter,
                                 s0, s1, s2, d0, d1, d2, nd);
   } else {
+#if RS_MIS_LDS
+    // Misaligned rows that fit the staging area, replicas at one alignment:
+    // through LDS.
+    const uint32_t lm = (inner + 15u) / 16u + 1u;
+    bool congruent = true;
+    for (uint32_t j = 1; j < nd; ++j)
+      congruent &= ((reinterpret_cast<uintptr_t>(a.ptr[dst_pool(R, j)]) ^ reinterpret_cast<uintptr_t>(
+                        a.ptr[dst_pool(R, 0)])) & 15u) == 0;
+    if (congruent && inner >= kMisMinRow && uint64_t(r1 - r0) * lm * 16u <= kMisTile &&
+        (r1 - r0) * 32u <= uint32_t(kMisEdge) * kThreads) {
+      bulk_misaligned_lds<kFan1>(a, R, sp, dp0, dst_off, r0, r1 - r0, inner, lm, e0, e1, nouter, s0, s1, s2,
+                                 d0, d1, d2, nd, mis_tile);
+      return;
+    }
+#endif
     // Misaligned: funnel-shifted 16-byte vectors numbered across the unit,
     // once per destination (each replica may sit at its own alignment).
     for (uint32_t j = 0; j < nd; ++j) {
@@ -666,10 +795,11 @@ __global__ __launch_bounds__(kThreads, RS_BULK_MIN_WAVES) void rs_bulk_kernel(La
   // One workgroup per work unit (looping workgroups measured slower).
   const uint32_t unit = unit_of_block<RS_XCD_MAP != 0>(blockIdx.x, gridDim.x, RS_XCD_CHUNK);
   const CopyRegion* R = find_region<CopyRegion>(a, unit);
+  __shared__ __attribute__((aligned(16))) char mis_tile[kMisTile];
   if (n_dst_of(R) == 1)
-    bulk_body<true>(a, R, unit);
+    bulk_body<true>(a, R, unit, mis_tile);
   else
-    bulk_body<false>(a, R, unit);
+    bulk_body<false>(a, R, unit, mis_tile);
 }
 
 // ---------------------------------------------------------------------------
@@ -1319,8 +1449,10 @@ size_t bulk_lds_pad(int dev) {
       hipDeviceGetAttribute(&per_wg, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
       per_cu <= 0 || per_wg <= 0)
     return 0;
-  int pad = (per_cu / RS_BULK_RESIDENT) & ~511;
-  if (pad > per_wg) pad = per_wg;
+  // The kernel's own static LDS (kMisTile) counts toward the per-workgroup share.
+  int pad = ((per_cu / RS_BULK_RESIDENT) & ~511) - int(kMisTile);
+  if (pad < 0) pad = 0;
+  if (pad + int(kMisTile) > per_wg) pad = per_wg - int(kMisTile);
   if (dev >= 0 && dev < kMaxDevices) cache[dev].store(pad + 1, std::memory_order_relaxed);
   return size_t(pad);
 }
