@@ -14,10 +14,14 @@
 //        whole groups: long rows are walked row by row by the whole workgroup;
 //        the vectors of short rows are numbered across the unit so every lane
 //        loads its share in one batch (sub-wave lane groups per row when rows
-//        have several outer dims).  Misaligned regions: each wave copies one
-//        row; once the destination is 16-byte aligned, its 16-byte stores
-//        take bytes from two aligned 16-byte source loads joined by byte
-//        funnel shifts (edges at the widest granule the co-alignment allows).
+//        have several outer dims).  Misaligned regions (source and
+//        destination differ modulo 16): rows of 512 bytes or more are staged
+//        through a static LDS area (whole source lines by direct-to-LDS
+//        loads) and every 16-byte-aligned destination block is rebuilt from
+//        two aligned LDS reads joined by byte funnel shifts; shorter rows
+//        number their (row, vector) pairs across the unit, each 16-byte
+//        store from two aligned source loads joined the same way; the edges
+//        of a row go byte by byte, and no load leaves a row.
 //        Launched so that at most five workgroups share a CU (see
 //        bulk_lds_pad): fewer streams concurrently per CU copy faster.
 //  thin  runs shorter than the thin threshold (e.g. the 8-byte rows of a
