@@ -1215,6 +1215,9 @@ __device__ __forceinline__ uint32_t e4m3x4(uint32_t w0, uint32_t w1, uint32_t m0
 #ifndef RS_MX_MIN_WAVES
 #define RS_MX_MIN_WAVES 1  // occupancy floor (waves per SIMD) the register allocator must keep
 #endif
+#ifndef RS_MX_FUNNEL
+#define RS_MX_FUNNEL 1     // sources whose rows are not 16-byte aligned: funnel-shifted 16-byte loads
+#endif
 #ifndef RS_MX_LDS_AUX
 #define RS_MX_LDS_AUX 2    // cache policy of the direct-to-LDS loads (2: non-temporal)
 #endif
@@ -1325,6 +1328,60 @@ __device__ __forceinline__ void mx_unit(const LaunchArgs& a, const MxRegion* R, 
   // Phase 1: every group of the unit into its LDS slot.  Whole, 16-byte
   // aligned groups load straight into LDS; a partial or misaligned group is
   // gathered element by element (zero-filled) and written by its lane.
+  // Source rows not 16-byte aligned (a source shard boundary off the 8-
+  // element grid): each group is two aligned 16-byte loads joined by a
+  // funnel shift, half the unit at a time, so all of a lane's loads of a
+  // half are in flight together; groups whose lines would reach past the
+  // row (its first and last) are gathered element by element.
+  const bool mis_rows =
+      !kTwo && RS_MX_FUNNEL &&
+      ((reinterpret_cast<uintptr_t>(sp) | (kOneRow ? so1 : (s0 | (nouter >= 2 ? s1 : 0) | (nouter >= 3 ? s2 : 0)))) &
+       15u) != 0;
+  if (mis_rows) {
+#pragma unroll
+    for (uint32_t half = 0; half < 2; ++half) {
+      u32x4 A[K / 2], B[K / 2];
+      uint32_t sh[K / 2];
+      bool fun[K / 2];
+#pragma unroll
+      for (uint32_t kk = 0; kk < K / 2; ++kk) {
+        const uint32_t k = half * (K / 2) + kk;
+        const uint32_t s = k * kMxThreads + tid;
+        const uint32_t rl = s >> lg, g = s & (Lp - 1u);
+        fun[kk] = false;
+        sh[kk] = 0;
+        if (rl < nr && g < ng) {
+          const char* rs = sp + (kOneRow ? so1 : row_off(r0 + rl, e0, e1, nouter, s0, s1, s2));
+          const char* p = rs + uint64_t(g) * 16u;
+          const uint32_t r = uint32_t(reinterpret_cast<uintptr_t>(p) & 15u);
+          const char* L = p - r;
+          if (g * 8u + 8u <= inner && L >= rs && L + (r ? 32u : 16u) <= rs + 2u * inner) {
+            A[kk] = *reinterpret_cast<const u32x4*>(L);
+            if (r) B[kk] = *reinterpret_cast<const u32x4*>(L + 16u);
+            fun[kk] = true;
+            sh[kk] = r;
+          }
+        }
+      }
+#pragma unroll
+      for (uint32_t kk = 0; kk < K / 2; ++kk) {
+        const uint32_t k = half * (K / 2) + kk;
+        const uint32_t s = k * kMxThreads + tid;
+        const uint32_t rl = s >> lg, g = s & (Lp - 1u);
+        if (fun[kk]) {
+          stage[s] = sh[kk] ? funnel16(A[kk], B[kk], sh[kk]) : A[kk];
+        } else if (rl < nr && g < ng) {
+          const uint16_t* q = reinterpret_cast<const uint16_t*>(
+              sp + (kOneRow ? so1 : row_off(r0 + rl, e0, e1, nouter, s0, s1, s2)) + uint64_t(g) * 16u);
+          const uint32_t n = min(inner - g * 8u, 8u);
+          uint32_t w[4] = {0, 0, 0, 0};
+          for (uint32_t i = 0; i < 8; ++i)
+            if (i < n) w[i >> 1] |= uint32_t(q[i]) << (16 * (i & 1));
+          stage[s] = u32x4{w[0], w[1], w[2], w[3]};
+        }
+      }
+    }
+  } else
 #pragma unroll
   for (uint32_t k = 0; k < K; ++k) {
     const uint32_t s = k * kMxThreads + tid;
