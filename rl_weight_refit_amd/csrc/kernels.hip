@@ -1218,6 +1218,9 @@ __device__ __forceinline__ uint32_t e4m3x4(uint32_t w0, uint32_t w1, uint32_t m0
 #ifndef RS_MX_FUNNEL
 #define RS_MX_FUNNEL 1     // sources whose rows are not 16-byte aligned: funnel-shifted 16-byte loads
 #endif
+#ifndef RS_MX_LINES
+#define RS_MX_LINES 1      // such sources staged as aligned lines in LDS, groups rebuilt in phase 2
+#endif
 #ifndef RS_MX_LDS_AUX
 #define RS_MX_LDS_AUX 2    // cache policy of the direct-to-LDS loads (2: non-temporal)
 #endif
@@ -1305,6 +1308,14 @@ __device__ __forceinline__ MxFields mx_fields(const LaunchArgs& a, const MxRegio
   return f;
 }
 
+// The first n (clamped to 0..8) of the eight bf16 elements of x, the rest zero.
+__device__ __forceinline__ u32x4 keep_elems(u32x4 x, int n) {
+  auto keep = [&](uint32_t w, int i) -> uint32_t {   // dword i holds elements 2i, 2i + 1
+    return n >= 2 * i + 2 ? w : (n == 2 * i + 1 ? (w & 0xFFFFu) : 0u);
+  };
+  return u32x4{keep(x.x, 0), keep(x.y, 1), keep(x.z, 2), keep(x.w, 3)};
+}
+
 template <bool kOneRow, bool kFan1, bool kTwo = false>
 __device__ __forceinline__ void mx_unit(const LaunchArgs& a, const MxRegion* R, const MxFields& f, uint32_t r0,
                                         uint32_t nr, u32x4* stage, uint8_t* sc_stage) {
@@ -1337,7 +1348,52 @@ __device__ __forceinline__ void mx_unit(const LaunchArgs& a, const MxRegion* R, 
       !kTwo && RS_MX_FUNNEL &&
       ((reinterpret_cast<uintptr_t>(sp) | (kOneRow ? so1 : (s0 | (nouter >= 2 ? s1 : 0) | (nouter >= 3 ? s2 : 0)))) &
        15u) != 0;
-  if (mis_rows) {
+  // Line layout (such rows when a row's slots hold its lines with two to
+  // spare and every row's two partial lines have a lane): slot j of row i
+  // holds the row's aligned source line j (row byte x at slot byte
+  // h_i + x, h_i = row address mod 16), whole lines by direct-to-LDS loads
+  // and the in-row elements of the partial first and last lines by their
+  // lanes after the wait; phase 2 rebuilds each group with funnel shifts.
+  const bool lines = RS_MX_LINES && mis_rows && ng + 2u <= Lp && 2u * nr <= kMxThreads;
+  if (lines) {
+    uint16_t pe[7];
+    uint32_t pb = 0, pn = 0;   // LDS byte of the first element, element count
+    if (tid < 2u * nr) {
+      const uint32_t rl = tid >> 1, side = tid & 1u;
+      const char* rs = sp + (kOneRow ? so1 : row_off(r0 + rl, e0, e1, nouter, s0, s1, s2));
+      const uint32_t h = uint32_t(reinterpret_cast<uintptr_t>(rs) & 15u), nb = 2u * inner;
+      const uint32_t jl = (h + nb - 1u) >> 4;   // last line
+      uint32_t b0 = 0, b1 = 0;                  // row bytes [b0, b1) of this partial line
+      if (side == 0) {
+        if (h != 0 || nb < 16u) b1 = min(16u - h, nb);  // a partial first line
+      } else if (jl > 0 && ((h + nb) & 15u) != 0) {
+        b0 = 16u * jl - h;                               // a partial last line
+        b1 = nb;
+      }
+      pn = (b1 - b0) >> 1;
+      pb = (rl << lg) * 16u + h + b0;
+      const uint16_t* q = reinterpret_cast<const uint16_t*>(rs + b0);
+#pragma unroll
+      for (uint32_t e = 0; e < 7; ++e) pe[e] = e < pn ? q[e] : uint16_t(0);
+    }
+#pragma unroll
+    for (uint32_t k = 0; k < K; ++k) {
+      const uint32_t s = k * kMxThreads + tid;
+      const uint32_t rl = s >> lg, j = s & (Lp - 1u);
+      if (rl < nr) {
+        const char* rs = sp + (kOneRow ? so1 : row_off(r0 + rl, e0, e1, nouter, s0, s1, s2));
+        const int x0 = int(16u * j) - int(reinterpret_cast<uintptr_t>(rs) & 15u);   // row byte at line j
+        if (x0 >= 0 && uint32_t(x0) + 16u <= 2u * inner)
+          __builtin_amdgcn_global_load_lds(rs + x0, (lds_void*)(stage + k * kMxThreads + (tid & ~63u)), 16, 0,
+                                           RS_MX_LDS_AUX);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    uint16_t* st16p = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(stage) + pb);
+#pragma unroll
+    for (uint32_t e = 0; e < 7; ++e)
+      if (e < pn) st16p[e] = pe[e];
+  } else if (mis_rows) {
 #pragma unroll
     for (uint32_t half = 0; half < 2; ++half) {
       u32x4 A[K / 2], B[K / 2];
@@ -1427,8 +1483,22 @@ __device__ __forceinline__ void mx_unit(const LaunchArgs& a, const MxRegion* R, 
     const uint32_t rl = s >> lg, g = s & (Lp - 1u);
     const uint32_t col = g * 8u;
     const int nvalid = rl < nr ? int(min(inner, col + 16u)) - int(min(inner, col)) : 0;
-    const u32x4 xa = nvalid > 0 ? stage[s] : u32x4{0u, 0u, 0u, 0u};
-    const u32x4 xb = nvalid > 8 ? stage[s + 1] : u32x4{0u, 0u, 0u, 0u};
+    u32x4 xa = nvalid > 0 ? stage[s] : u32x4{0u, 0u, 0u, 0u};
+    u32x4 xb = nvalid > 8 ? stage[s + 1] : u32x4{0u, 0u, 0u, 0u};
+    if (lines && nvalid > 0) {
+      // Groups g, g + 1 of the row: bytes h .. h + 31 of lines g .. g + 2,
+      // elements past the row's end zeroed.
+      const char* rs = sp + (kOneRow ? so1 : row_off(r0 + rl, e0, e1, nouter, s0, s1, s2));
+      const uint32_t h = uint32_t(reinterpret_cast<uintptr_t>(rs) & 15u);
+      if (h) {
+        const u32x4 L2 = nvalid > 8 ? stage[s + 2] : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 L0 = xa, L1 = stage[s + 1];
+        xa = funnel16(L0, L1, h);
+        xb = nvalid > 8 ? funnel16(L1, L2, h) : u32x4{0u, 0u, 0u, 0u};
+      }
+      xa = keep_elems(xa, nvalid);
+      xb = keep_elems(xb, nvalid - 8);
+    }
     const MxCodes c = mx_encode(xa, xb);
     if (nvalid > 0) {
       const uint64_t doff = dst_off_r + (kOneRow ? do1 : row_off(r0 + rl, e0, e1, nouter, d0, d1, d2)) + col;
