@@ -461,3 +461,55 @@ def test_high_rank_layouts(seed):
 def test_high_rank_mxfp8(seed):
     gh.log("high rank mxfp8 %d" % seed)
     gh.check_against_oracle(helpers.high_rank_case(seed, mx=True))
+
+
+def _padded_source(shape, mesh, pl, pad):
+    """A bf16 source side whose slots are views with `pad` extra elements
+    per row (row strides off the 16-byte grid)."""
+    from oracle import layout as olayout
+    desc = {"shape": shape, "dtype": "bf16", "mesh": mesh, "placements": pl, "slot_of_coord": None,
+            "quant": None}
+    bufs, slots = {}, []
+    for k, (_, ln) in enumerate(olayout.slot_boxes(desc)):
+        dims = list(ln)
+        st, acc = [], 1
+        for i in reversed(range(len(dims))):
+            st.append(acc)
+            acc *= dims[i] + (pad if i == len(dims) - 1 else 0)
+        bufs["s%d" % k] = {"dtype": "bf16", "elems": acc + 3}
+        slots.append({"buf": "s%d" % k, "view": (3, list(reversed(st)))})
+    return bufs, synth.side(mesh, pl, slots=slots)
+
+
+MX_MISALIGNED = {
+    # source shards off the 8-element grid along the last dim: rows staged as
+    # aligned lines (several rows per unit, one row per unit)
+    "tp3_last_dim_1000": ([4, 16, 1000], ([3], [2]), ([2], [1]), 0),
+    "tp3_last_dim_7168": ([2, 8, 7168], ([3], [2]), ([2, 2], [0, 1]), 0),
+    "tp5_last_dim_replicated": ([3, 24, 1337], ([5], [2]), ([2, 2], [1, -1]), 0),
+    # padded source rows: row strides off the 16-byte grid; 1,024-element
+    # rows leave no spare slots (the register funnel path), 300 and 7,000 do
+    "padded_rows_1024": ([4, 12, 1024], ([2], [0]), ([2], [1]), 1),
+    "padded_rows_300": ([6, 40, 300], ([1], [-1]), ([3], [1]), 3),
+    "padded_rows_7000": ([2, 6, 7000], ([2], [1]), ([1], [-1]), 5),
+}
+
+
+@pytest.mark.parametrize("shifts", [(0, 0), (2, 3), (6, 0)])
+@pytest.mark.parametrize("name", sorted(MX_MISALIGNED))
+def test_mxfp8_misaligned_source_rows(name, shifts):
+    """MXFP8 installs from source rows that are not 16-byte aligned (source
+    shards cut off the 8-element grid, padded row strides, shifted
+    pointers): groups rebuilt from aligned lines with funnel shifts, the
+    rows' partial first and last lines element by element."""
+    shape, (sm, sp), (dm, dp), pad = MX_MISALIGNED[name]
+    bufs = {}
+    if pad:
+        bufs, src = _padded_source(shape, sm, sp, pad)
+    else:
+        src = synth.side(sm, sp)
+    t = {"name": "w", "shape": shape, "dtype": "bf16", "src": src,
+         "dst": synth.side(dm, dp, quant="mxfp8"), "values": {"kind": "normal", "std": 0.02, "seed": 81}}
+    gh.log("mx misaligned %s %s" % (name, shifts))
+    gh.check_against_oracle({"name": "mx_mis_" + name, "buffers": bufs, "tensors": [t]},
+                            src_shift=shifts[0], dst_shift=shifts[1])
