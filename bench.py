@@ -368,6 +368,25 @@ def secondary(torch, binding, stream):
                                    GBps_back_to_back=round(nb / bb / 1e6, 1))
         out[key] = slab
         del srcs, dsts
+    # The DSV3 gate and up projections installed as MXFP8 from a source cut
+    # TP3 along the 7,168-wide hidden dim: source rows of 2,390 elements
+    # (4,780 B apart, off the 16-byte grid) and blocks that straddle two
+    # source shards.
+    wl = synth.moe_dsv3(quant="mxfp8")
+    wl["tensors"] = [dict(t, src=synth.side([3], [2])) for t in wl["tensors"][:2]]
+    src = device_sources(torch, binding, wl)
+    sp = [x.data_ptr() for t in src for x in t]
+    named, dp = device_destinations(torch, binding, wl)
+    plan = plan_of(binding, wl)
+    info = plan.info()
+    ms = time_plan(torch, binding, plan, sp, dp, stream, poison=list(named.values()))
+    nb = info["bytes_read"] + info["bytes_written"]
+    out["mxfp8_dsv3_gate_up_from_tp3_hidden"] = {"ms": round(ms, 4), "GBps": round(nb / ms / 1e6, 1),
+                                                 "bytes": nb, "regions": info["regions"],
+                                                 "launches": info["n_launches"]}
+    plan.destroy()
+    del src, named
+    torch.cuda.empty_cache()
     # A large uneven bf16 layout: TP3 -> TP2 over an odd last dim (2,049),
     # so regions start at source/destination offsets that differ modulo 16
     # (the misaligned path: funnel-shifted 16-byte loads, aligned stores).
