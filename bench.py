@@ -179,8 +179,18 @@ def device_destinations(torch, binding, wl):
                 ptrs.append(named[key].data_ptr())
         else:
             ptrs += [named[e["buf"]].data_ptr() for e in d["slots"]]
-        if d.get("quant") == "mxfp8":
+        if d.get("quant") == "mxfp8" and d.get("scale_slots") is not None:
             ptrs += [named[e["buf"]].data_ptr() for e in d["scale_slots"]]
+        elif d.get("quant") == "mxfp8":
+            # Dense per-slot scale buffers: the slot's box with its last
+            # extent in 32-element blocks.
+            sp = spec(t, "dst")
+            for k in range(int(np.prod(d["mesh"]))):
+                _, ln = binding.reshard_shard_box(sp, k)
+                nsc = int(np.prod(ln[:-1])) * (-(-ln[-1] // 32)) if ln else 0
+                key = "%s/scale/%d" % (t["name"], k)
+                named[key] = torch.empty(max(1, nsc), dtype=torch.uint8, device="cuda")
+                ptrs.append(named[key].data_ptr())
     return named, ptrs
 
 
