@@ -133,6 +133,9 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) {
 // at least 512 bytes needs at most 16384 + 31 * 32 bytes (a row slot is
 // ceil(row / 16) + 1 lines: at most 31 bytes beyond the row's own).
 constexpr uint32_t kMisTile = RS_MIS_LDS ? 17408u : 16u;
+#ifndef RS_THIN_SWIZZLE
+#define RS_THIN_SWIZZLE 1      // group-loaded thin units with members <= 4 bytes: swizzled LDS slots
+#endif
 #ifndef RS_THIN_GROUP_BATCH
 #define RS_THIN_GROUP_BATCH 1  // group-loaded thin units: a lane's loads all in flight before LDS writes
 #endif
@@ -815,7 +818,19 @@ __global__ __launch_bounds__(kThreads, RS_BULK_MIN_WAVES) void rs_bulk_kernel(La
 // the staged span (row = q / inner, col = q % inner).  G: the granule the
 // LDS side allows (a divisor of inner, cm and S); 16-byte stores where the
 // destination is 16-byte aligned, granules for the rest.
-template <int G>
+// LDS slot swizzle of group-loaded blocks whose members are at most 4 bytes
+// wide: 16-byte slot s is kept at slot s ^ ((s >> 4) & 7), i.e. byte a at
+// a ^ (((a >> 8) & 7) << 4).  A member's stores read 4-byte (or narrower)
+// granules of rows 4v .. 4v + 3, 32 bytes apart for 32-byte rows: unswizzled,
+// a wave's reads fall on two bank groups (32 lanes per bank); swizzled, on
+// sixteen.  The map only permutes slots inside aligned groups of eight and
+// is its own inverse, so the loads fetch source slot swz(p) into slot p.
+template <bool kSw>
+__device__ __forceinline__ uint32_t lds_swz8(uint32_t a) {
+  return kSw ? a ^ (((a >> 8) & 7u) << 4) : a;
+}
+
+template <int G, bool kSw>
 __device__ __forceinline__ void group_store(char* D, const char* lds, uint32_t cm, uint32_t S, uint32_t inner,
                                            uint32_t nbytes, uint32_t tid) {
   uint32_t head = 0;
@@ -827,7 +842,7 @@ __device__ __forceinline__ void group_store(char* D, const char* lds, uint32_t c
       uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int k = 0; k < 16 / G; ++k) {
-        const char* p = lds + row * S + cm + col;
+        const char* p = lds + lds_swz8<kSw>(row * S + cm + col);
         if (G == 16) {
           const u32x4 t = *reinterpret_cast<const u32x4*>(p);
           w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
@@ -857,7 +872,7 @@ __device__ __forceinline__ void group_store(char* D, const char* lds, uint32_t c
   const uint32_t g = low_granule(uint32_t(G) | uint32_t(reinterpret_cast<uintptr_t>(D) & 15u));
   for (uint32_t q = head + tid * g; q < nbytes; q += kThreads * g) {
     const uint32_t row = q / inner, col = q - row * inner;
-    copy_granule(D + q, lds + row * S + cm + col, g);
+    copy_granule(D + q, lds + lds_swz8<kSw>(row * S + cm + col), g);
   }
 }
 
@@ -866,21 +881,20 @@ __device__ __forceinline__ void group_store(char* D, const char* lds, uint32_t c
 // [r0, r1) of the group's column span go into LDS once -- 16-byte vectors
 // when consecutive rows of the span are contiguous in the source -- and
 // every member writes its packed destination rows from there.
-__device__ __forceinline__ void thin_group_unit(const LaunchArgs& a, const CopyRegion* R, uint32_t ul, char* tile) {
+// kSw: members at most 4 bytes wide, slots swizzled (lds_swz8) where the
+// block goes straight into LDS.
+template <bool kSw>
+__device__ __forceinline__ void thin_group_body(const LaunchArgs& a, const CopyRegion* R, uint32_t ul, char* tile,
+                                                uint64_t lo, uint32_t S) {
   const uint32_t tid = threadIdx.x;
   const uint32_t gm = (R->flags >> 16) & 255u;
   const uint32_t rows = R->rows, rpu = R->rows_per_unit;
   const uint32_t e0 = R->e0, e1 = R->e1, nouter = R->flags & kFlagOuterMask;
   const uint64_t s0 = R->sstr[0], s1 = R->sstr[1], s2 = R->sstr[2];
-  uint64_t lo = R->src_off, hi = R->src_off + R->inner;
-  for (uint32_t m = 1; m < gm; ++m) {
-    lo = min(lo, R[m].src_off);
-    hi = max(hi, R[m].src_off + R[m].inner);
-  }
-  const uint32_t S = uint32_t(hi - lo);
   const char* base = static_cast<const char*>(a.ptr[src_pool(R)]) + lo;
   const uint32_t r0 = ul * rpu, r1 = min(r0 + rpu, rows), T = r1 - r0;
   uint32_t sh = 0;
+  bool swz = false;
   if (nouter <= 1 && s0 == S) {
     // One contiguous block: byte head, then 16-byte vectors with all of a
     // lane's loads in flight before any LDS write, then a byte tail.
@@ -893,11 +907,13 @@ __device__ __forceinline__ void thin_group_unit(const LaunchArgs& a, const CopyR
       // (no registers; every load of the unit in flight at once).
       constexpr uint32_t kB = (kGroupTile / 16 + kThreads - 1) / kThreads;
       const uint32_t nv = n >> 4;
+      swz = kSw && (nv & 7u) == 0;
 #pragma unroll
       for (uint32_t k = 0; k < kB; ++k) {
         const uint32_t v = k * kThreads + tid;
+        const uint32_t vs = swz ? v ^ ((v >> 4) & 7u) : v;   // below nv: nv is a multiple of 8
         if (v < nv)
-          __builtin_amdgcn_global_load_lds(src + 16u * v,
+          __builtin_amdgcn_global_load_lds(src + 16u * vs,
                                            (lds_void*)(tile + 16u * (k * kThreads + (tid & ~63u))), 16, 0,
                                            RS_THIN_LDS_AUX);
       }
@@ -945,15 +961,39 @@ __device__ __forceinline__ void thin_group_unit(const LaunchArgs& a, const CopyR
     const uint32_t G = low_granule((sh + cm) | S | inner);
     for (uint32_t j = 0; j < nd; ++j) {
       char* D = static_cast<char*>(a.ptr[dst_pool(M, j)]) + M->dst_off + uint64_t(r0) * inner;
-      switch (G) {
-        case 16: group_store<16>(D, lds, cm, S, inner, nbytes, tid); break;
-        case 8: group_store<8>(D, lds, cm, S, inner, nbytes, tid); break;
-        case 4: group_store<4>(D, lds, cm, S, inner, nbytes, tid); break;
-        case 2: group_store<2>(D, lds, cm, S, inner, nbytes, tid); break;
-        default: group_store<1>(D, lds, cm, S, inner, nbytes, tid); break;
+      if (kSw && swz) {
+        switch (G) {
+          case 4: group_store<4, true>(D, lds, cm, S, inner, nbytes, tid); break;
+          case 2: group_store<2, true>(D, lds, cm, S, inner, nbytes, tid); break;
+          default: group_store<1, true>(D, lds, cm, S, inner, nbytes, tid); break;
+        }
+      } else {
+        switch (G) {
+          case 16: group_store<16, false>(D, lds, cm, S, inner, nbytes, tid); break;
+          case 8: group_store<8, false>(D, lds, cm, S, inner, nbytes, tid); break;
+          case 4: group_store<4, false>(D, lds, cm, S, inner, nbytes, tid); break;
+          case 2: group_store<2, false>(D, lds, cm, S, inner, nbytes, tid); break;
+          default: group_store<1, false>(D, lds, cm, S, inner, nbytes, tid); break;
+        }
       }
     }
   }
+}
+
+__device__ __forceinline__ void thin_group_unit(const LaunchArgs& a, const CopyRegion* R, uint32_t ul, char* tile) {
+  const uint32_t gm = (R->flags >> 16) & 255u;
+  uint64_t lo = R->src_off, hi = R->src_off + R->inner;
+  for (uint32_t m = 1; m < gm; ++m) {
+    lo = min(lo, R[m].src_off);
+    hi = max(hi, R[m].src_off + R[m].inner);
+  }
+  const uint32_t S = uint32_t(hi - lo);
+  // The member at the group's first column has the widest granule (members
+  // of one group are equally wide).
+  if (RS_THIN_SWIZZLE && low_granule(S | R->inner) <= 4u)
+    thin_group_body<true>(a, R, ul, tile, lo, S);
+  else
+    thin_group_body<false>(a, R, ul, tile, lo, S);
 }
 
 // Thin sibling groups loaded whole (launches of their own: this path needs
