@@ -4,7 +4,8 @@ oracle, byte for byte: column slabs whose regions read the same source rows
 uneven column splits (members of different widths are not grouped),
 groups loaded whole by one workgroup per row block (contiguous spans, spans
 narrower than the source row, wide spans, several units with a ragged
-tail, replicas without fan-out),
+tail, replicas without fan-out, members of 4 bytes or less read through
+swizzled LDS slots),
 destination replicas, three-dim tensors with several outer dims, and
 shifted buffers."""
 
@@ -45,6 +46,11 @@ CASES = {
     "whole_partial_span_u8": ([70000, 10], "u8", ([2], [0]), ([3], [1])),
     "whole_wide_span_bf16": ([20000, 96], "bf16", ([2], [0]), ([16], [1])),
     "whole_f64_pairs": ([30000, 4], "f64", ([3], [0]), ([2], [1])),
+    # members of 4 bytes or less (swizzled LDS slots), a last unit of 5 rows
+    # per source (its block not a whole number of 128-byte slot groups)
+    "narrow_f32_8_cols_ragged": ([2 * (512 * 3 + 5), 8], "f32", ([2], [0]), ([8], [1])),
+    "narrow_bf16_8_cols": ([40000, 16], "bf16", ([2], [0]), ([8], [1])),
+    "narrow_u8_16_cols": ([50000, 16], "u8", ([2], [0]), ([16], [1])),
 }
 
 
