@@ -818,8 +818,8 @@ __global__ __launch_bounds__(kThreads, RS_BULK_MIN_WAVES) void rs_bulk_kernel(La
 // the staged span (row = q / inner, col = q % inner).  G: the granule the
 // LDS side allows (a divisor of inner, cm and S); 16-byte stores where the
 // destination is 16-byte aligned, granules for the rest.
-// LDS slot swizzle of group-loaded blocks whose members are at most 4 bytes
-// wide: 16-byte slot s is kept at slot s ^ ((s >> 4) & 7), i.e. byte a at
+// LDS slot swizzle of group-loaded blocks with members that read granules of
+// 4 bytes or less: 16-byte slot s is kept at slot s ^ ((s >> 4) & 7), i.e. byte a at
 // a ^ (((a >> 8) & 7) << 4).  A member's stores read 4-byte (or narrower)
 // granules of rows 4v .. 4v + 3, 32 bytes apart for 32-byte rows: unswizzled,
 // a wave's reads fall on two bank groups (32 lanes per bank); swizzled, on
@@ -881,8 +881,8 @@ __device__ __forceinline__ void group_store(char* D, const char* lds, uint32_t c
 // [r0, r1) of the group's column span go into LDS once -- 16-byte vectors
 // when consecutive rows of the span are contiguous in the source -- and
 // every member writes its packed destination rows from there.
-// kSw: members at most 4 bytes wide, slots swizzled (lds_swz8) where the
-// block goes straight into LDS.
+// kSw: some member reads granules of 4 bytes or less; slots swizzled
+// (lds_swz8) where the block goes straight into LDS.
 template <bool kSw>
 __device__ __forceinline__ void thin_group_body(const LaunchArgs& a, const CopyRegion* R, uint32_t ul, char* tile,
                                                 uint64_t lo, uint32_t S) {
@@ -983,14 +983,16 @@ __device__ __forceinline__ void thin_group_body(const LaunchArgs& a, const CopyR
 __device__ __forceinline__ void thin_group_unit(const LaunchArgs& a, const CopyRegion* R, uint32_t ul, char* tile) {
   const uint32_t gm = (R->flags >> 16) & 255u;
   uint64_t lo = R->src_off, hi = R->src_off + R->inner;
+  uint32_t wbits = R->inner;   // OR of the members' widths and column offsets
   for (uint32_t m = 1; m < gm; ++m) {
     lo = min(lo, R[m].src_off);
     hi = max(hi, R[m].src_off + R[m].inner);
+    wbits |= R[m].inner | uint32_t(R[m].src_off - R->src_off);
   }
   const uint32_t S = uint32_t(hi - lo);
-  // The member at the group's first column has the widest granule (members
-  // of one group are equally wide).
-  if (RS_THIN_SWIZZLE && low_granule(S | R->inner) <= 4u)
+  // Swizzled slots when some member reads granules of 4 bytes or less (the
+  // granule of every member divides low_granule(S | wbits)).
+  if (RS_THIN_SWIZZLE && low_granule(S | wbits) <= 4u)
     thin_group_body<true>(a, R, ul, tile, lo, S);
   else
     thin_group_body<false>(a, R, ul, tile, lo, S);

@@ -1214,10 +1214,13 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
   // rows at different columns) and which of them are loaded whole: every
   // member writes packed rows and the group's column span is short.  Those
   // run in launches of their own, with a kernel of their own.
-  auto same_rows = [](const Final& x, const Final& y) {
-    if (x.rp->src_index != y.rp->src_index || x.rows != y.rows || x.units != y.units ||
-        x.rows_per_unit != y.rows_per_unit || x.rp->outer.size() != y.rp->outer.size() ||
-        x.rp->outer.size() == 0)
+  // Thin regions reading the same source rows (same buffer, row count and
+  // outer dims, column offsets within one source row).  Loaded whole, their
+  // widths may differ; taking units member-fastest, they must also have
+  // equal units.
+  auto same_src_rows = [](const Final& x, const Final& y) {
+    if (x.rp->src_index != y.rp->src_index || x.rows != y.rows ||
+        x.rp->outer.size() != y.rp->outer.size() || x.rp->outer.size() == 0)
       return false;
     uint64_t xe[3], xs[3], xd[3], xc[3], ye[3], ys[3], yd[3], yc[3];
     outer_fields(x.rp->outer, xe, xs, xd, xc);
@@ -1227,30 +1230,51 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
     const uint64_t a = x.rp->src_off, b = y.rp->src_off;
     return (a > b ? a - b : b - a) < xs[0];
   };
+  auto same_units = [](const Final& x, const Final& y) {
+    return x.units == y.units && x.rows_per_unit == y.rows_per_unit;
+  };
   std::vector<uint32_t> group_of(fin.size(), 0);  // 1 + group number, 0: none
   std::vector<uint8_t> whole(fin.size(), 0);
   if (RS_THIN_SIBLINGS) {
     std::vector<size_t> thin;
     for (size_t q = 0; q < fin.size(); ++q)
       if (fin[q].bucket == kThin) thin.push_back(q);
-    size_t k = 0;
     uint32_t ng = 0;
+    // Members [k, e) become group ng; loaded whole when every member writes
+    // packed rows and their column span fits the group tile.
+    auto make_group = [&](size_t k, size_t e, bool allow_whole) -> bool {
+      bool packed_all = true;
+      uint64_t lo = ~uint64_t(0), hi = 0;
+      for (size_t q = k; q < e; ++q) {
+        const Final& f = fin[thin[q]];
+        packed_all &= (f.flags & kFlagDstPacked) != 0;
+        lo = std::min(lo, f.rp->src_off);
+        hi = std::max(hi, f.rp->src_off + f.rp->inner);
+      }
+      const bool w = RS_THIN_GROUP_LOAD && packed_all && hi - lo <= kGroupSpanMax;
+      if (!w && !allow_whole) return false;
+      ++ng;
+      for (size_t q = k; q < e; ++q) {
+        group_of[thin[q]] = ng;
+        whole[thin[q]] = w ? 1 : 0;
+      }
+      return true;
+    };
+    size_t k = 0;
     while (k < thin.size()) {
       size_t e = k + 1;
-      while (e < thin.size() && e - k < 255 && same_rows(fin[thin[k]], fin[thin[e]])) ++e;
-      if (e - k >= 2) {
-        ++ng;
-        bool packed_all = true;
-        uint64_t lo = ~uint64_t(0), hi = 0;
-        for (size_t q = k; q < e; ++q) {
-          const Final& f = fin[thin[q]];
-          group_of[thin[q]] = ng;
-          packed_all &= (f.flags & kFlagDstPacked) != 0;
-          lo = std::min(lo, f.rp->src_off);
-          hi = std::max(hi, f.rp->src_off + f.rp->inner);
+      while (e < thin.size() && e - k < 255 && same_src_rows(fin[thin[k]], fin[thin[e]])) ++e;
+      // The whole run as one group loaded whole, or else runs of members
+      // with equal units (loaded whole where they qualify, member-fastest
+      // otherwise).
+      if (e - k < 2 || !make_group(k, e, false)) {
+        size_t q = k;
+        while (q < e) {
+          size_t r = q + 1;
+          while (r < e && same_units(fin[thin[q]], fin[thin[r]])) ++r;
+          if (r - q >= 2) make_group(q, r, true);
+          q = r;
         }
-        if (RS_THIN_GROUP_LOAD && packed_all && hi - lo <= kGroupSpanMax)
-          for (size_t q = k; q < e; ++q) whole[thin[q]] = 1;
       }
       k = e;
     }
@@ -1355,7 +1379,13 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
                 hi = std::max(hi, batch[q]->rp->src_off + batch[q]->rp->inner);
               }
               const uint64_t rows = batch[k]->rows;
-              const uint64_t rpu = std::min<uint64_t>(std::max<uint64_t>(1, kGroupTile / (hi - lo)), rows);
+              // Whole 128-byte slot groups per unit where that keeps most of
+              // the tile: a contiguous, aligned block then goes straight into
+              // LDS (and can be swizzled) whatever the span.
+              uint64_t rpu = std::max<uint64_t>(1, kGroupTile / (hi - lo));
+              const uint64_t m = 128 / std::gcd<uint64_t>(hi - lo, 128);
+              if (rpu >= 2 * m) rpu -= rpu % m;
+              rpu = std::min<uint64_t>(rpu, rows);
               for (size_t q = k; q < e; ++q) {
                 sib[q] |= kFlagGroupLoad;
                 rpu_k[q] = uint32_t(rpu);
@@ -1365,8 +1395,11 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
           } else if (kernel == kThinGroup) {
             // A lone member left by a pool cut: a group of one.
             sib[k] = kFlagGroupLoad | (1u << 16);
-            const uint64_t rows = batch[k]->rows;
-            const uint64_t rpu = std::min<uint64_t>(std::max<uint64_t>(1, kGroupTile / batch[k]->rp->inner), rows);
+            const uint64_t rows = batch[k]->rows, w = batch[k]->rp->inner;
+            uint64_t rpu = std::max<uint64_t>(1, kGroupTile / w);
+            const uint64_t m = 128 / std::gcd<uint64_t>(w, 128);
+            if (rpu >= 2 * m) rpu -= rpu % m;
+            rpu = std::min<uint64_t>(rpu, rows);
             rpu_k[k] = uint32_t(rpu);
             units_k[k] = uint32_t((rows + rpu - 1) / rpu);
           }

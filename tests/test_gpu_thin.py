@@ -1,7 +1,8 @@
 """GPU parity of the LDS-staged thin kernel's sibling groups against the CPU
 oracle, byte for byte: column slabs whose regions read the same source rows
 (groups of 2 to 8 members, several work units each, a partial last unit),
-uneven column splits (members of different widths are not grouped),
+uneven column splits (members of different widths, grouped when loaded
+whole),
 groups loaded whole by one workgroup per row block (contiguous spans, spans
 narrower than the source row, wide spans, several units with a ragged
 tail, replicas without fan-out, members of 4 bytes or less read through
