@@ -980,31 +980,26 @@ __device__ __forceinline__ void thin_group_body(const LaunchArgs& a, const CopyR
   }
 }
 
+template <bool kSw>
 __device__ __forceinline__ void thin_group_unit(const LaunchArgs& a, const CopyRegion* R, uint32_t ul, char* tile) {
   const uint32_t gm = (R->flags >> 16) & 255u;
   uint64_t lo = R->src_off, hi = R->src_off + R->inner;
-  uint32_t wbits = R->inner;   // OR of the members' widths and column offsets
   for (uint32_t m = 1; m < gm; ++m) {
     lo = min(lo, R[m].src_off);
     hi = max(hi, R[m].src_off + R[m].inner);
-    wbits |= R[m].inner | uint32_t(R[m].src_off - R->src_off);
   }
-  const uint32_t S = uint32_t(hi - lo);
-  // Swizzled slots when some member reads granules of 4 bytes or less (the
-  // granule of every member divides low_granule(S | wbits)).
-  if (RS_THIN_SWIZZLE && low_granule(S | wbits) <= 4u)
-    thin_group_body<true>(a, R, ul, tile, lo, S);
-  else
-    thin_group_body<false>(a, R, ul, tile, lo, S);
+  thin_group_body<kSw && RS_THIN_SWIZZLE>(a, R, ul, tile, lo, uint32_t(hi - lo));
 }
 
 // Thin sibling groups loaded whole (launches of their own: this path needs
-// more registers than the thin kernel's others).
+// more registers than the thin kernel's others).  kSw: groups with a member
+// whose LDS reads are 4 bytes or narrower (swizzled LDS slots).
+template <bool kSw>
 __global__ __launch_bounds__(kThreads) void rs_thin_group_kernel(LaunchArgs a) {
   __shared__ __attribute__((aligned(16))) char tile[kGroupTile + 16];
   const uint32_t unit = unit_of_block<RS_THIN_XCD_CHUNK != 0>(blockIdx.x, gridDim.x, RS_THIN_XCD_CHUNK);
   const CopyRegion* R = find_region<CopyRegion>(a, unit);
-  thin_group_unit(a, R, unit - R->unit_begin, tile);
+  thin_group_unit<kSw>(a, R, unit - R->unit_begin, tile);
 }
 
 __global__ __launch_bounds__(kThreads) void rs_thin_kernel(LaunchArgs a) {
@@ -1675,7 +1670,10 @@ hipError_t launch(uint32_t bucket, uint32_t grid, const LaunchArgs& args, hipStr
       break;
     case kThin: hipLaunchKernelGGL(rs_thin_kernel, dim3(grid), dim3(kThreads), 0, stream, args); break;
     case kThinGroup:
-      hipLaunchKernelGGL(rs_thin_group_kernel, dim3(grid), dim3(kThreads), 0, stream, args);
+      hipLaunchKernelGGL(rs_thin_group_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, args);
+      break;
+    case kThinGroupNarrow:
+      hipLaunchKernelGGL(rs_thin_group_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, args);
       break;
     case kTiny: hipLaunchKernelGGL(rs_tiny_kernel, dim3(grid), dim3(kThreads), 0, stream, args); break;
     case kMx: hipLaunchKernelGGL(rs_mx_kernel, dim3(grid), dim3(kMxThreads), 0, stream, args); break;

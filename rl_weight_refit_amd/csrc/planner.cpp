@@ -1234,7 +1234,7 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
     return x.units == y.units && x.rows_per_unit == y.rows_per_unit;
   };
   std::vector<uint32_t> group_of(fin.size(), 0);  // 1 + group number, 0: none
-  std::vector<uint8_t> whole(fin.size(), 0);
+  std::vector<uint8_t> whole(fin.size(), 0);   // 1: loaded whole; 2: loaded whole, narrow members
   if (RS_THIN_SIBLINGS) {
     std::vector<size_t> thin;
     for (size_t q = 0; q < fin.size(); ++q)
@@ -1253,10 +1253,13 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
       }
       const bool w = RS_THIN_GROUP_LOAD && packed_all && hi - lo <= kGroupSpanMax;
       if (!w && !allow_whole) return false;
+      // Members reading granules of 4 bytes or less from LDS.
+      uint64_t wb = hi - lo;
+      for (size_t q = k; q < e; ++q) wb |= fin[thin[q]].rp->inner | (fin[thin[q]].rp->src_off - lo);
       ++ng;
       for (size_t q = k; q < e; ++q) {
         group_of[thin[q]] = ng;
-        whole[thin[q]] = w ? 1 : 0;
+        whole[thin[q]] = w ? ((wb & 7u) ? 2 : 1) : 0;
       }
       return true;
     };
@@ -1280,14 +1283,16 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
     }
   }
 
-  // Launch passes: one per bucket, then the thin groups loaded whole.
-  for (uint32_t pass = 0; pass <= kBuckets; ++pass) {
+  // Launch passes: one per bucket, then the thin groups loaded whole (with
+  // and without narrow members).
+  for (uint32_t pass = 0; pass <= kBuckets + 1; ++pass) {
     const uint32_t bucket = pass < kBuckets ? pass : uint32_t(kThin);
-    const uint32_t kernel = pass < kBuckets ? pass : uint32_t(kThinGroup);
+    const uint32_t kernel = pass < kBuckets ? pass : pass == kBuckets ? uint32_t(kThinGroup) : kThinGroupNarrow;
+    const uint8_t want_whole = pass < kBuckets ? 0 : pass == kBuckets ? 1 : 2;
     std::vector<const Final*> list;
     list.reserve(fin.size());
     for (size_t q = 0; q < fin.size(); ++q)
-      if (fin[q].bucket == bucket && (bucket != kThin || whole[q] == (pass == kBuckets)))
+      if (fin[q].bucket == bucket && (bucket != kThin || whole[q] == want_whole))
         list.push_back(&fin[q]);
     size_t i = 0;
     while (i < list.size()) {
@@ -1370,7 +1375,7 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
           while (gid && e < batch.size() && group_of[size_t(batch[e] - fin.data())] == gid) ++e;
           if (e - k >= 2) {
             for (size_t q = k; q < e; ++q) sib[q] = (uint32_t(e - k) << 16) | (uint32_t(q - k) << 24);
-            if (kernel == kThinGroup) {
+            if (kernel == kThinGroup || kernel == kThinGroupNarrow) {
               // The group's units belong to its first member: each unit
               // moves rows_per_unit rows of every member.
               uint64_t lo = ~uint64_t(0), hi = 0;
@@ -1392,7 +1397,7 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
                 units_k[q] = q == k ? uint32_t((rows + rpu - 1) / rpu) : 0;
               }
             }
-          } else if (kernel == kThinGroup) {
+          } else if (kernel == kThinGroup || kernel == kThinGroupNarrow) {
             // A lone member left by a pool cut: a group of one.
             sib[k] = kFlagGroupLoad | (1u << 16);
             const uint64_t rows = batch[k]->rows, w = batch[k]->rp->inner;
@@ -1527,7 +1532,7 @@ rs_status region_info(const PlanData& d, uint64_t index, rs_region* out) {
     const uint64_t k = index - base;
     std::memset(out, 0, sizeof(*out));
     out->tensor = d.region_tensor[index];
-    out->bucket = L.bucket == kThinGroup ? uint32_t(kThin) : L.bucket;
+    out->bucket = L.bucket >= kThinGroup ? uint32_t(kThin) : L.bucket;
     auto user = [&](uint16_t slot) { return L.pool[slot] & ~kDstBit; };
     if (L.bucket == kMx) {
       MxRegion m;

@@ -59,6 +59,9 @@ enum Bucket : uint32_t { kBulk = 0, kThin = 1, kTiny = 2, kMx = 3, kBuckets = 4 
 // Launch kind of thin sibling groups loaded whole (reported as thin regions;
 // a kernel of their own, so the thin kernel keeps its register budget).
 constexpr uint32_t kThinGroup = kBuckets;
+// The same for groups with a member whose LDS reads are 4 bytes or narrower
+// (that kernel swizzles its LDS slots).
+constexpr uint32_t kThinGroupNarrow = kBuckets + 1;
 
 // Region flags.
 enum : uint32_t {

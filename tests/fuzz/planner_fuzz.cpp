@@ -321,9 +321,10 @@ bool run_case(Rng& g, uint64_t c, bool corrupt) {
       // A group loaded whole: its first member takes all of the group's
       // units (rows_per_unit rows of every member each), the others none.
       seen[k].assign(whole && m ? 0 : nu, 0);
-      if (L.bucket != rs::kThin && L.bucket != rs::kThinGroup && gm) die("sibling group outside the thin bucket", c);
+      const bool group_launch = L.bucket == rs::kThinGroup || L.bucket == rs::kThinGroupNarrow;
+      if (L.bucket != rs::kThin && !group_launch && gm) die("sibling group outside the thin bucket", c);
       if ((gm == 1 && !whole) || (gm && m >= gm) || (!gm && m)) die("bad sibling group fields", c);
-      if (whole != (L.bucket == rs::kThinGroup)) die("group-load flag outside its launch kind", c);
+      if (whole != group_launch) die("group-load flag outside its launch kind", c);
       if (whole && !gm) die("group-load flag outside a sibling group", c);
       if (gm && (k < m || k - m + gm > L.n_regions)) die("sibling group leaves its launch", c);
       if (gm && m == 0) ++g_sibling_groups;
