@@ -469,7 +469,8 @@ def host_info():
 
 def host_workers():
     """Worker processes for the parallel oracle leg: the host CPUs available
-    to this process, at most 16 (the CPU share of one GPU on the box)."""
+    to this process, at most 16 (the CPU share of one GPU on an eight-GPU
+    MI355X node)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
