@@ -294,7 +294,8 @@ def secondary(torch, binding, stream):
         out[name] = {"ms": round(ms, 4), "GBps": round(nb / ms / 1e6, 1), "bytes": nb,
                      "bytes_no_fanout": nbf, "GBps_no_fanout_credit": round(nbf / ms / 1e6, 1),
                      "regions": info["n_regions"], "ms_back_to_back": round(bb, 4),
-                     "GBps_back_to_back": round(nb / bb / 1e6, 1)}
+                     "GBps_back_to_back": round(nb / bb / 1e6, 1),
+                     "plan_us": plan_times(binding, wl, 1000)}
         del src, named
     # The DSV3 layer with every source expert in a buffer of its own (no
     # stacking copy on the training side): 768 source pointers.
