@@ -197,10 +197,10 @@ def high_rank_case(seed, mx=False):
                          else {"kind": "index"}}]}
 
 
-def random_plan_case(seed):
+def random_plan_case(seed, max_bytes=3 << 20):
     """A seeded random plan: 1 to 3 tensors in one plan (so launches share
     the pointer pool and several buckets run in one execute), ranks 1-4,
-    u8 / bf16 / i32 / f64, 4 KB to 3 MB each, meshes of 1-2 dims with 1-4
+    u8 / bf16 / i32 / f64, 4 KB to max_bytes (3 MB) each, meshes of 1-2 dims with 1-4
     slots per dim, Shard / Replicate placements, sides held as padded views
     into shared buffers at random, a fifth of the tensors installed as MXFP8;
     random planning options (fan-out, unit, tiny and thin thresholds) and
@@ -218,7 +218,7 @@ def random_plan_case(seed):
         last = max(1, last_bytes // es)
         if mx:
             last = max(last, int(rng.integers(20, 300)))
-        total = int(rng.integers(4096, 3 << 20)) // es
+        total = int(rng.integers(4096, max_bytes)) // es
         rest = max(1, total // last)
         shape = [last]
         for _ in range(ndim - 2):
