@@ -169,11 +169,16 @@ typedef struct rs_plan_info {
   uint64_t n_regions;            /* regions after coalescing and splitting */
   uint64_t n_regions_bucket[4];  /* bulk, thin (LDS), tiny, mxfp8 */
   uint64_t n_units_bucket[4];    /* work units (grid size) per bucket */
-  uint64_t n_launches;           /* kernel launches per reshard_execute */
+  uint64_t n_launches;           /* kernel launches per reshard_execute (see n_launches_pooled) */
   uint64_t bytes_read;
   uint64_t bytes_written;
   uint64_t bytes_read_no_fanout; /* source bytes if every replica read its own copy */
   uint64_t plan_ns;              /* wall time reshard_plan spent building this plan (CPU) */
+  uint64_t n_launches_pooled;    /* kernel launches when the pointers travel in the kernel
+                                    arguments: reshard_execute_no_alloc, and reshard_execute
+                                    without a device pointer table (equal to n_launches
+                                    unless the plan has more pointers than one launch's
+                                    arguments hold; see reshard_execute) */
 } rs_plan_info;
 
 /* One region of a plan, for inspection (tests, tools).  A region copies
@@ -243,14 +248,27 @@ rs_status reshard_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int
  * microseconds per pointer).  The first
  * call on a device uploads the plan's tables there (a blocking allocation
  * and copy); later calls allocate nothing and only enqueue kernels, so they
- * may be captured into a HIP graph.  Errors: RS_ERR_INVALID,
- * RS_ERR_ALLOC, RS_ERR_HIP (launch or upload failure).  Faults during
- * execution surface on the stream like any HIP error. */
+ * may be captured into a HIP graph.
+ * Pointer tables: one launch's kernel arguments hold 500 pointers.  So that
+ * a batch of many small tensors still moves in one launch per kernel (the
+ * one coalesced call of "NeMo-RL: Optimizing Non-Colocated Refit for
+ * Asynchronous RL", "Optimization #2"), a plan
+ * with more (rs_plan_info.n_launches < n_launches_pooled) keeps on each
+ * device a table of the pointers of every call with a pointer set it has
+ * not seen, up to 8 sets per device, each uploaded by that call (a blocking
+ * allocation and copy; never while `stream` is capturing a graph) and freed
+ * with the plan; a call whose pointers have a table runs n_launches
+ * launches that read them from it, any other call the n_launches_pooled
+ * launches that carry them in their arguments.  The results are the same.
+ * Errors: RS_ERR_INVALID, RS_ERR_ALLOC, RS_ERR_HIP (launch or upload
+ * failure).  Faults during execution surface on the stream like any HIP
+ * error. */
 rs_status reshard_execute(const rs_plan* plan, void* const* src_ptrs, void* const* dst_ptrs,
                           void* stream);
-/* Partial failure: a plan whose pointers exceed one launch's pointer pool
- * runs as several launches (rs_plan_info.n_launches).  All argument checks
- * come before the first launch; if the HIP runtime then refuses launch k,
+/* Partial failure: a plan runs as one launch per kernel kind it uses, and
+ * the pooled form of a plan with more pointers than one launch's arguments
+ * hold as more (rs_plan_info.n_launches, n_launches_pooled).  All argument
+ * checks come before the first launch; if the HIP runtime then refuses launch k,
  * launches 0..k-1 stay enqueued and write their regions, the call returns
  * RS_ERR_HIP naming launch k, and the destinations are only partly
  * installed (execute again once the cause is fixed). */
@@ -258,7 +276,8 @@ rs_status reshard_execute(const rs_plan* plan, void* const* src_ptrs, void* cons
 /* reshard_execute for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc.  Same arguments, checks, launches and results as
- * reshard_execute, but the plan's region tables are not uploaded into an
+ * reshard_execute (in n_launches_pooled launches: no pointer tables), but
+ * the plan's region tables are not uploaded into an
  * allocation of the plan: every call copies them (hipMemcpyAsync on
  * `stream`, from the plan's host image) into a static device array of the
  * library, RESHARD_TABLE_AREA_BYTES long, which each GPU holds from the
@@ -271,7 +290,7 @@ rs_status reshard_execute(const rs_plan* plan, void* const* src_ptrs, void* cons
  * Errors: those of reshard_execute, and RS_ERR_UNSUPPORTED, before anything
  * is copied or launched, for a plan whose tables exceed the area
  * (rs_plan_info gives n_regions; a region takes 128 bytes, an MXFP8 region
- * 208, plus 4 bytes per 256 work units). */
+ * 240, plus 4 bytes per 256 work units). */
 #define RESHARD_TABLE_AREA_BYTES (4u << 20)
 rs_status reshard_execute_no_alloc(const rs_plan* plan, void* const* src_ptrs,
                                    void* const* dst_ptrs, void* stream);

@@ -58,7 +58,8 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [("n_tensors", c_u64), ("n_src_ptrs", c_u64), ("n_dst_ptrs", c_u64),
                 ("n_regions", c_u64), ("n_regions_bucket", c_u64 * 4),
                 ("n_units_bucket", c_u64 * 4), ("n_launches", c_u64), ("bytes_read", c_u64),
-                ("bytes_written", c_u64), ("bytes_read_no_fanout", c_u64), ("plan_ns", c_u64)]
+                ("bytes_written", c_u64), ("bytes_read_no_fanout", c_u64), ("plan_ns", c_u64),
+                ("n_launches_pooled", c_u64)]
 
 
 class Region(ctypes.Structure):
@@ -200,7 +201,8 @@ class Plan:
                 "units": dict(zip(BUCKETS, list(out.n_units_bucket))),
                 "n_launches": out.n_launches, "bytes_read": out.bytes_read,
                 "bytes_written": out.bytes_written,
-                "bytes_read_no_fanout": out.bytes_read_no_fanout, "plan_ns": out.plan_ns}
+                "bytes_read_no_fanout": out.bytes_read_no_fanout, "plan_ns": out.plan_ns,
+                "n_launches_pooled": out.n_launches_pooled}
 
     def region(self, i):
         r = Region()

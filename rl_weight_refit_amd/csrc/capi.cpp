@@ -15,8 +15,10 @@
 #include "rs_device.hpp"
 
 namespace rs {
-// Enqueues one launch of a bucket's kernel on `stream`, whose device is `dev`.
+// Enqueues one launch of a bucket's kernel on `stream`, whose device is `dev`
+// (pointers in the arguments, or in a device table).
 hipError_t launch(uint32_t bucket, uint32_t grid, const LaunchArgs& args, hipStream_t stream, int dev);
+hipError_t launch(uint32_t bucket, uint32_t grid, const TableArgs& args, hipStream_t stream, int dev);
 // Device address of the library's static table area on device `dev` (see
 // kernels.hip); looked up once per device.
 hipError_t table_area(int dev, char** out);
@@ -30,7 +32,17 @@ struct rs_plan {
     int device;
     void* ptr;
   };
-  mutable std::vector<DevTable> tables;  // one upload of d.image per device
+  mutable std::vector<DevTable> tables;  // one upload of d.image (+ d.table_image) per device
+  // Device tables of the caller's pointers for the table form of the
+  // launches: one per pointer set a device has seen, immutable once
+  // uploaded, at most kMaxPointerSets per device.
+  struct PtrTable {
+    int device;
+    std::vector<void*> ptrs;  // sources then destinations; NULL where no region reads it
+    void* ptr;
+  };
+  mutable std::vector<PtrTable> ptr_tables;
+  static constexpr int kMaxPointerSets = 8;
 };
 
 namespace {
@@ -91,15 +103,20 @@ rs_status plan_tables(const rs_plan* plan, int dev, char** base) {
   if (he != hipSuccess) return fail(RS_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(he) + "\n");
   if (cur != dev && (he = hipSetDevice(dev)) != hipSuccess)
     return fail(RS_ERR_HIP, std::string("hipSetDevice: ") + hipGetErrorString(he) + "\n");
+  // The table form's regions follow the pooled form's (whose image ends on
+  // a 256-byte boundary).
   const std::vector<uint8_t>& img = plan->d.image;
+  const std::vector<uint8_t>& timg = plan->d.table_image;
   void* p = nullptr;
   rs_status st = RS_OK;
   std::string msg;
-  he = hipMalloc(&p, img.size());
+  he = hipMalloc(&p, img.size() + timg.size());
   if (he != hipSuccess) {
     st = RS_ERR_ALLOC;
     msg = std::string("hipMalloc of the plan tables: ") + hipGetErrorString(he) + "\n";
-  } else if ((he = hipMemcpy(p, img.data(), img.size(), hipMemcpyHostToDevice)) != hipSuccess) {
+  } else if ((he = hipMemcpy(p, img.data(), img.size(), hipMemcpyHostToDevice)) != hipSuccess ||
+             (!timg.empty() && (he = hipMemcpy(static_cast<char*>(p) + img.size(), timg.data(), timg.size(),
+                                               hipMemcpyHostToDevice)) != hipSuccess)) {
     (void)hipFree(p);
     st = RS_ERR_HIP;
     msg = std::string("upload of the plan tables: ") + hipGetErrorString(he) + "\n";
@@ -109,6 +126,54 @@ rs_status plan_tables(const rs_plan* plan, int dev, char** base) {
   }
   if (cur != dev) (void)hipSetDevice(cur);
   return st == RS_OK ? RS_OK : fail(st, msg);
+}
+
+// Device table of this call's pointers for the table form of the launches,
+// or NULL to run the pooled form: found among the tables of the pointer
+// sets the plan has seen on device `dev`, else uploaded (a blocking
+// allocation and copy) while the device holds fewer than kMaxPointerSets
+// and `stream` is not capturing a graph.  An allocation or copy that fails
+// leaves the pooled form to run; it is not an error.
+void* pointer_table(const rs_plan* plan, int dev, void* const* src_ptrs, void* const* dst_ptrs,
+                    hipStream_t stream) {
+  const rs::PlanData& d = plan->d;
+  const size_t ns = d.src_used.size(), nd = d.dst_used.size();
+  std::vector<void*> want(ns + nd, nullptr);
+  for (size_t i = 0; i < ns; ++i)
+    if (d.src_used[i]) want[i] = src_ptrs[i];
+  for (size_t i = 0; i < nd; ++i)
+    if (d.dst_used[i]) want[ns + i] = dst_ptrs[i];
+  std::lock_guard<std::mutex> lock(plan->mu);
+  int seen = 0;
+  for (const auto& t : plan->ptr_tables) {
+    if (t.device != dev) continue;
+    ++seen;
+    if (t.ptrs == want) return t.ptr;
+  }
+  if (seen >= rs_plan::kMaxPointerSets) return nullptr;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess || (cur != dev && hipSetDevice(dev) != hipSuccess)) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  void* p = nullptr;
+  const size_t bytes = want.size() * sizeof(void*);
+  if (hipMalloc(&p, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    p = nullptr;
+  } else if (hipMemcpy(p, want.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipGetLastError();
+    (void)hipFree(p);
+    p = nullptr;
+  }
+  if (cur != dev) (void)hipSetDevice(cur);
+  if (p) plan->ptr_tables.push_back({dev, std::move(want), p});
+  return p;
 }
 
 // Where execute() finds the plan's device tables.
@@ -211,9 +276,12 @@ rs_status execute(const rs_plan* plan, void* const* src_ptrs, void* const* dst_p
     if (nerr) return fail(RS_ERR_INVALID, err.str());
   }
   char* base = nullptr;
+  void* ptab = nullptr;
   if (where == Tables::kPlanOwned) {
     const rs_status ts = plan_tables(plan, dev, &base);
     if (ts != RS_OK) return ts;
+    if (!d.table_launches.empty())
+      ptab = pointer_table(plan, dev, src_ptrs, dst_ptrs, static_cast<hipStream_t>(stream));
   } else {
     he = rs::table_area(dev, &base);
     if (he != hipSuccess)
@@ -225,22 +293,33 @@ rs_status execute(const rs_plan* plan, void* const* src_ptrs, void* const* dst_p
     if (he != hipSuccess)
       return fail(RS_ERR_HIP, std::string("copy of the plan tables: ") + hipGetErrorString(he) + "\n");
   }
-  for (size_t li = 0; li < d.launches.size(); ++li) {
-    const rs::Launch& L = d.launches[li];
-    rs::LaunchArgs args;
-    std::memset(&args, 0, sizeof(args));
-    args.regions = base + L.regions_off;
-    args.unit_region = L.units_off ? reinterpret_cast<const uint32_t*>(base + L.units_off) : nullptr;
-    args.n_regions = L.n_regions;
-    args.n_units = L.n_units;
-    for (size_t k = 0; k < L.pool.size(); ++k) {
-      const uint32_t e = L.pool[k];
-      args.ptr[k] = (e & rs::kDstBit) ? dst_ptrs[e & ~rs::kDstBit] : src_ptrs[e];
+  // The table form: its regions after the pooled form's, every pointer
+  // from the device table.
+  const std::vector<rs::Launch>& launches = ptab ? d.table_launches : d.launches;
+  char* const lbase = ptab ? base + d.image.size() : base;
+  for (size_t li = 0; li < launches.size(); ++li) {
+    const rs::Launch& L = launches[li];
+    const void* regions = lbase + L.regions_off;
+    const uint32_t* unit_region = L.units_off ? reinterpret_cast<const uint32_t*>(lbase + L.units_off) : nullptr;
+    if (L.table) {
+      const rs::TableArgs args{regions, unit_region, L.n_regions, L.n_units, static_cast<void* const*>(ptab)};
+      he = rs::launch(L.bucket, L.n_units, args, static_cast<hipStream_t>(stream), dev);
+    } else {
+      rs::LaunchArgs args;
+      std::memset(&args, 0, sizeof(args));
+      args.regions = regions;
+      args.unit_region = unit_region;
+      args.n_regions = L.n_regions;
+      args.n_units = L.n_units;
+      for (size_t k = 0; k < L.pool.size(); ++k) {
+        const uint32_t e = L.pool[k];
+        args.ptr[k] = (e & rs::kDstBit) ? dst_ptrs[e & ~rs::kDstBit] : src_ptrs[e];
+      }
+      he = rs::launch(L.bucket, L.n_units, args, static_cast<hipStream_t>(stream), dev);
     }
-    he = rs::launch(L.bucket, L.n_units, args, static_cast<hipStream_t>(stream), dev);
     if (he != hipSuccess) {
       std::ostringstream m;
-      m << "kernel launch " << li << " of " << d.launches.size() << ": " << hipGetErrorString(he)
+      m << "kernel launch " << li << " of " << launches.size() << ": " << hipGetErrorString(he)
         << (li ? " (the earlier launches stay enqueued)" : "") << "\n";
       return fail(RS_ERR_HIP, m.str());
     }
@@ -305,6 +384,9 @@ void reshard_plan_destroy(rs_plan* plan) {
   int cur = -1;
   const bool have_cur = hipGetDevice(&cur) == hipSuccess;
   for (const auto& t : plan->tables) {
+    if (hipSetDevice(t.device) == hipSuccess) (void)hipFree(t.ptr);
+  }
+  for (const auto& t : plan->ptr_tables) {
     if (hipSetDevice(t.device) == hipSuccess) (void)hipFree(t.ptr);
   }
   if (have_cur && !plan->tables.empty()) (void)hipSetDevice(cur);

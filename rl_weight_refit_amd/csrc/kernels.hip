@@ -191,10 +191,24 @@ __device__ __forceinline__ uint32_t sc_pool(const MxRegion* R, uint32_t j) {
   return pool_field(R, 2 + kMaxFan + j);
 }
 
+// Pointer pool entry i of a launch.  Every kernel is built twice: with the
+// pointers in its arguments (LaunchArgs), and with them in a device table of
+// the plan (TableArgs) for launches with more pointers than the arguments
+// hold.  The table is read through the constant address space (it does not
+// change while the kernel runs), so a uniform index is a scalar load, as for
+// the arguments; the pointer is marked global so that the accesses through
+// it stay global (not flat) instructions.
+typedef __attribute__((address_space(4))) const uint64_t const_u64;
+typedef __attribute__((address_space(1))) char global_char;
+__device__ __forceinline__ void* pool_ptr(const LaunchArgs& a, uint32_t i) { return a.ptr[i]; }
+__device__ __forceinline__ void* pool_ptr(const TableArgs& a, uint32_t i) {
+  return (void*)(global_char*)(((const_u64*)(a.ptab))[i]);
+}
+
 // Region of a work unit: the chunk table brackets it, a short binary search
 // over the regions' first units finds it (all loads are uniform).
-template <class Reg>
-__device__ __forceinline__ const Reg* find_region(const LaunchArgs& a, uint32_t unit) {
+template <class Reg, class Args>
+__device__ __forceinline__ const Reg* find_region(const Args& a, uint32_t unit) {
   const Reg* regs = static_cast<const Reg*>(a.regions);
   const uint32_t c = unit >> kChunkShift;
   uint32_t lo = __builtin_amdgcn_readfirstlane(a.unit_region[c]);
@@ -298,8 +312,8 @@ __device__ __forceinline__ void block_copy_bytes(char* d, const char* s, uint32_
 
 // Short aligned rows: lane groups of L lanes per row; each lane holds M
 // vectors of each of U rows before storing them.
-template <bool kFan1, int M>
-__device__ __forceinline__ void bulk_short_rows(const LaunchArgs& a, const CopyRegion* R,
+template <bool kFan1, int M, class Args>
+__device__ __forceinline__ void bulk_short_rows(const Args& a, const CopyRegion* R,
                                                 const char* sp, char* dp0, uint64_t dst_off,
                                                 uint32_t r0, uint32_t r1, uint32_t vpr, uint32_t L,
                                                 uint32_t e0, uint32_t e1, uint32_t nouter,
@@ -327,7 +341,7 @@ __device__ __forceinline__ void bulk_short_rows(const LaunchArgs& a, const CopyR
       }
     }
     for (uint32_t j = 0; j < nd; ++j) {
-      char* d = kFan1 ? dp0 : static_cast<char*>(a.ptr[dst_pool(R, j)]) + dst_off;
+      char* d = kFan1 ? dp0 : static_cast<char*>(pool_ptr(a, dst_pool(R, j))) + dst_off;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint32_t r = rb + u * step;
@@ -348,8 +362,8 @@ __device__ __forceinline__ void bulk_short_rows(const LaunchArgs& a, const CopyR
 // vectors is one load batch, whatever vpr is.  The row is floor(f / vpr),
 // computed as (f * ceil(2^32 / vpr)) >> 32: exact for f < 2^20 and vpr < 2^11
 // (the error term f / 2^32 stays below the smallest gap 1 / vpr).
-template <bool kFan1>
-__device__ __forceinline__ void bulk_short_flat(const LaunchArgs& a, const CopyRegion* R,
+template <bool kFan1, class Args>
+__device__ __forceinline__ void bulk_short_flat(const Args& a, const CopyRegion* R,
                                                 const char* sp, uint64_t dst_off, uint32_t r0,
                                                 uint32_t r1, uint32_t vpr, uint64_t s0, uint64_t d0,
                                                 uint32_t nd) {
@@ -370,7 +384,7 @@ __device__ __forceinline__ void bulk_short_flat(const LaunchArgs& a, const CopyR
       if (f < nvec) x[k] = ld16(sp + uint64_t(r) * s0 + 16ull * v);
     }
     for (uint32_t j = 0; j < nd; ++j) {
-      char* d = static_cast<char*>(a.ptr[dst_pool(R, kFan1 ? 0 : j)]) + dst_off;
+      char* d = static_cast<char*>(pool_ptr(a, dst_pool(R, kFan1 ? 0 : j))) + dst_off;
 #pragma unroll
       for (int k = 0; k < U; ++k)
         if (f0 + k * kThreads + tid < nvec) st16(d + o[k], x[k]);
@@ -391,8 +405,8 @@ constexpr uint32_t kWaves = kThreads / 64;
 
 // Rows with at most one outer dim (row r at r * stride): lane by lane, group
 // vector f is row f / vpr (magic division, exact while f * vpr < 2^32).
-template <bool kFan1>
-__device__ __forceinline__ void bulk_spread_flat(const LaunchArgs& a, const CopyRegion* R,
+template <bool kFan1, class Args>
+__device__ __forceinline__ void bulk_spread_flat(const Args& a, const CopyRegion* R,
                                                  const char* sp, uint64_t dst_off, uint32_t g0,
                                                  uint32_t j, uint32_t nvec, uint32_t vpr,
                                                  uint64_t s0, uint64_t d0, uint32_t nd) {
@@ -413,7 +427,7 @@ __device__ __forceinline__ void bulk_spread_flat(const LaunchArgs& a, const Copy
       if (t < nvec) x[k] = ld16(sp + r * s0 + 16ull * v);
     }
     for (uint32_t jd = 0; jd < nd; ++jd) {
-      char* d = static_cast<char*>(a.ptr[dst_pool(R, kFan1 ? 0 : jd)]) + dst_off;
+      char* d = static_cast<char*>(pool_ptr(a, dst_pool(R, kFan1 ? 0 : jd))) + dst_off;
 #pragma unroll
       for (int k = 0; k < U; ++k)
         if (t0 + k * kThreads + tid < nvec) st16(d + o[k], x[k]);
@@ -426,8 +440,8 @@ __device__ __forceinline__ void bulk_spread_flat(const LaunchArgs& a, const Copy
 // arithmetic is uniform.  A wave's pieces are kWaves * kSpread apart in the
 // group; it splits its first piece's row into outer indices once and then
 // advances piece column and indices by carries, with no division per piece.
-template <bool kFan1>
-__device__ __forceinline__ void bulk_spread_rows(const LaunchArgs& a, const CopyRegion* R,
+template <bool kFan1, class Args>
+__device__ __forceinline__ void bulk_spread_rows(const Args& a, const CopyRegion* R,
                                                  const char* sp, uint64_t dst_off, uint32_t g0,
                                                  uint32_t j, uint32_t npu, uint32_t ppr,
                                                  uint32_t e0, uint32_t e1, uint32_t nouter,
@@ -477,7 +491,7 @@ __device__ __forceinline__ void bulk_spread_rows(const LaunchArgs& a, const Copy
       }
     }
     for (uint32_t jd = 0; jd < nd; ++jd) {
-      char* d = static_cast<char*>(a.ptr[dst_pool(R, kFan1 ? 0 : jd)]) + dst_off;
+      char* d = static_cast<char*>(pool_ptr(a, dst_pool(R, kFan1 ? 0 : jd))) + dst_off;
 #pragma unroll
       for (int k = 0; k < U; ++k)
         if (l0 + k * kWaves + wave < npu) st16(d + o[k], x[k]);
@@ -621,8 +635,8 @@ __device__ __forceinline__ MisSpan mis_span(const char* src, const char* dst, ui
   return m;
 }
 
-template <bool kFan1>
-__device__ __forceinline__ void bulk_misaligned_lds(const LaunchArgs& a, const CopyRegion* R, const char* sp,
+template <bool kFan1, class Args>
+__device__ __forceinline__ void bulk_misaligned_lds(const Args& a, const CopyRegion* R, const char* sp,
                                                     char* dp0, uint64_t dst_off, uint32_t r0, uint32_t rows,
                                                     uint32_t n, uint32_t lm, uint32_t e0, uint32_t e1,
                                                     uint32_t nouter, uint64_t s0, uint64_t s1, uint64_t s2,
@@ -665,7 +679,7 @@ __device__ __forceinline__ void bulk_misaligned_lds(const LaunchArgs& a, const C
   const uint32_t blocks = rows * mb;
   const uint64_t magb = ((uint64_t(1) << 32) + mb - 1) / mb;
   for (uint32_t jd = 0; jd < nd; ++jd) {
-    char* dp = kFan1 ? dp0 : static_cast<char*>(a.ptr[dst_pool(R, jd)]) + dst_off;
+    char* dp = kFan1 ? dp0 : static_cast<char*>(pool_ptr(a, dst_pool(R, jd))) + dst_off;
     for (uint32_t f = tid; f < blocks; f += kThreads) {
       const uint32_t i = uint32_t((uint64_t(f) * magb) >> 32), b = f - i * mb;
       char* dst = dp + row_off(r0 + i, e0, e1, nouter, d0, d1, d2);
@@ -694,8 +708,8 @@ __device__ __forceinline__ void bulk_misaligned_lds(const LaunchArgs& a, const C
   }
 }
 
-template <bool kFan1>
-__device__ __forceinline__ void bulk_body(const LaunchArgs& a, const CopyRegion* R, uint32_t unit,
+template <bool kFan1, class Args>
+__device__ __forceinline__ void bulk_body(const Args& a, const CopyRegion* R, uint32_t unit,
                                           char* mis_tile) {
   const uint32_t tid = threadIdx.x;
   const uint64_t src_off = R->src_off, dst_off = R->dst_off;
@@ -705,13 +719,13 @@ __device__ __forceinline__ void bulk_body(const LaunchArgs& a, const CopyRegion*
   const uint32_t rpu = R->rows_per_unit, ub = R->unit_begin, flags = R->flags;
   const uint32_t nd = kFan1 ? 1u : n_dst_of(R);
   const uint32_t nouter = flags & kFlagOuterMask;
-  const char* sp = static_cast<const char*>(a.ptr[src_pool(R)]) + src_off;
-  char* dp0 = static_cast<char*>(a.ptr[dst_pool(R, 0)]) + dst_off;
+  const char* sp = static_cast<const char*>(pool_ptr(a, src_pool(R))) + src_off;
+  char* dp0 = static_cast<char*>(pool_ptr(a, dst_pool(R, 0))) + dst_off;
 
   uint32_t al = (flags >> 8) & 15u;
   al |= uint32_t(reinterpret_cast<uintptr_t>(sp) & 15u);
   for (uint32_t j = 0; j < nd; ++j)
-    al |= uint32_t((reinterpret_cast<uintptr_t>(a.ptr[dst_pool(R, j)]) + dst_off) & 15u);
+    al |= uint32_t((reinterpret_cast<uintptr_t>(pool_ptr(a, dst_pool(R, j))) + dst_off) & 15u);
 
   const uint32_t r0 = (unit - ub) * rpu;
   const uint32_t r1 = min(r0 + rpu, rows);
@@ -748,7 +762,7 @@ __device__ __forceinline__ void bulk_body(const LaunchArgs& a, const CopyRegion*
         for (int k = 0; k < RS_UNROLL; ++k)
           if (v + k * kThreads < vpr) x[k] = ld16(s + 16ull * (v + k * kThreads));
         for (uint32_t j = 0; j < nd; ++j) {
-          char* d = (kFan1 ? dp0 : static_cast<char*>(a.ptr[dst_pool(R, j)]) + dst_off) + dof;
+          char* d = (kFan1 ? dp0 : static_cast<char*>(pool_ptr(a, dst_pool(R, j))) + dst_off) + dof;
 #pragma unroll
           for (int k = 0; k < RS_UNROLL; ++k)
             if (v + k * kThreads < vpr) st16(d + 16ull * (v + k * kThreads), x[k]);
@@ -780,8 +794,8 @@ __device__ __forceinline__ void bulk_body(const LaunchArgs& a, const CopyRegion*
     const uint32_t lm = (inner + 15u) / 16u + 1u;
     bool congruent = true;
     for (uint32_t j = 1; j < nd; ++j)
-      congruent &= ((reinterpret_cast<uintptr_t>(a.ptr[dst_pool(R, j)]) ^ reinterpret_cast<uintptr_t>(
-                        a.ptr[dst_pool(R, 0)])) & 15u) == 0;
+      congruent &= ((reinterpret_cast<uintptr_t>(pool_ptr(a, dst_pool(R, j))) ^ reinterpret_cast<uintptr_t>(
+                        pool_ptr(a, dst_pool(R, 0)))) & 15u) == 0;
     if (congruent && inner >= kMisMinRow && uint64_t(r1 - r0) * lm * 16u <= kMisTile &&
         (r1 - r0) * 32u <= uint32_t(kMisEdge) * kThreads) {
       bulk_misaligned_lds<kFan1>(a, R, sp, dp0, dst_off, r0, r1 - r0, inner, lm, e0, e1, nouter, s0, s1, s2,
@@ -792,13 +806,14 @@ __device__ __forceinline__ void bulk_body(const LaunchArgs& a, const CopyRegion*
     // Misaligned: funnel-shifted 16-byte vectors numbered across the unit,
     // once per destination (each replica may sit at its own alignment).
     for (uint32_t j = 0; j < nd; ++j) {
-      char* dp = kFan1 ? dp0 : static_cast<char*>(a.ptr[dst_pool(R, j)]) + dst_off;
+      char* dp = kFan1 ? dp0 : static_cast<char*>(pool_ptr(a, dst_pool(R, j))) + dst_off;
       bulk_misaligned_rows(sp, dp, r0, r1, inner, e0, e1, nouter, s0, s1, s2, d0, d1, d2);
     }
   }
 }
 
-__global__ __launch_bounds__(kThreads, RS_BULK_MIN_WAVES) void rs_bulk_kernel(LaunchArgs a) {
+template <class Args>
+__global__ __launch_bounds__(kThreads, RS_BULK_MIN_WAVES) void rs_bulk_kernel(Args a) {
   // One workgroup per work unit (looping workgroups measured slower).
   const uint32_t unit = unit_of_block<RS_XCD_MAP != 0>(blockIdx.x, gridDim.x, RS_XCD_CHUNK);
   const CopyRegion* R = find_region<CopyRegion>(a, unit);
@@ -883,15 +898,15 @@ __device__ __forceinline__ void group_store(char* D, const char* lds, uint32_t c
 // every member writes its packed destination rows from there.
 // kSw: some member reads granules of 4 bytes or less; slots swizzled
 // (lds_swz8) where the block goes straight into LDS.
-template <bool kSw>
-__device__ __forceinline__ void thin_group_body(const LaunchArgs& a, const CopyRegion* R, uint32_t ul, char* tile,
+template <bool kSw, class Args>
+__device__ __forceinline__ void thin_group_body(const Args& a, const CopyRegion* R, uint32_t ul, char* tile,
                                                 uint64_t lo, uint32_t S) {
   const uint32_t tid = threadIdx.x;
   const uint32_t gm = (R->flags >> 16) & 255u;
   const uint32_t rows = R->rows, rpu = R->rows_per_unit;
   const uint32_t e0 = R->e0, e1 = R->e1, nouter = R->flags & kFlagOuterMask;
   const uint64_t s0 = R->sstr[0], s1 = R->sstr[1], s2 = R->sstr[2];
-  const char* base = static_cast<const char*>(a.ptr[src_pool(R)]) + lo;
+  const char* base = static_cast<const char*>(pool_ptr(a, src_pool(R))) + lo;
   const uint32_t r0 = ul * rpu, r1 = min(r0 + rpu, rows), T = r1 - r0;
   uint32_t sh = 0;
   bool swz = false;
@@ -960,7 +975,7 @@ __device__ __forceinline__ void thin_group_body(const LaunchArgs& a, const CopyR
     const uint32_t nbytes = T * inner;
     const uint32_t G = low_granule((sh + cm) | S | inner);
     for (uint32_t j = 0; j < nd; ++j) {
-      char* D = static_cast<char*>(a.ptr[dst_pool(M, j)]) + M->dst_off + uint64_t(r0) * inner;
+      char* D = static_cast<char*>(pool_ptr(a, dst_pool(M, j))) + M->dst_off + uint64_t(r0) * inner;
       if (kSw && swz) {
         switch (G) {
           case 4: group_store<4, true>(D, lds, cm, S, inner, nbytes, tid); break;
@@ -980,8 +995,8 @@ __device__ __forceinline__ void thin_group_body(const LaunchArgs& a, const CopyR
   }
 }
 
-template <bool kSw>
-__device__ __forceinline__ void thin_group_unit(const LaunchArgs& a, const CopyRegion* R, uint32_t ul, char* tile) {
+template <bool kSw, class Args>
+__device__ __forceinline__ void thin_group_unit(const Args& a, const CopyRegion* R, uint32_t ul, char* tile) {
   const uint32_t gm = (R->flags >> 16) & 255u;
   uint64_t lo = R->src_off, hi = R->src_off + R->inner;
   for (uint32_t m = 1; m < gm; ++m) {
@@ -994,15 +1009,16 @@ __device__ __forceinline__ void thin_group_unit(const LaunchArgs& a, const CopyR
 // Thin sibling groups loaded whole (launches of their own: this path needs
 // more registers than the thin kernel's others).  kSw: groups with a member
 // whose LDS reads are 4 bytes or narrower (swizzled LDS slots).
-template <bool kSw>
-__global__ __launch_bounds__(kThreads) void rs_thin_group_kernel(LaunchArgs a) {
+template <bool kSw, class Args>
+__global__ __launch_bounds__(kThreads) void rs_thin_group_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) char tile[kGroupTile + 16];
   const uint32_t unit = unit_of_block<RS_THIN_XCD_CHUNK != 0>(blockIdx.x, gridDim.x, RS_THIN_XCD_CHUNK);
   const CopyRegion* R = find_region<CopyRegion>(a, unit);
   thin_group_unit<kSw>(a, R, unit - R->unit_begin, tile);
 }
 
-__global__ __launch_bounds__(kThreads) void rs_thin_kernel(LaunchArgs a) {
+template <class Args>
+__global__ __launch_bounds__(kThreads) void rs_thin_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) char tile[kThinTile + 16];
   const uint32_t tid = threadIdx.x;
   const uint32_t unit = unit_of_block<RS_THIN_XCD_CHUNK != 0>(blockIdx.x, gridDim.x, RS_THIN_XCD_CHUNK);
@@ -1026,12 +1042,12 @@ __global__ __launch_bounds__(kThreads) void rs_thin_kernel(LaunchArgs a) {
   const uint32_t rpu = R->rows_per_unit, flags = R->flags;
   const uint32_t nd = n_dst_of(R);
   const uint32_t nouter = flags & kFlagOuterMask;
-  const char* sp = static_cast<const char*>(a.ptr[src_pool(R)]) + src_off;
+  const char* sp = static_cast<const char*>(pool_ptr(a, src_pool(R))) + src_off;
 
   uint32_t al = (flags >> 8) & 15u;
   al |= uint32_t(reinterpret_cast<uintptr_t>(sp) & 15u);
   for (uint32_t j = 0; j < nd; ++j)
-    al |= uint32_t((reinterpret_cast<uintptr_t>(a.ptr[dst_pool(R, j)]) + dst_off) & 15u);
+    al |= uint32_t((reinterpret_cast<uintptr_t>(pool_ptr(a, dst_pool(R, j))) + dst_off) & 15u);
   const uint32_t g = low_granule(al);
   const uint32_t gpr = inner / g;
 
@@ -1044,7 +1060,7 @@ __global__ __launch_bounds__(kThreads) void rs_thin_kernel(LaunchArgs a) {
   if (flags & kFlagDstPacked) {
     // Gather strided source rows into LDS (congruent with the first
     // destination mod 16), then write the contiguous destination block.
-    const char* D0 = static_cast<const char*>(a.ptr[dst_pool(R, 0)]) + dst_off + uint64_t(r0) * inner;
+    const char* D0 = static_cast<const char*>(pool_ptr(a, dst_pool(R, 0))) + dst_off + uint64_t(r0) * inner;
     const uint32_t sh = uint32_t(reinterpret_cast<uintptr_t>(D0) & 15u);
     for (uint32_t f = tid; f < total; f += kThreads) {
       const uint32_t row = f / gpr;
@@ -1054,7 +1070,7 @@ __global__ __launch_bounds__(kThreads) void rs_thin_kernel(LaunchArgs a) {
     }
     __syncthreads();
     for (uint32_t j = 0; j < nd; ++j) {
-      char* Dj = static_cast<char*>(a.ptr[dst_pool(R, j)]) + dst_off + uint64_t(r0) * inner;
+      char* Dj = static_cast<char*>(pool_ptr(a, dst_pool(R, j))) + dst_off + uint64_t(r0) * inner;
       if ((reinterpret_cast<uintptr_t>(Dj) & 15u) == sh)
         block_copy_congruent(Dj, tile + sh, nbytes, tid);
       else
@@ -1071,7 +1087,7 @@ __global__ __launch_bounds__(kThreads) void rs_thin_kernel(LaunchArgs a) {
       const uint32_t k = f - row * gpr;
       const uint64_t dof = row_off(r0 + row, e0, e1, nouter, d0, d1, d2);
       for (uint32_t j = 0; j < nd; ++j) {
-        char* d = static_cast<char*>(a.ptr[dst_pool(R, j)]) + dst_off + dof + uint64_t(k) * g;
+        char* d = static_cast<char*>(pool_ptr(a, dst_pool(R, j))) + dst_off + dof + uint64_t(k) * g;
         copy_granule(d, tile + sh + row * inner + k * g, g);
       }
     }
@@ -1083,7 +1099,7 @@ __global__ __launch_bounds__(kThreads) void rs_thin_kernel(LaunchArgs a) {
       const uint64_t so = row_off(r0 + row, e0, e1, nouter, s0, s1, s2);
       const uint64_t dof = row_off(r0 + row, e0, e1, nouter, d0, d1, d2);
       for (uint32_t j = 0; j < nd; ++j) {
-        char* d = static_cast<char*>(a.ptr[dst_pool(R, j)]) + dst_off + dof + uint64_t(k) * g;
+        char* d = static_cast<char*>(pool_ptr(a, dst_pool(R, j))) + dst_off + dof + uint64_t(k) * g;
         copy_granule(d, sp + so + uint64_t(k) * g, g);
       }
     }
@@ -1094,11 +1110,12 @@ __global__ __launch_bounds__(kThreads) void rs_thin_kernel(LaunchArgs a) {
 // tiny (wave prefix sum over many small regions)
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ uint32_t region_granule(const LaunchArgs& a, const CopyRegion* R) {
+template <class Args>
+__device__ __forceinline__ uint32_t region_granule(const Args& a, const CopyRegion* R) {
   uint32_t al = (R->flags >> 8) & 15u;
-  al |= uint32_t((reinterpret_cast<uintptr_t>(a.ptr[R->src_ptr]) + R->src_off) & 15u);
+  al |= uint32_t((reinterpret_cast<uintptr_t>(pool_ptr(a, R->src_ptr)) + R->src_off) & 15u);
   for (uint32_t j = 0; j < R->n_dst; ++j)
-    al |= uint32_t((reinterpret_cast<uintptr_t>(a.ptr[R->dst_ptr[j]]) + R->dst_off) & 15u);
+    al |= uint32_t((reinterpret_cast<uintptr_t>(pool_ptr(a, R->dst_ptr[j])) + R->dst_off) & 15u);
   return low_granule(al);
 }
 
@@ -1137,7 +1154,8 @@ __device__ __forceinline__ void store_granule(char* p, uint32_t g, u32x4 v) {
 // a time so their loads overlap.
 constexpr int kTinyInFlight = 4;
 
-__global__ __launch_bounds__(kThreads) void rs_tiny_kernel(LaunchArgs a) {
+template <class Args>
+__global__ __launch_bounds__(kThreads) void rs_tiny_kernel(Args a) {
   __shared__ uint32_t start[kThreads];
   __shared__ uint32_t gpr_of[kThreads];
   __shared__ uint8_t gsize[kThreads];
@@ -1191,7 +1209,7 @@ __global__ __launch_bounds__(kThreads) void rs_tiny_kernel(LaunchArgs a) {
         const uint64_t so = row_off(row, R->e0, R->e1, nouter, R->sstr[0], R->sstr[1], R->sstr[2]);
         dofs[u] = R->dst_off + row_off(row, R->e0, R->e1, nouter, R->dstr[0], R->dstr[1], R->dstr[2]) +
                   uint64_t(k) * gl;
-        v[u] = load_granule(static_cast<const char*>(a.ptr[R->src_ptr]) + R->src_off + so + uint64_t(k) * gl, gl);
+        v[u] = load_granule(static_cast<const char*>(pool_ptr(a, R->src_ptr)) + R->src_off + so + uint64_t(k) * gl, gl);
       }
     }
 #pragma unroll
@@ -1200,7 +1218,7 @@ __global__ __launch_bounds__(kThreads) void rs_tiny_kernel(LaunchArgs a) {
         const CopyRegion* R = regs + base + owner[u];
         const uint32_t gl = gsize[wave * 64 + owner[u]];
         for (uint32_t j = 0; j < R->n_dst; ++j)
-          store_granule(static_cast<char*>(a.ptr[R->dst_ptr[j]]) + dofs[u], gl, v[u]);
+          store_granule(static_cast<char*>(pool_ptr(a, R->dst_ptr[j])) + dofs[u], gl, v[u]);
       }
     }
   }
@@ -1316,7 +1334,8 @@ struct MxFields {
   uint64_t t0, t1, t2;
 };
 
-__device__ __forceinline__ MxFields mx_fields(const LaunchArgs& a, const MxRegion* R) {
+template <class Args>
+__device__ __forceinline__ MxFields mx_fields(const Args& a, const MxRegion* R) {
   MxFields f;
   f.src_off = R->src_off;
   f.dst_off = R->dst_off;
@@ -1330,14 +1349,14 @@ __device__ __forceinline__ MxFields mx_fields(const LaunchArgs& a, const MxRegio
   f.nouter = R->flags & kFlagOuterMask;
   f.sc_inner = R->sc_inner;
   f.nd = n_dst_of(R);
-  f.sp = static_cast<const char*>(a.ptr[src_pool(R)]) + f.src_off;
-  f.dk = static_cast<char*>(a.ptr[dst_pool(R, 0)]);
-  f.sk = static_cast<char*>(a.ptr[sc_pool(R, 0)]);
+  f.sp = static_cast<const char*>(pool_ptr(a, src_pool(R))) + f.src_off;
+  f.dk = static_cast<char*>(pool_ptr(a, dst_pool(R, 0)));
+  f.sk = static_cast<char*>(pool_ptr(a, sc_pool(R, 0)));
   f.split = R->split;
   f.sp2 = nullptr;
   f.t0 = f.t1 = f.t2 = 0;
   if (f.split < f.inner) {
-    f.sp2 = static_cast<const char*>(a.ptr[pool_field(R, 2 + 2 * kMaxFan)]) + R->src2_off;
+    f.sp2 = static_cast<const char*>(pool_ptr(a, pool_field(R, 2 + 2 * kMaxFan))) + R->src2_off;
     f.t0 = R->sstr2[0];
     f.t1 = R->sstr2[1];
     f.t2 = R->sstr2[2];
@@ -1353,8 +1372,8 @@ __device__ __forceinline__ u32x4 keep_elems(u32x4 x, int n) {
   return u32x4{keep(x.x, 0), keep(x.y, 1), keep(x.z, 2), keep(x.w, 3)};
 }
 
-template <bool kOneRow, bool kFan1, bool kTwo = false>
-__device__ __forceinline__ void mx_unit(const LaunchArgs& a, const MxRegion* R, const MxFields& f, uint32_t r0,
+template <bool kOneRow, bool kFan1, bool kTwo = false, class Args>
+__device__ __forceinline__ void mx_unit(const Args& a, const MxRegion* R, const MxFields& f, uint32_t r0,
                                         uint32_t nr, u32x4* stage, uint8_t* sc_stage) {
   constexpr uint32_t K = kMxSlots / kMxThreads;
   const uint32_t tid = threadIdx.x;
@@ -1540,7 +1559,7 @@ __device__ __forceinline__ void mx_unit(const LaunchArgs& a, const MxRegion* R, 
     if (nvalid > 0) {
       const uint64_t doff = dst_off_r + (kOneRow ? do1 : row_off(r0 + rl, e0, e1, nouter, d0, d1, d2)) + col;
       for (uint32_t j = 0; j < (kFan1 ? 1u : nd); ++j) {
-        char* d = (kFan1 ? dk : static_cast<char*>(a.ptr[dst_pool(R, j)])) + doff;
+        char* d = (kFan1 ? dk : static_cast<char*>(pool_ptr(a, dst_pool(R, j)))) + doff;
         if (nvalid == 16 && (reinterpret_cast<uintptr_t>(d) & 15u) == 0) {
           __builtin_nontemporal_store(c.v, reinterpret_cast<u32x4*>(d));
         } else {
@@ -1562,13 +1581,13 @@ __device__ __forceinline__ void mx_unit(const LaunchArgs& a, const MxRegion* R, 
       const uint64_t so = sc_off_r + row_off(r0 + rl, e0, e1, nouter, c0, c1, c2) + uint64_t(b) * sc_inner;
       const char v = char(sc_stage[t]);
       for (uint32_t j = 0; j < (kFan1 ? 1u : nd); ++j)
-        __builtin_nontemporal_store(v, (kFan1 ? sk : static_cast<char*>(a.ptr[sc_pool(R, j)])) + so);
+        __builtin_nontemporal_store(v, (kFan1 ? sk : static_cast<char*>(pool_ptr(a, sc_pool(R, j)))) + so);
     }
   }
 }
 
-template <bool kOneRow>
-__device__ __forceinline__ void mx_unit_fan(const LaunchArgs& a, const MxRegion* R, const MxFields& f,
+template <bool kOneRow, class Args>
+__device__ __forceinline__ void mx_unit_fan(const Args& a, const MxRegion* R, const MxFields& f,
                                             uint32_t r0, uint32_t nr, u32x4* stage, uint8_t* sc_stage) {
   if (f.split < f.inner)
     mx_unit<kOneRow, false, true>(a, R, f, r0, nr, stage, sc_stage);
@@ -1578,7 +1597,8 @@ __device__ __forceinline__ void mx_unit_fan(const LaunchArgs& a, const MxRegion*
     mx_unit<kOneRow, false>(a, R, f, r0, nr, stage, sc_stage);
 }
 
-__global__ __launch_bounds__(kMxThreads, RS_MX_MIN_WAVES) void rs_mx_kernel(LaunchArgs a) {
+template <class Args>
+__global__ __launch_bounds__(kMxThreads, RS_MX_MIN_WAVES) void rs_mx_kernel(Args a) {
   __shared__ u32x4 stage[kMxSlots];
   __shared__ __attribute__((aligned(16))) uint8_t sc_stage[kMxSlots / 4];
   const uint32_t unit = unit_of_block<RS_MX_XCD_MAP != 0>(blockIdx.x, gridDim.x, RS_MX_XCD_CHUNK);
@@ -1662,24 +1682,33 @@ hipError_t table_area(int dev, char** out) {
   return hipSuccess;
 }
 
-hipError_t launch(uint32_t bucket, uint32_t grid, const LaunchArgs& args, hipStream_t stream, int dev) {
+template <class Args>
+hipError_t launch_kind(uint32_t bucket, uint32_t grid, const Args& args, hipStream_t stream, int dev) {
   if (grid == 0) return hipSuccess;
   switch (bucket) {
     case kBulk:
-      hipLaunchKernelGGL(rs_bulk_kernel, dim3(grid), dim3(kThreads), bulk_lds_pad(dev), stream, args);
+      hipLaunchKernelGGL(rs_bulk_kernel<Args>, dim3(grid), dim3(kThreads), bulk_lds_pad(dev), stream, args);
       break;
-    case kThin: hipLaunchKernelGGL(rs_thin_kernel, dim3(grid), dim3(kThreads), 0, stream, args); break;
+    case kThin: hipLaunchKernelGGL(rs_thin_kernel<Args>, dim3(grid), dim3(kThreads), 0, stream, args); break;
     case kThinGroup:
-      hipLaunchKernelGGL(rs_thin_group_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, args);
+      hipLaunchKernelGGL((rs_thin_group_kernel<false, Args>), dim3(grid), dim3(kThreads), 0, stream, args);
       break;
     case kThinGroupNarrow:
-      hipLaunchKernelGGL(rs_thin_group_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, args);
+      hipLaunchKernelGGL((rs_thin_group_kernel<true, Args>), dim3(grid), dim3(kThreads), 0, stream, args);
       break;
-    case kTiny: hipLaunchKernelGGL(rs_tiny_kernel, dim3(grid), dim3(kThreads), 0, stream, args); break;
-    case kMx: hipLaunchKernelGGL(rs_mx_kernel, dim3(grid), dim3(kMxThreads), 0, stream, args); break;
+    case kTiny: hipLaunchKernelGGL(rs_tiny_kernel<Args>, dim3(grid), dim3(kThreads), 0, stream, args); break;
+    case kMx: hipLaunchKernelGGL(rs_mx_kernel<Args>, dim3(grid), dim3(kMxThreads), 0, stream, args); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch(uint32_t bucket, uint32_t grid, const LaunchArgs& args, hipStream_t stream, int dev) {
+  return launch_kind(bucket, grid, args, stream, dev);
+}
+
+hipError_t launch(uint32_t bucket, uint32_t grid, const TableArgs& args, hipStream_t stream, int dev) {
+  return launch_kind(bucket, grid, args, stream, dev);
 }
 
 }  // namespace rs

@@ -1284,222 +1284,256 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
   }
 
   // Launch passes: one per bucket, then the thin groups loaded whole (with
-  // and without narrow members).
-  for (uint32_t pass = 0; pass <= kBuckets + 1; ++pass) {
-    const uint32_t bucket = pass < kBuckets ? pass : uint32_t(kThin);
-    const uint32_t kernel = pass < kBuckets ? pass : pass == kBuckets ? uint32_t(kThinGroup) : kThinGroupNarrow;
-    const uint8_t want_whole = pass < kBuckets ? 0 : pass == kBuckets ? 1 : 2;
-    std::vector<const Final*> list;
-    list.reserve(fin.size());
-    for (size_t q = 0; q < fin.size(); ++q)
-      if (fin[q].bucket == bucket && (bucket != kThin || whole[q] == want_whole))
-        list.push_back(&fin[q]);
-    size_t i = 0;
-    while (i < list.size()) {
-      // Greedy group: regions in order while their pointers fit the pool.
-      std::vector<uint32_t> members;    // pool slot -> caller pointer index (| kDstBit)
-      std::vector<const Final*> batch;
-      members.reserve(kPool);
-      batch.reserve(list.size() - i);
-      uint64_t units = 0;
+  // and without narrow members).  Pooled form (table == false): each launch
+  // takes regions in order while their pointers fit the kernel-argument pool
+  // of kPool entries (pool_cut tells whether that split any pass).  Table
+  // form: no pool limit; pool indices are indices into the caller's
+  // pointers, source pointers first, then destination pointers (the device
+  // table reshard_execute fills).  record: this form's regions and counts
+  // go into the plan summary.
+  bool pool_cut = false;
+  auto emit = [&](bool table, std::vector<uint8_t>& image, std::vector<Launch>& launches, bool record) {
+    for (uint32_t pass = 0; pass <= kBuckets + 1; ++pass) {
+      const uint32_t bucket = pass < kBuckets ? pass : uint32_t(kThin);
+      const uint32_t kernel =
+          pass < kBuckets ? pass : pass == kBuckets ? uint32_t(kThinGroup) : kThinGroupNarrow;
+      const uint8_t want_whole = pass < kBuckets ? 0 : pass == kBuckets ? 1 : 2;
+      std::vector<const Final*> list;
+      list.reserve(fin.size());
+      for (size_t q = 0; q < fin.size(); ++q)
+        if (fin[q].bucket == bucket && (bucket != kThin || whole[q] == want_whole))
+          list.push_back(&fin[q]);
+      size_t i = 0;
       while (i < list.size()) {
-        const Final* f = list[i];
-        uint32_t need[2 + 2 * kMaxFan];
-        int nneed = 0;
-        need[nneed++] = f->rp->src_index;
-        if (f->rp->mx && f->rp->split < f->rp->inner) need[nneed++] = f->rp->src2_index;
-        for (uint32_t j = 0; j < f->rp->n_dst; ++j) {
-          need[nneed++] = f->rp->dst_index[j] | kDstBit;
-          if (f->rp->mx) need[nneed++] = f->rp->sc_index[j] | kDstBit;
-        }
-        size_t add = 0;
-        for (int q = 0; q < nneed; ++q) {
-          const uint32_t k = need[q];
-          const int32_t at = (k & kDstBit) ? pool_dst[k & ~kDstBit] : pool_src[k];
-          if (at < 0) {
-            bool dup = false;
-            for (int q2 = 0; q2 < q; ++q2) dup |= need[q2] == k;
-            add += dup ? 0 : 1;
+        // Greedy group: regions in order while their pointers fit the pool.
+        std::vector<uint32_t> members;    // pool slot -> caller pointer index (| kDstBit)
+        std::vector<const Final*> batch;
+        if (!table) members.reserve(kPool);
+        batch.reserve(list.size() - i);
+        uint64_t units = 0;
+        while (i < list.size()) {
+          const Final* f = list[i];
+          if (table) {
+            if (!batch.empty() && units + f->units > kMaxUnitsPerLaunch) break;
+            batch.push_back(f);
+            units += f->units;
+            ++i;
+            continue;
           }
-        }
-        if (!batch.empty() && (members.size() + add > size_t(kPool) ||
-                             units + f->units > kMaxUnitsPerLaunch))
-          break;
-        for (int q = 0; q < nneed; ++q) {
-          const uint32_t k = need[q];
-          int32_t& at = (k & kDstBit) ? pool_dst[k & ~kDstBit] : pool_src[k];
-          if (at < 0) {
-            at = int32_t(members.size());
-            members.push_back(k);
+          uint32_t need[2 + 2 * kMaxFan];
+          int nneed = 0;
+          need[nneed++] = f->rp->src_index;
+          if (f->rp->mx && f->rp->split < f->rp->inner) need[nneed++] = f->rp->src2_index;
+          for (uint32_t j = 0; j < f->rp->n_dst; ++j) {
+            need[nneed++] = f->rp->dst_index[j] | kDstBit;
+            if (f->rp->mx) need[nneed++] = f->rp->sc_index[j] | kDstBit;
           }
+          size_t add = 0;
+          for (int q = 0; q < nneed; ++q) {
+            const uint32_t k = need[q];
+            const int32_t at = (k & kDstBit) ? pool_dst[k & ~kDstBit] : pool_src[k];
+            if (at < 0) {
+              bool dup = false;
+              for (int q2 = 0; q2 < q; ++q2) dup |= need[q2] == k;
+              add += dup ? 0 : 1;
+            }
+          }
+          if (!batch.empty() && (members.size() + add > size_t(kPool) ||
+                               units + f->units > kMaxUnitsPerLaunch)) {
+            pool_cut |= members.size() + add > size_t(kPool);
+            break;
+          }
+          for (int q = 0; q < nneed; ++q) {
+            const uint32_t k = need[q];
+            int32_t& at = (k & kDstBit) ? pool_dst[k & ~kDstBit] : pool_src[k];
+            if (at < 0) {
+              at = int32_t(members.size());
+              members.push_back(k);
+            }
+          }
+          batch.push_back(f);
+          units += f->units;
+          ++i;
         }
-        batch.push_back(f);
-        units += f->units;
-        ++i;
-      }
-      auto pool = [&](uint32_t k) -> uint16_t {
-        return uint16_t((k & kDstBit) ? pool_dst[k & ~kDstBit] : pool_src[k]);
-      };
-      Launch L;
-      L.bucket = kernel;
-      L.n_regions = uint32_t(batch.size());
-      L.pool = members;
-      align_up(out.image, 256);
-      L.regions_off = out.image.size();
-      const size_t rsz = bucket == kMx ? sizeof(MxRegion) : sizeof(CopyRegion);
-      out.image.resize(out.image.size() + rsz * batch.size(), 0);
-      uint32_t ub = 0;
-      std::vector<uint32_t> unit_region;
-      unit_region.reserve(2 + (units >> kChunkShift));
-      // Thin sibling groups: consecutive thin regions that read the same
-      // source rows (same source buffer, outer dims and row count, column
-      // offsets within one source row) take their units interleaved in the
-      // kernel, so the workgroups reading the same rows run together and
-      // share the fetched lines.  Flags bits 16-23 hold the group size,
-      // bits 24-31 the member index.
-      std::vector<uint32_t> sib(batch.size(), 0);
-      std::vector<uint32_t> units_k(batch.size()), rpu_k(batch.size());
-      for (size_t k = 0; k < batch.size(); ++k) {
-        units_k[k] = batch[k]->units;
-        rpu_k[k] = batch[k]->rows_per_unit;
-      }
-      if (bucket == kThin) {
-        // Sibling groups of this launch: consecutive members of one group
-        // (a group cut by the pointer pool continues in the next launch as
-        // a group of its own).  Flags bits 16-23 hold the group size, bits
-        // 24-31 the member index.
-        size_t k = 0;
-        while (k < batch.size()) {
-          const uint32_t gid = group_of[size_t(batch[k] - fin.data())];
-          size_t e = k + 1;
-          while (gid && e < batch.size() && group_of[size_t(batch[e] - fin.data())] == gid) ++e;
-          if (e - k >= 2) {
-            for (size_t q = k; q < e; ++q) sib[q] = (uint32_t(e - k) << 16) | (uint32_t(q - k) << 24);
-            if (kernel == kThinGroup || kernel == kThinGroupNarrow) {
-              // The group's units belong to its first member: each unit
-              // moves rows_per_unit rows of every member.
-              uint64_t lo = ~uint64_t(0), hi = 0;
-              for (size_t q = k; q < e; ++q) {
-                lo = std::min(lo, batch[q]->rp->src_off);
-                hi = std::max(hi, batch[q]->rp->src_off + batch[q]->rp->inner);
+        auto pool = [&](uint32_t k) -> uint16_t {
+          if (table) return uint16_t((k & kDstBit) ? n_src_ptrs + (k & ~kDstBit) : k);
+          return uint16_t((k & kDstBit) ? pool_dst[k & ~kDstBit] : pool_src[k]);
+        };
+        Launch L;
+        L.bucket = kernel;
+        L.n_regions = uint32_t(batch.size());
+        L.pool = members;
+        L.table = table;
+        align_up(image, 256);
+        L.regions_off = image.size();
+        const size_t rsz = bucket == kMx ? sizeof(MxRegion) : sizeof(CopyRegion);
+        image.resize(image.size() + rsz * batch.size(), 0);
+        uint32_t ub = 0;
+        std::vector<uint32_t> unit_region;
+        unit_region.reserve(2 + (units >> kChunkShift));
+        // Thin sibling groups: consecutive thin regions that read the same
+        // source rows (same source buffer, outer dims and row count, column
+        // offsets within one source row) take their units interleaved in the
+        // kernel, so the workgroups reading the same rows run together and
+        // share the fetched lines.  Flags bits 16-23 hold the group size,
+        // bits 24-31 the member index.
+        std::vector<uint32_t> sib(batch.size(), 0);
+        std::vector<uint32_t> units_k(batch.size()), rpu_k(batch.size());
+        for (size_t k = 0; k < batch.size(); ++k) {
+          units_k[k] = batch[k]->units;
+          rpu_k[k] = batch[k]->rows_per_unit;
+        }
+        if (bucket == kThin) {
+          // Sibling groups of this launch: consecutive members of one group
+          // (a group cut by the pointer pool continues in the next launch as
+          // a group of its own).  Flags bits 16-23 hold the group size, bits
+          // 24-31 the member index.
+          size_t k = 0;
+          while (k < batch.size()) {
+            const uint32_t gid = group_of[size_t(batch[k] - fin.data())];
+            size_t e = k + 1;
+            while (gid && e < batch.size() && group_of[size_t(batch[e] - fin.data())] == gid) ++e;
+            if (e - k >= 2) {
+              for (size_t q = k; q < e; ++q) sib[q] = (uint32_t(e - k) << 16) | (uint32_t(q - k) << 24);
+              if (kernel == kThinGroup || kernel == kThinGroupNarrow) {
+                // The group's units belong to its first member: each unit
+                // moves rows_per_unit rows of every member.
+                uint64_t lo = ~uint64_t(0), hi = 0;
+                for (size_t q = k; q < e; ++q) {
+                  lo = std::min(lo, batch[q]->rp->src_off);
+                  hi = std::max(hi, batch[q]->rp->src_off + batch[q]->rp->inner);
+                }
+                const uint64_t rows = batch[k]->rows;
+                // Whole 128-byte slot groups per unit where that keeps most of
+                // the tile: a contiguous, aligned block then goes straight into
+                // LDS (and can be swizzled) whatever the span.
+                uint64_t rpu = std::max<uint64_t>(1, kGroupTile / (hi - lo));
+                const uint64_t m = 128 / std::gcd<uint64_t>(hi - lo, 128);
+                if (rpu >= 2 * m) rpu -= rpu % m;
+                rpu = std::min<uint64_t>(rpu, rows);
+                for (size_t q = k; q < e; ++q) {
+                  sib[q] |= kFlagGroupLoad;
+                  rpu_k[q] = uint32_t(rpu);
+                  units_k[q] = q == k ? uint32_t((rows + rpu - 1) / rpu) : 0;
+                }
               }
-              const uint64_t rows = batch[k]->rows;
-              // Whole 128-byte slot groups per unit where that keeps most of
-              // the tile: a contiguous, aligned block then goes straight into
-              // LDS (and can be swizzled) whatever the span.
-              uint64_t rpu = std::max<uint64_t>(1, kGroupTile / (hi - lo));
-              const uint64_t m = 128 / std::gcd<uint64_t>(hi - lo, 128);
+            } else if (kernel == kThinGroup || kernel == kThinGroupNarrow) {
+              // A lone member left by a pool cut: a group of one.
+              sib[k] = kFlagGroupLoad | (1u << 16);
+              const uint64_t rows = batch[k]->rows, w = batch[k]->rp->inner;
+              uint64_t rpu = std::max<uint64_t>(1, kGroupTile / w);
+              const uint64_t m = 128 / std::gcd<uint64_t>(w, 128);
               if (rpu >= 2 * m) rpu -= rpu % m;
               rpu = std::min<uint64_t>(rpu, rows);
-              for (size_t q = k; q < e; ++q) {
-                sib[q] |= kFlagGroupLoad;
-                rpu_k[q] = uint32_t(rpu);
-                units_k[q] = q == k ? uint32_t((rows + rpu - 1) / rpu) : 0;
-              }
+              rpu_k[k] = uint32_t(rpu);
+              units_k[k] = uint32_t((rows + rpu - 1) / rpu);
             }
-          } else if (kernel == kThinGroup || kernel == kThinGroupNarrow) {
-            // A lone member left by a pool cut: a group of one.
-            sib[k] = kFlagGroupLoad | (1u << 16);
-            const uint64_t rows = batch[k]->rows, w = batch[k]->rp->inner;
-            uint64_t rpu = std::max<uint64_t>(1, kGroupTile / w);
-            const uint64_t m = 128 / std::gcd<uint64_t>(w, 128);
-            if (rpu >= 2 * m) rpu -= rpu % m;
-            rpu = std::min<uint64_t>(rpu, rows);
-            rpu_k[k] = uint32_t(rpu);
-            units_k[k] = uint32_t((rows + rpu - 1) / rpu);
+            k = e;
           }
-          k = e;
         }
-      }
-      for (size_t k = 0; k < batch.size(); ++k) {
-        const Final& f = *batch[k];
-        const Raw& r = *f.rp;
-        uint64_t ext[3], ss[3], ds[3], sc[3], ss2[3];
-        outer_fields(r.outer, ext, ss, ds, sc, ss2);
-        uint8_t* dstp = out.image.data() + L.regions_off + rsz * k;
-        if (bucket == kMx) {
-          MxRegion m;
-          std::memset(&m, 0, sizeof(m));
-          m.src_off = r.src_off;
-          m.dst_off = r.dst_off;
-          m.sc_off = r.sc_off;
-          for (int q = 0; q < 3; ++q) {
-            m.sstr[q] = ss[q];
-            m.dstr[q] = ds[q];
-            m.scstr[q] = sc[q];
+        for (size_t k = 0; k < batch.size(); ++k) {
+          const Final& f = *batch[k];
+          const Raw& r = *f.rp;
+          uint64_t ext[3], ss[3], ds[3], sc[3], ss2[3];
+          outer_fields(r.outer, ext, ss, ds, sc, ss2);
+          uint8_t* dstp = image.data() + L.regions_off + rsz * k;
+          if (bucket == kMx) {
+            MxRegion m;
+            std::memset(&m, 0, sizeof(m));
+            m.src_off = r.src_off;
+            m.dst_off = r.dst_off;
+            m.sc_off = r.sc_off;
+            for (int q = 0; q < 3; ++q) {
+              m.sstr[q] = ss[q];
+              m.dstr[q] = ds[q];
+              m.scstr[q] = sc[q];
+            }
+            m.split = uint32_t(r.split);
+            if (r.split < r.inner) {
+              m.src2_ptr = pool(r.src2_index);
+              m.src2_off = r.src2_off;
+              for (int q = 0; q < 3; ++q) m.sstr2[q] = ss2[q];
+            }
+            m.e0 = uint32_t(ext[0]);
+            m.e1 = uint32_t(ext[1]);
+            m.rows = uint32_t(f.rows);
+            m.inner = uint32_t(r.inner);
+            m.rows_per_unit = f.rows_per_unit;
+            m.unit_begin = ub;
+            m.flags = f.flags;
+            m.sc_inner = uint32_t(r.sc_inner);
+            m.src_ptr = pool(r.src_index);
+            m.n_dst = uint16_t(r.n_dst);
+            for (uint32_t j = 0; j < r.n_dst; ++j) {
+              m.dst_ptr[j] = pool(r.dst_index[j] | kDstBit);
+              m.sc_ptr[j] = pool(r.sc_index[j] | kDstBit);
+            }
+            std::memcpy(dstp, &m, sizeof(m));
+          } else {
+            CopyRegion c;
+            std::memset(&c, 0, sizeof(c));
+            c.src_off = r.src_off;
+            c.dst_off = r.dst_off;
+            uint64_t al = r.src_off | r.dst_off | r.inner;
+            for (int q = 0; q < 3; ++q) {
+              c.sstr[q] = ss[q];
+              c.dstr[q] = ds[q];
+              if (ext[q] > 1) al |= ss[q] | ds[q];
+            }
+            c.e0 = uint32_t(ext[0]);
+            c.e1 = uint32_t(ext[1]);
+            c.rows = uint32_t(f.rows);
+            c.inner = uint32_t(r.inner);
+            c.rows_per_unit = rpu_k[k];
+            c.unit_begin = ub;
+            c.flags = f.flags | (uint32_t(al & 15) << 8) | sib[k];
+            c.src_ptr = pool(r.src_index);
+            c.n_dst = uint16_t(r.n_dst);
+            for (uint32_t j = 0; j < r.n_dst; ++j) c.dst_ptr[j] = pool(r.dst_index[j] | kDstBit);
+            std::memcpy(dstp, &c, sizeof(c));
           }
-          m.split = uint32_t(r.split);
-          if (r.split < r.inner) {
-            m.src2_ptr = pool(r.src2_index);
-            m.src2_off = r.src2_off;
-            for (int q = 0; q < 3; ++q) m.sstr2[q] = ss2[q];
+          if (bucket != kTiny) {
+            // Chunk table: the region of every (1 << kChunkShift)-th unit.
+            const uint64_t first = (uint64_t(ub) + (1u << kChunkShift) - 1) >> kChunkShift;
+            for (uint64_t c = first; (c << kChunkShift) < uint64_t(ub) + units_k[k]; ++c)
+              unit_region.push_back(uint32_t(k));
           }
-          m.e0 = uint32_t(ext[0]);
-          m.e1 = uint32_t(ext[1]);
-          m.rows = uint32_t(f.rows);
-          m.inner = uint32_t(r.inner);
-          m.rows_per_unit = f.rows_per_unit;
-          m.unit_begin = ub;
-          m.flags = f.flags;
-          m.sc_inner = uint32_t(r.sc_inner);
-          m.src_ptr = pool(r.src_index);
-          m.n_dst = uint16_t(r.n_dst);
-          for (uint32_t j = 0; j < r.n_dst; ++j) {
-            m.dst_ptr[j] = pool(r.dst_index[j] | kDstBit);
-            m.sc_ptr[j] = pool(r.sc_index[j] | kDstBit);
-          }
-          std::memcpy(dstp, &m, sizeof(m));
-        } else {
-          CopyRegion c;
-          std::memset(&c, 0, sizeof(c));
-          c.src_off = r.src_off;
-          c.dst_off = r.dst_off;
-          uint64_t al = r.src_off | r.dst_off | r.inner;
-          for (int q = 0; q < 3; ++q) {
-            c.sstr[q] = ss[q];
-            c.dstr[q] = ds[q];
-            if (ext[q] > 1) al |= ss[q] | ds[q];
-          }
-          c.e0 = uint32_t(ext[0]);
-          c.e1 = uint32_t(ext[1]);
-          c.rows = uint32_t(f.rows);
-          c.inner = uint32_t(r.inner);
-          c.rows_per_unit = rpu_k[k];
-          c.unit_begin = ub;
-          c.flags = f.flags | (uint32_t(al & 15) << 8) | sib[k];
-          c.src_ptr = pool(r.src_index);
-          c.n_dst = uint16_t(r.n_dst);
-          for (uint32_t j = 0; j < r.n_dst; ++j) c.dst_ptr[j] = pool(r.dst_index[j] | kDstBit);
-          std::memcpy(dstp, &c, sizeof(c));
-        }
-        if (bucket != kTiny) {
-          // Chunk table: the region of every (1 << kChunkShift)-th unit.
-          const uint64_t first = (uint64_t(ub) + (1u << kChunkShift) - 1) >> kChunkShift;
-          for (uint64_t c = first; (c << kChunkShift) < uint64_t(ub) + units_k[k]; ++c)
-            unit_region.push_back(uint32_t(k));
-        }
-        ub += units_k[k];
+          ub += units_k[k];
 
-        out.region_tensor.push_back(r.tensor);
+          if (record) out.region_tensor.push_back(r.tensor);
+        }
+        if (bucket == kTiny) {
+          L.n_units = uint32_t((batch.size() + kThreads - 1) / kThreads);
+          L.units_off = 0;
+        } else {
+          L.n_units = ub;
+          unit_region.push_back(uint32_t(batch.size() - 1));  // entry for unit n_units - 1
+          align_up(image, 256);
+          L.units_off = image.size();
+          image.resize(image.size() + 4 * unit_region.size());
+          std::memcpy(image.data() + L.units_off, unit_region.data(), 4 * unit_region.size());
+        }
+        for (uint32_t k : members) ((k & kDstBit) ? pool_dst[k & ~kDstBit] : pool_src[k]) = -1;
+        if (record) {
+          nreg_bucket[bucket] += batch.size();
+          nunit_bucket[bucket] += L.n_units;
+        }
+        launches.push_back(std::move(L));
       }
-      if (bucket == kTiny) {
-        L.n_units = uint32_t((batch.size() + kThreads - 1) / kThreads);
-        L.units_off = 0;
-      } else {
-        L.n_units = ub;
-        unit_region.push_back(uint32_t(batch.size() - 1));  // entry for unit n_units - 1
-        align_up(out.image, 256);
-        L.units_off = out.image.size();
-        out.image.resize(out.image.size() + 4 * unit_region.size());
-        std::memcpy(out.image.data() + L.units_off, unit_region.data(), 4 * unit_region.size());
-      }
-      for (uint32_t k : members) ((k & kDstBit) ? pool_dst[k & ~kDstBit] : pool_src[k]) = -1;
-      nreg_bucket[bucket] += batch.size();
-      nunit_bucket[bucket] += L.n_units;
-      out.launches.push_back(std::move(L));
     }
+    align_up(image, 256);
+  };
+  emit(false, out.image, out.launches, true);
+  // A plan whose pointers the pool cut into more launches also gets the
+  // table form (one launch per pass), which reshard_execute runs once the
+  // plan holds a device table of the call's pointers.  Pool indices are 16
+  // bits wide, so the caller's pointers must number at most 65,536.
+  out.table_image.clear();
+  out.table_launches.clear();
+  if (pool_cut && n_src_ptrs + n_dst_ptrs <= 65536) {
+    out.table_image.reserve(out.image.size());
+    emit(true, out.table_image, out.table_launches, false);
   }
-  align_up(out.image, 256);
 
   rs_plan_info& I = out.info;
   std::memset(&I, 0, sizeof(I));
@@ -1511,7 +1545,8 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
     I.n_regions_bucket[b] = nreg_bucket[b];
     I.n_units_bucket[b] = nunit_bucket[b];
   }
-  I.n_launches = out.launches.size();
+  I.n_launches = out.table_launches.empty() ? out.launches.size() : out.table_launches.size();
+  I.n_launches_pooled = out.launches.size();
   I.bytes_read = bytes_read;
   I.bytes_written = bytes_written;
   I.bytes_read_no_fanout = bytes_nofan;

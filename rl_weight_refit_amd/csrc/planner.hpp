@@ -20,12 +20,19 @@ struct Launch {
   uint64_t regions_off = 0;    // byte offset of the region array in the image
   uint64_t units_off = 0;      // byte offset of the unit -> region table (0 if none)
   std::vector<uint32_t> pool;  // pool slot -> caller pointer index (| kDstBit for dst_ptrs)
+  bool table = false;          // table form: pool index = caller pointer index, sources
+                               // first (the pointers come from a device table)
 };
 
 struct PlanData {
   std::vector<uint32_t> region_tensor;  // tensor of each region, in image order
   std::vector<uint8_t> image;      // device tables, uploaded once per device
   std::vector<Launch> launches;
+  // Table form of the launches (empty unless the pointer pool cut a pass of
+  // the pooled form into several launches): regions in the same order, in
+  // an image of their own, uploaded after `image`.
+  std::vector<uint8_t> table_image;
+  std::vector<Launch> table_launches;
   std::vector<uint8_t> src_used;   // pointer index -> referenced by some region
   std::vector<uint8_t> dst_used;
   std::vector<uint8_t> src_align;  // required pointer alignment (bytes)

@@ -159,8 +159,20 @@ struct LaunchArgs {
   const uint32_t* unit_region;
   uint32_t n_regions;
   uint32_t n_units;
-  void* ptr[kPool];
+  void* ptr[kPool];             // the launch's pointer pool
 };
 static_assert(sizeof(LaunchArgs) <= 4096, "kernel arguments must fit in 4 KiB");
+static_assert(kPool >= 2 + 2 * kMaxFan, "the pool holds every pointer of one region");
+
+// Kernel arguments of a launch whose pointers come from a device table of the
+// plan (its regions' pool indices index that table): the same fields, the
+// pool replaced by the table's address.
+struct TableArgs {
+  const void* regions;
+  const uint32_t* unit_region;
+  uint32_t n_regions;
+  uint32_t n_units;
+  void* const* ptab;
+};
 
 }  // namespace rs

@@ -31,6 +31,7 @@ uint64_t g_valid_rejected = 0;       // uncorrupted cases the planner declined (
 uint64_t g_sibling_groups = 0;       // thin sibling groups checked
 uint64_t g_two_piece = 0;            // MXFP8 regions with two source pieces replayed
 uint64_t g_group_loads = 0;          // thin sibling groups loaded whole
+uint64_t g_table_forms = 0;          // plans with a table form (pointers from a device table) checked
 
 struct Rng {
   uint64_t s;
@@ -310,9 +311,10 @@ bool run_case(Rng& g, uint64_t c, bool corrupt) {
   // each of its regions' units exactly once.  Thin sibling groups (flags
   // bits 16-31) must be consecutive regions with equal unit counts, which
   // the thin kernel relies on when it takes their units member-fastest.
-  for (const rs::Launch& L : P.launches) {
+  auto walk_units = [&](const std::vector<rs::Launch>& launches, const std::vector<uint8_t>& image) {
+  for (const rs::Launch& L : launches) {
     if (L.bucket == rs::kTiny || L.bucket == rs::kMx) continue;
-    const rs::CopyRegion* regs = reinterpret_cast<const rs::CopyRegion*>(P.image.data() + L.regions_off);
+    const rs::CopyRegion* regs = reinterpret_cast<const rs::CopyRegion*>(image.data() + L.regions_off);
     std::vector<std::vector<uint8_t>> seen(L.n_regions);
     for (uint32_t k = 0; k < L.n_regions; ++k) {
       const uint32_t nu = (regs[k].rows + regs[k].rows_per_unit - 1) / regs[k].rows_per_unit;
@@ -366,6 +368,73 @@ bool run_case(Rng& g, uint64_t c, bool corrupt) {
     for (const auto& v : seen)
       for (uint8_t x : v)
         if (x != 1) die("a work unit is not taken", c);
+  }
+  };
+  walk_units(P.launches, P.image);
+  // Table form (a plan whose pointers the kernel-argument pool cut into
+  // several launches of one kind): the same regions in the same order, one
+  // launch per kind, every pool index the caller's pointer index (sources
+  // first) that the pooled form's pool slot names.  Sibling-group fields and
+  // units may differ where the pool cut a group.
+  if (!P.table_launches.empty()) {
+    ++g_table_forms;
+    if (P.info.n_launches != P.table_launches.size() || P.info.n_launches_pooled != P.launches.size() ||
+        P.table_launches.size() >= P.launches.size())
+      die("table form launch counts", c);
+    walk_units(P.table_launches, P.table_image);
+    const uint64_t ns = P.info.n_src_ptrs;
+    auto caller = [&](const rs::Launch& L, uint16_t slot) -> uint64_t {
+      if (slot >= L.pool.size()) die("pool slot out of range", c);
+      const uint32_t e = L.pool[slot];
+      return (e & rs::kDstBit) ? ns + (e & ~rs::kDstBit) : e;
+    };
+    size_t ti = 0, tk = 0;
+    for (const rs::Launch& L : P.launches) {
+      if (L.table) die("pooled launch marked as table form", c);
+      for (uint32_t k = 0; k < L.n_regions; ++k, ++tk) {
+        while (ti < P.table_launches.size() && tk >= P.table_launches[ti].n_regions) {
+          tk = 0;
+          ++ti;
+        }
+        if (ti >= P.table_launches.size()) die("table form has fewer regions", c);
+        const rs::Launch& T = P.table_launches[ti];
+        if (!T.table || !T.pool.empty() || T.bucket != L.bucket) die("table launch fields", c);
+        if (L.bucket == rs::kMx) {
+          rs::MxRegion a, b;
+          std::memcpy(&a, P.image.data() + L.regions_off + k * sizeof(a), sizeof(a));
+          std::memcpy(&b, P.table_image.data() + T.regions_off + tk * sizeof(b), sizeof(b));
+          bool same = a.src_off == b.src_off && a.dst_off == b.dst_off && a.sc_off == b.sc_off &&
+                      a.e0 == b.e0 && a.e1 == b.e1 && a.rows == b.rows && a.inner == b.inner &&
+                      a.rows_per_unit == b.rows_per_unit && a.flags == b.flags && a.sc_inner == b.sc_inner &&
+                      a.n_dst == b.n_dst && a.split == b.split && caller(L, a.src_ptr) == b.src_ptr;
+          for (int q = 0; q < 3; ++q)
+            same &= a.sstr[q] == b.sstr[q] && a.dstr[q] == b.dstr[q] && a.scstr[q] == b.scstr[q];
+          for (uint32_t j = 0; j < a.n_dst; ++j)
+            same &= caller(L, a.dst_ptr[j]) == b.dst_ptr[j] && caller(L, a.sc_ptr[j]) == b.sc_ptr[j];
+          if (a.split < a.inner) {
+            same &= caller(L, a.src2_ptr) == b.src2_ptr && a.src2_off == b.src2_off;
+            for (int q = 0; q < 3; ++q) same &= a.sstr2[q] == b.sstr2[q];
+          }
+          if (!same) die("table form MXFP8 region differs", c);
+        } else {
+          rs::CopyRegion a, b;
+          std::memcpy(&a, P.image.data() + L.regions_off + k * sizeof(a), sizeof(a));
+          std::memcpy(&b, P.table_image.data() + T.regions_off + tk * sizeof(b), sizeof(b));
+          bool same = a.src_off == b.src_off && a.dst_off == b.dst_off && a.e0 == b.e0 && a.e1 == b.e1 &&
+                      a.rows == b.rows && a.inner == b.inner && (a.flags & 0xFFFu) == (b.flags & 0xFFFu) &&
+                      a.n_dst == b.n_dst && caller(L, a.src_ptr) == b.src_ptr;
+          if (L.bucket != rs::kThin && L.bucket != rs::kThinGroup && L.bucket != rs::kThinGroupNarrow)
+            same &= a.rows_per_unit == b.rows_per_unit && a.flags == b.flags;
+          for (int q = 0; q < 3; ++q) same &= a.sstr[q] == b.sstr[q] && a.dstr[q] == b.dstr[q];
+          for (uint32_t j = 0; j < a.n_dst; ++j) same &= caller(L, a.dst_ptr[j]) == b.dst_ptr[j];
+          if (!same) die("table form region differs", c);
+        }
+      }
+    }
+    if (ti + 1 != P.table_launches.size() || tk != P.table_launches.back().n_regions)
+      die("table form has more regions", c);
+  } else if (P.info.n_launches != P.launches.size() || P.info.n_launches_pooled != P.launches.size()) {
+    die("launch counts", c);
   }
 
   // Replay every region.
@@ -484,8 +553,10 @@ int main(int argc, char** argv) {
   std::printf("cases %" PRIu64 ": planned and replayed %" PRIu64 ", rejected %" PRIu64
               " (%" PRIu64 " of them uncorrupted, unsupported), corrupted but accepted %" PRIu64
               "; regions replayed: bulk %" PRIu64 ", thin %" PRIu64 ", tiny %" PRIu64 ", mxfp8 %" PRIu64
-              "; thin sibling groups %" PRIu64 " (loaded whole %" PRIu64 "); two-piece MXFP8 regions %" PRIu64 "\n",
+              "; thin sibling groups %" PRIu64 " (loaded whole %" PRIu64 "); two-piece MXFP8 regions %" PRIu64
+              "; table forms %" PRIu64 "\n",
               cases, planned, rejected, g_valid_rejected, corrupt_ok, g_bucket_regions[0],
-              g_bucket_regions[1], g_bucket_regions[2], g_bucket_regions[3], g_sibling_groups, g_group_loads, g_two_piece);
+              g_bucket_regions[1], g_bucket_regions[2], g_bucket_regions[3], g_sibling_groups, g_group_loads, g_two_piece,
+              g_table_forms);
   return 0;
 }

@@ -1,8 +1,10 @@
 """GPU execution contract: plans on non-default streams, one plan executed
 concurrently on several streams (and from several host threads) into
-separate destinations, two plans at once, and an execute captured into a
-HIP graph and replayed.  Every result is compared byte for byte with the
-CPU oracle, poison and guard bytes included.
+separate destinations, two plans at once, an execute captured into a HIP
+graph and replayed, and a plan with more pointers than one launch's
+arguments hold (its device pointer tables, and the pooled launches it falls
+back to).  Every result is compared byte for byte with the CPU oracle,
+poison and guard bytes included.
 """
 
 import threading
@@ -33,6 +35,10 @@ WORKLOADS = {
     "moe_small_mxfp8": lambda: synth.moe_experts(16, 512, 192, 8, 4, 4, seed=9, quant="mxfp8"),
     "uneven_7": lambda: synth.uneven_case(7),
     "dense_ffn_fanout": lambda: synth.dense_ffn(hidden=256, inter=1000, src_tp=4, dst_tp=2, dst_dp=2),
+    # 61 layers of small tensors unpacked from one buffer into 4 TP slots
+    # each: 1,465 pointers, more than one launch's kernel arguments hold.
+    "misc_unpack_many_ptrs": lambda: synth.reverse(synth.misc_pack(hidden=256, q_rank=64, kv_rank=32,
+                                                                   experts=8)),
 }
 
 
@@ -53,7 +59,7 @@ def test_non_default_stream(name):
     gh.check_device(wl["name"], flat)
 
 
-@pytest.mark.parametrize("name", ["moe_small", "moe_small_mxfp8", "uneven_7"])
+@pytest.mark.parametrize("name", ["moe_small", "moe_small_mxfp8", "uneven_7", "misc_unpack_many_ptrs"])
 def test_one_plan_on_several_streams(name):
     """The same plan, four streams, four destination sets, no synchronisation
     between the executes."""
@@ -105,7 +111,8 @@ def test_two_plans_at_once():
     gh.check_device(wb["name"], fb)
 
 
-@pytest.mark.parametrize("name", ["worked_8x8_tiny", "moe_small_mxfp8", "uneven_7", "dense_ffn_fanout"])
+@pytest.mark.parametrize("name", ["worked_8x8_tiny", "moe_small_mxfp8", "uneven_7", "dense_ffn_fanout",
+                                  "misc_unpack_many_ptrs"])
 def test_graph_capture_and_replay(name):
     """After its first execute (which uploads the tables) a plan only enqueues
     kernels, so it can be captured into a HIP graph.  Each replay follows an
@@ -159,3 +166,48 @@ def test_debug_checks_reject_a_short_allocation(monkeypatch):
     finally:
         torch.cuda.synchronize()
         hip.hipFree(short)
+
+
+def test_pointer_tables_and_pooled_fallback():
+    """A plan with more pointers than one launch's arguments hold runs in one
+    launch per kernel from a device table of the call's pointers, one table
+    per pointer set, up to 8 sets per device; a ninth and tenth set run the
+    pooled launches.  Each set, executed twice (the second time from its
+    table), and the sets run after the limit all match the oracle."""
+    wl, plan, bufs = _setup("misc_unpack_many_ptrs", copies=10)
+    info = plan.info()
+    assert info["n_src_ptrs"] + info["n_dst_ptrs"] > 500
+    assert info["n_launches"] < info["n_launches_pooled"], info
+    s = torch.cuda.Stream()
+    for rep in range(2):
+        for src_dev, sp, dp, flat in bufs:
+            if rep:
+                for d in {id(d): d for _, d in flat}.values():
+                    d.body().fill_(d.poison)
+                torch.cuda.synchronize()
+            binding.reshard_execute(plan, sp, dp, s.cuda_stream)
+            s.synchronize()
+            gh.check_device(wl["name"], flat)
+
+
+def test_graph_capture_of_a_new_pointer_set():
+    """After a first execute (which uploads the plan's tables), an execute
+    captured with pointers the plan has not seen (no pointer table may be
+    made while capturing) records the pooled launches; replays rewrite the
+    destinations exactly."""
+    wl, plan, [(_, sp0, dp0, flat0), (_, sp, dp, flat)] = _setup("misc_unpack_many_ptrs", copies=2)
+    s = torch.cuda.Stream()
+    binding.reshard_execute(plan, sp0, dp0, s.cuda_stream)
+    s.synchronize()
+    gh.check_device(wl["name"], flat0)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        binding.reshard_execute(plan, sp, dp, torch.cuda.current_stream().cuda_stream)
+    dsts = {id(d): d for _, d in flat}.values()
+    for rep in range(3):
+        for d in dsts:
+            d.body().fill_(d.poison)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        gh.check_device(wl["name"], flat)
