@@ -1315,10 +1315,12 @@ __device__ __forceinline__ MxCodes mx_encode(u32x4 xa, u32x4 xb) {
   return c;
 }
 
-// One work unit of the MXFP8 kernel: nr rows (nr <= kMxSlots >> lg) of inner
-// elements, staged in LDS with row i at slot i << lg (one 16-byte slot per
-// 8-element group).  kOneRow: the unit is a single row, whose addresses are
-// uniform across the workgroup.
+// One work unit of the MXFP8 kernel: nr rows (nr <= kMxSlots / P) of inner
+// elements, staged in LDS with row i at slot i * P (one 16-byte slot per
+// 8-element group), P = mx_row_pitch(inner).  kOneRow: the unit is a single
+// row, whose addresses are uniform across the workgroup.  kPitch: P is not a
+// power of two, so slot s belongs to row s / P (a multiply by a reciprocal
+// that is exact for every slot index) instead of s >> log2(P).
 // The fields of an MXFP8 region a work unit needs, read from the table once
 // at kernel entry, before any branch or store: a table read after a store is
 // a vector load (the compiler cannot rule out that the store changed the
@@ -1364,6 +1366,25 @@ __device__ __forceinline__ MxFields mx_fields(const Args& a, const MxRegion* R) 
   return f;
 }
 
+// Eight bf16 elements as a 16-byte group: the first n of v, the rest zero.
+__device__ __forceinline__ u32x4 pack8(const uint16_t* v, uint32_t n) {
+  uint32_t w[4];
+#pragma unroll
+  for (uint32_t i = 0; i < 4; ++i)
+    w[i] = (2 * i < n ? uint32_t(v[2 * i]) : 0u) | (2 * i + 1 < n ? uint32_t(v[2 * i + 1]) << 16 : 0u);
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// The n (1..8) elements at q as a zero-filled group.  Every load reads one
+// of the n (element min(i, n - 1)), so all eight are issued before the first
+// wait instead of one after another.
+__device__ __forceinline__ u32x4 gather8(const uint16_t* q, uint32_t n) {
+  uint16_t v[8];
+#pragma unroll
+  for (uint32_t i = 0; i < 8; ++i) v[i] = q[min(i, n - 1u)];
+  return pack8(v, n);
+}
+
 // The first n (clamped to 0..8) of the eight bf16 elements of x, the rest zero.
 __device__ __forceinline__ u32x4 keep_elems(u32x4 x, int n) {
   auto keep = [&](uint32_t w, int i) -> uint32_t {   // dword i holds elements 2i, 2i + 1
@@ -1372,7 +1393,7 @@ __device__ __forceinline__ u32x4 keep_elems(u32x4 x, int n) {
   return u32x4{keep(x.x, 0), keep(x.y, 1), keep(x.z, 2), keep(x.w, 3)};
 }
 
-template <bool kOneRow, bool kFan1, bool kTwo = false, class Args>
+template <bool kOneRow, bool kFan1, bool kTwo = false, bool kPitch = false, class Args>
 __device__ __forceinline__ void mx_unit(const Args& a, const MxRegion* R, const MxFields& f, uint32_t r0,
                                         uint32_t nr, u32x4* stage, uint8_t* sc_stage) {
   constexpr uint32_t K = kMxSlots / kMxThreads;
@@ -1389,8 +1410,15 @@ __device__ __forceinline__ void mx_unit(const Args& a, const MxRegion* R, const 
   char* const sk = f.sk;
   const uint64_t so1 = kOneRow ? row_off(r0, e0, e1, nouter, s0, s1, s2) : 0;
   const uint64_t do1 = kOneRow ? row_off(r0, e0, e1, nouter, d0, d1, d2) : 0;
-  const uint32_t lg = mx_slot_shift(inner), Lp = 1u << lg;
+  const uint32_t lg = mx_slot_shift(inner), Lp = kPitch ? mx_row_pitch(inner) : 1u << lg;
   const uint32_t ng = (inner + 7u) >> 3;
+  // Row and slot-in-row of slot s (and of scale byte t, 4 per 4 slots):
+  // ceil(2^32 / P) times s, high word, is s / P for s < kMxSlots and
+  // P <= kMxSlots (likewise for P / 4 and t < kMxSlots / 4).
+  const uint32_t mrow = kPitch ? 0xFFFFFFFFu / Lp + 1u : 0u;
+  const uint32_t msc = kPitch ? 0xFFFFFFFFu / (Lp >> 2) + 1u : 0u;
+  auto row_of = [&](uint32_t s) -> uint32_t { return kPitch ? __umulhi(s, mrow) : s >> lg; };
+  auto col_of = [&](uint32_t s, uint32_t rl) -> uint32_t { return kPitch ? s - rl * Lp : s & (Lp - 1u); };
 
   // Phase 1: every group of the unit into its LDS slot.  Whole, 16-byte
   // aligned groups load straight into LDS; a partial or misaligned group is
@@ -1427,7 +1455,7 @@ __device__ __forceinline__ void mx_unit(const Args& a, const MxRegion* R, const 
         b1 = nb;
       }
       pn = (b1 - b0) >> 1;
-      pb = (rl << lg) * 16u + h + b0;
+      pb = (kPitch ? rl * Lp : rl << lg) * 16u + h + b0;
       const uint16_t* q = reinterpret_cast<const uint16_t*>(rs + b0);
 #pragma unroll
       for (uint32_t e = 0; e < 7; ++e) pe[e] = e < pn ? q[e] : uint16_t(0);
@@ -1435,7 +1463,7 @@ __device__ __forceinline__ void mx_unit(const Args& a, const MxRegion* R, const 
 #pragma unroll
     for (uint32_t k = 0; k < K; ++k) {
       const uint32_t s = k * kMxThreads + tid;
-      const uint32_t rl = s >> lg, j = s & (Lp - 1u);
+      const uint32_t rl = row_of(s), j = col_of(s, rl);
       if (rl < nr) {
         const char* rs = sp + (kOneRow ? so1 : row_off(r0 + rl, e0, e1, nouter, s0, s1, s2));
         const int x0 = int(16u * j) - int(reinterpret_cast<uintptr_t>(rs) & 15u);   // row byte at line j
@@ -1459,7 +1487,7 @@ __device__ __forceinline__ void mx_unit(const Args& a, const MxRegion* R, const 
       for (uint32_t kk = 0; kk < K / 2; ++kk) {
         const uint32_t k = half * (K / 2) + kk;
         const uint32_t s = k * kMxThreads + tid;
-        const uint32_t rl = s >> lg, g = s & (Lp - 1u);
+        const uint32_t rl = row_of(s), g = col_of(s, rl);
         fun[kk] = false;
         sh[kk] = 0;
         if (rl < nr && g < ng) {
@@ -1479,17 +1507,14 @@ __device__ __forceinline__ void mx_unit(const Args& a, const MxRegion* R, const 
       for (uint32_t kk = 0; kk < K / 2; ++kk) {
         const uint32_t k = half * (K / 2) + kk;
         const uint32_t s = k * kMxThreads + tid;
-        const uint32_t rl = s >> lg, g = s & (Lp - 1u);
+        const uint32_t rl = row_of(s), g = col_of(s, rl);
         if (fun[kk]) {
           stage[s] = sh[kk] ? funnel16(A[kk], B[kk], sh[kk]) : A[kk];
         } else if (rl < nr && g < ng) {
-          const uint16_t* q = reinterpret_cast<const uint16_t*>(
-              sp + (kOneRow ? so1 : row_off(r0 + rl, e0, e1, nouter, s0, s1, s2)) + uint64_t(g) * 16u);
-          const uint32_t n = min(inner - g * 8u, 8u);
-          uint32_t w[4] = {0, 0, 0, 0};
-          for (uint32_t i = 0; i < 8; ++i)
-            if (i < n) w[i >> 1] |= uint32_t(q[i]) << (16 * (i & 1));
-          stage[s] = u32x4{w[0], w[1], w[2], w[3]};
+          stage[s] = gather8(reinterpret_cast<const uint16_t*>(
+                                 sp + (kOneRow ? so1 : row_off(r0 + rl, e0, e1, nouter, s0, s1, s2)) +
+                                 uint64_t(g) * 16u),
+                             min(inner - g * 8u, 8u));
         }
       }
     }
@@ -1497,21 +1522,19 @@ __device__ __forceinline__ void mx_unit(const Args& a, const MxRegion* R, const 
 #pragma unroll
   for (uint32_t k = 0; k < K; ++k) {
     const uint32_t s = k * kMxThreads + tid;
-    const uint32_t rl = s >> lg, g = s & (Lp - 1u);
+    const uint32_t rl = row_of(s), g = col_of(s, rl);
     if (kTwo && rl < nr && g < ng) {
-      // Two pieces: each element from the piece that holds its column.
+      // Two pieces: each element from the piece that holds its column (the
+      // column clamped to the row, so all eight loads are issued at once).
       const char* p1 = sp + row_off(r0 + rl, e0, e1, nouter, s0, s1, s2);
       const char* p2 = f.sp2 + row_off(r0 + rl, e0, e1, nouter, f.t0, f.t1, f.t2);
-      uint32_t w[4] = {0, 0, 0, 0};
+      uint16_t v[8];
+#pragma unroll
       for (uint32_t i = 0; i < 8; ++i) {
-        const uint32_t c = g * 8u + i;
-        if (c < inner) {
-          const uint16_t v = c < f.split ? *reinterpret_cast<const uint16_t*>(p1 + 2u * c)
-                                         : *reinterpret_cast<const uint16_t*>(p2 + 2u * (c - f.split));
-          w[i >> 1] |= uint32_t(v) << (16 * (i & 1));
-        }
+        const uint32_t c = min(g * 8u + i, inner - 1u);
+        v[i] = *reinterpret_cast<const uint16_t*>(c < f.split ? p1 + 2u * c : p2 + 2u * (c - f.split));
       }
-      stage[s] = u32x4{w[0], w[1], w[2], w[3]};
+      stage[s] = pack8(v, min(inner - g * 8u, 8u));
     } else if (rl < nr && g < ng) {
       const char* p = sp + (kOneRow ? so1 : row_off(r0 + rl, e0, e1, nouter, s0, s1, s2)) +
                       uint64_t(g) * 16u;
@@ -1519,12 +1542,7 @@ __device__ __forceinline__ void mx_unit(const Args& a, const MxRegion* R, const 
         __builtin_amdgcn_global_load_lds(p, (lds_void*)(stage + k * kMxThreads + (tid & ~63u)), 16, 0,
                                          RS_MX_LDS_AUX);
       } else {
-        const uint16_t* q = reinterpret_cast<const uint16_t*>(p);
-        const uint32_t n = min(inner - g * 8u, 8u);
-        uint32_t w[4] = {0, 0, 0, 0};
-        for (uint32_t i = 0; i < 8; ++i)
-          if (i < n) w[i >> 1] |= uint32_t(q[i]) << (16 * (i & 1));
-        stage[s] = u32x4{w[0], w[1], w[2], w[3]};
+        stage[s] = gather8(reinterpret_cast<const uint16_t*>(p), min(inner - g * 8u, 8u));
       }
     }
   }
@@ -1536,7 +1554,7 @@ __device__ __forceinline__ void mx_unit(const Args& a, const MxRegion* R, const 
 #pragma unroll
   for (uint32_t k = 0; k < K / 2; ++k) {
     const uint32_t s = 2 * (k * kMxThreads + tid);
-    const uint32_t rl = s >> lg, g = s & (Lp - 1u);
+    const uint32_t rl = row_of(s), g = col_of(s, rl);
     const uint32_t col = g * 8u;
     const int nvalid = rl < nr ? int(min(inner, col + 16u)) - int(min(inner, col)) : 0;
     u32x4 xa = nvalid > 0 ? stage[s] : u32x4{0u, 0u, 0u, 0u};
@@ -1572,11 +1590,12 @@ __device__ __forceinline__ void mx_unit(const Args& a, const MxRegion* R, const 
     }
   }
   // Phase 3: the unit's block scales, block b of row i at LDS byte
-  // (i << lg) / 4 + b, written by consecutive lanes.
+  // i * P / 4 + b, written by consecutive lanes.
   __syncthreads();
   const uint32_t nb = (inner + 31u) >> 5;
   for (uint32_t t = tid; t < kMxSlots / 4; t += kMxThreads) {
-    const uint32_t rl = t >> (lg - 2), b = t & ((Lp >> 2) - 1u);
+    const uint32_t rl = kPitch ? __umulhi(t, msc) : t >> (lg - 2);
+    const uint32_t b = kPitch ? t - rl * (Lp >> 2) : t & ((Lp >> 2) - 1u);
     if (rl < nr && b < nb) {
       const uint64_t so = sc_off_r + row_off(r0 + rl, e0, e1, nouter, c0, c1, c2) + uint64_t(b) * sc_inner;
       const char v = char(sc_stage[t]);
@@ -1589,15 +1608,17 @@ __device__ __forceinline__ void mx_unit(const Args& a, const MxRegion* R, const 
 template <bool kOneRow, class Args>
 __device__ __forceinline__ void mx_unit_fan(const Args& a, const MxRegion* R, const MxFields& f,
                                             uint32_t r0, uint32_t nr, u32x4* stage, uint8_t* sc_stage) {
-  if (f.split < f.inner)
-    mx_unit<kOneRow, false, true>(a, R, f, r0, nr, stage, sc_stage);
-  else if (f.nd == 1)
+  if (f.nd == 1)
     mx_unit<kOneRow, true>(a, R, f, r0, nr, stage, sc_stage);
   else
     mx_unit<kOneRow, false>(a, R, f, r0, nr, stage, sc_stage);
 }
 
-template <class Args>
+// kAux: launches of the two-piece regions and of those whose rows take a
+// pitch that is not a power of two (mx_row_pitch; a two-piece region, one
+// block wide, never does); every unit, one row or several, on the multi-row
+// path.
+template <bool kAux, class Args>
 __global__ __launch_bounds__(kMxThreads, RS_MX_MIN_WAVES) void rs_mx_kernel(Args a) {
   __shared__ u32x4 stage[kMxSlots];
   __shared__ __attribute__((aligned(16))) uint8_t sc_stage[kMxSlots / 4];
@@ -1606,10 +1627,18 @@ __global__ __launch_bounds__(kMxThreads, RS_MX_MIN_WAVES) void rs_mx_kernel(Args
   const uint32_t r0 = (unit - R->unit_begin) * R->rows_per_unit;
   const uint32_t nr = min(R->rows_per_unit, R->rows - r0);
   const MxFields f = mx_fields(a, R);
-  if (nr == 1)
+  if (kAux) {
+    if (f.split < f.inner)
+      mx_unit<false, false, true>(a, R, f, r0, nr, stage, sc_stage);
+    else if (f.nd == 1)
+      mx_unit<false, true, false, true>(a, R, f, r0, nr, stage, sc_stage);
+    else
+      mx_unit<false, false, false, true>(a, R, f, r0, nr, stage, sc_stage);
+  } else if (nr == 1) {
     mx_unit_fan<true>(a, R, f, r0, nr, stage, sc_stage);
-  else
+  } else {
     mx_unit_fan<false>(a, R, f, r0, nr, stage, sc_stage);
+  }
 }
 
 }  // namespace
@@ -1697,7 +1726,12 @@ hipError_t launch_kind(uint32_t bucket, uint32_t grid, const Args& args, hipStre
       hipLaunchKernelGGL((rs_thin_group_kernel<true, Args>), dim3(grid), dim3(kThreads), 0, stream, args);
       break;
     case kTiny: hipLaunchKernelGGL(rs_tiny_kernel<Args>, dim3(grid), dim3(kThreads), 0, stream, args); break;
-    case kMx: hipLaunchKernelGGL(rs_mx_kernel<Args>, dim3(grid), dim3(kMxThreads), 0, stream, args); break;
+    case kMx:
+      hipLaunchKernelGGL((rs_mx_kernel<false, Args>), dim3(grid), dim3(kMxThreads), 0, stream, args);
+      break;
+    case kMxAux:
+      hipLaunchKernelGGL((rs_mx_kernel<true, Args>), dim3(grid), dim3(kMxThreads), 0, stream, args);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -1138,7 +1138,7 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
       f.bucket = kMx;
       const uint64_t row_bytes = r.inner * 2;
       // Whole rows per LDS-staged work unit (a long row is one segment).
-      const uint64_t rpu = kMxSlots >> mx_slot_shift(uint32_t(r.inner));
+      const uint64_t rpu = kMxSlots / mx_row_pitch(uint32_t(r.inner));
       f.rows_per_unit = uint32_t(std::min<uint64_t>(rpu, f.rows));
       const uint64_t nb = (r.inner + kMxBlock - 1) / kMxBlock;
       bytes_read += f.rows * row_bytes;
@@ -1284,24 +1284,27 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
   }
 
   // Launch passes: one per bucket, then the thin groups loaded whole (with
-  // and without narrow members).  Pooled form (table == false): each launch
+  // and without narrow members), then the MXFP8 regions of the second MXFP8
+  // kernel (two-piece, or rows at a pitch that is not a power of two).
+  // Pooled form (table == false): each launch
   // takes regions in order while their pointers fit the kernel-argument pool
   // of kPool entries (pool_cut tells whether that split any pass).  Table
   // form: no pool limit; pool indices are indices into the caller's
   // pointers, source pointers first, then destination pointers (the device
   // table reshard_execute fills).  record: this form's regions and counts
   // go into the plan summary.
+  auto mx_aux = [](const Raw& r) { return r.split < r.inner || mx_pitched(uint32_t(r.inner)); };
   bool pool_cut = false;
   auto emit = [&](bool table, std::vector<uint8_t>& image, std::vector<Launch>& launches, bool record) {
-    for (uint32_t pass = 0; pass <= kBuckets + 1; ++pass) {
-      const uint32_t bucket = pass < kBuckets ? pass : uint32_t(kThin);
-      const uint32_t kernel =
-          pass < kBuckets ? pass : pass == kBuckets ? uint32_t(kThinGroup) : kThinGroupNarrow;
-      const uint8_t want_whole = pass < kBuckets ? 0 : pass == kBuckets ? 1 : 2;
+    for (uint32_t pass = 0; pass <= kBuckets + 2; ++pass) {
+      const uint32_t kernel = pass;   // launch kind: the buckets, kThinGroup, kThinGroupNarrow, kMxAux
+      const uint32_t bucket = bucket_of_kind(kernel);
+      const uint8_t want_whole = kernel == kThinGroup ? 1 : kernel == kThinGroupNarrow ? 2 : 0;
       std::vector<const Final*> list;
       list.reserve(fin.size());
       for (size_t q = 0; q < fin.size(); ++q)
-        if (fin[q].bucket == bucket && (bucket != kThin || whole[q] == want_whole))
+        if (fin[q].bucket == bucket && (bucket != kThin || whole[q] == want_whole) &&
+            (bucket != kMx || mx_aux(*fin[q].rp) == (kernel == kMxAux)))
           list.push_back(&fin[q]);
       size_t i = 0;
       while (i < list.size()) {
@@ -1567,9 +1570,9 @@ rs_status region_info(const PlanData& d, uint64_t index, rs_region* out) {
     const uint64_t k = index - base;
     std::memset(out, 0, sizeof(*out));
     out->tensor = d.region_tensor[index];
-    out->bucket = L.bucket >= kThinGroup ? uint32_t(kThin) : L.bucket;
+    out->bucket = bucket_of_kind(L.bucket);
     auto user = [&](uint16_t slot) { return L.pool[slot] & ~kDstBit; };
-    if (L.bucket == kMx) {
+    if (out->bucket == kMx) {
       MxRegion m;
       std::memcpy(&m, d.image.data() + L.regions_off + k * sizeof(MxRegion), sizeof(m));
       out->src_index = user(m.src_ptr);

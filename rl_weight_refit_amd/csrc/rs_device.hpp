@@ -34,10 +34,10 @@ constexpr uint32_t kSpreadPiece = RS_SPREAD_PIECE;
 static_assert(kSpread >= 1 && kSpreadPiece >= 16 && (kSpreadPiece & (kSpreadPiece - 1)) == 0,
               "spread pieces are a power of two of 16-byte vectors");
 // MXFP8 work units are staged in LDS, kMxSlots 16-byte slots (8 bf16
-// elements each) per workgroup.  A row takes 2^mx_slot_shift(inner) slots
-// (the power of two at or above its 8-element groups, at least one 32-element
-// block), so a unit holds kMxSlots >> mx_slot_shift(inner) whole rows; rows
-// longer than kMxBatchElems are split at block boundaries first.
+// elements each) per workgroup.  A row takes mx_row_pitch(inner) slots
+// (normally the power of two at or above its 8-element groups, at least one
+// 32-element block), so a unit holds kMxSlots / mx_row_pitch(inner) whole
+// rows; rows longer than kMxBatchElems are split at block boundaries first.
 #ifndef RS_MX_SLOTS
 #define RS_MX_SLOTS 1024
 #endif
@@ -54,6 +54,18 @@ constexpr uint32_t mx_slot_shift(uint32_t inner) {
   while ((1u << s) < (inner + 7) / 8) ++s;
   return s;
 }
+// Slots per row of a multi-row MXFP8 unit: 2^mx_slot_shift(inner), unless a
+// pitch of the row's groups plus two spare slots (for rows staged as aligned
+// source lines), rounded up to whole 32-element blocks, fits at least half
+// as many rows again into the kMxSlots (rows of 2,368 elements: 3 at 300
+// slots, 2 at 512; such rows run in launches of their own, which a smaller
+// gain does not pay for).  A pitch that is not a power of two is then never one.
+constexpr uint32_t mx_row_pitch(uint32_t inner) {
+  const uint32_t lp = 1u << mx_slot_shift(inner);
+  const uint32_t p = ((inner + 7) / 8 + 2 + 3) & ~3u;
+  return (p <= kMxSlots && 2 * (kMxSlots / p) >= 3 * (kMxSlots / lp)) ? p : lp;
+}
+constexpr bool mx_pitched(uint32_t inner) { return (mx_row_pitch(inner) & (mx_row_pitch(inner) - 1)) != 0; }
 
 enum Bucket : uint32_t { kBulk = 0, kThin = 1, kTiny = 2, kMx = 3, kBuckets = 4 };
 // Launch kind of thin sibling groups loaded whole (reported as thin regions;
@@ -62,6 +74,17 @@ constexpr uint32_t kThinGroup = kBuckets;
 // The same for groups with a member whose LDS reads are 4 bytes or narrower
 // (that kernel swizzles its LDS slots).
 constexpr uint32_t kThinGroupNarrow = kBuckets + 1;
+// MXFP8 regions off the common shapes -- rows at a pitch that is not a power
+// of two (mx_row_pitch), and two-piece regions (a block two source shards
+// share) -- in launches and a kernel instantiation of their own, so the
+// common kernel keeps its registers.
+constexpr uint32_t kMxAux = kBuckets + 2;
+static_assert(kThinGroup == kBuckets && kThinGroupNarrow == kBuckets + 1 && kMxAux == kBuckets + 2,
+              "launch kinds follow the buckets in this order");
+// Region bucket of a launch kind.
+constexpr uint32_t bucket_of_kind(uint32_t kind) {
+  return kind == kThinGroup || kind == kThinGroupNarrow ? uint32_t(kThin) : kind == kMxAux ? uint32_t(kMx) : kind;
+}
 
 // Region flags.
 enum : uint32_t {

@@ -313,7 +313,22 @@ bool run_case(Rng& g, uint64_t c, bool corrupt) {
   // the thin kernel relies on when it takes their units member-fastest.
   auto walk_units = [&](const std::vector<rs::Launch>& launches, const std::vector<uint8_t>& image) {
   for (const rs::Launch& L : launches) {
-    if (L.bucket == rs::kTiny || L.bucket == rs::kMx) continue;
+    if (L.bucket == rs::kTiny || rs::bucket_of_kind(L.bucket) == rs::kMx) {
+      if (L.bucket == rs::kMx || L.bucket == rs::kMxAux) {
+        // MXFP8 launches: the second kind holds exactly the two-piece
+        // regions and those whose rows take a pitch that is not a power of
+        // two (a two-piece region, one block wide, never does).
+        const rs::MxRegion* mr = reinterpret_cast<const rs::MxRegion*>(image.data() + L.regions_off);
+        for (uint32_t k = 0; k < L.n_regions; ++k) {
+          const bool two = mr[k].split < mr[k].inner, pitched = rs::mx_pitched(mr[k].inner);
+          if ((two || pitched) != (L.bucket == rs::kMxAux)) die("MXFP8 region in the wrong launch kind", c);
+          if (two && pitched) die("two-piece region at a pitch", c);
+          if (mr[k].rows_per_unit != std::min<uint32_t>(mr[k].rows, rs::kMxSlots / rs::mx_row_pitch(mr[k].inner)))
+            die("MXFP8 rows per unit", c);
+        }
+      }
+      continue;
+    }
     const rs::CopyRegion* regs = reinterpret_cast<const rs::CopyRegion*>(image.data() + L.regions_off);
     std::vector<std::vector<uint8_t>> seen(L.n_regions);
     for (uint32_t k = 0; k < L.n_regions; ++k) {
@@ -399,7 +414,7 @@ bool run_case(Rng& g, uint64_t c, bool corrupt) {
         if (ti >= P.table_launches.size()) die("table form has fewer regions", c);
         const rs::Launch& T = P.table_launches[ti];
         if (!T.table || !T.pool.empty() || T.bucket != L.bucket) die("table launch fields", c);
-        if (L.bucket == rs::kMx) {
+        if (rs::bucket_of_kind(L.bucket) == rs::kMx) {
           rs::MxRegion a, b;
           std::memcpy(&a, P.image.data() + L.regions_off + k * sizeof(a), sizeof(a));
           std::memcpy(&b, P.table_image.data() + T.regions_off + tk * sizeof(b), sizeof(b));

@@ -495,6 +495,38 @@ MX_MISALIGNED = {
 }
 
 
+MX_PITCHED = {
+    # rows whose units take a slot pitch that is not a power of two (rows of
+    # 1,088 elements: 7 per unit at 140 slots instead of 4 at 256), from
+    # aligned source rows, with a remainder unit of 5 rows and rows crossing
+    # the outer dim inside a unit
+    "aligned_rows_1088": ([3, 50, 3264], ([3], [2]), ([2], [1])),
+    # misaligned rows of 608 / 576 / 582 elements (two-piece blocks between
+    # them), every destination row to two replicas
+    "replicated_1830": ([2, 30, 1830], ([3], [2]), ([2, 2], [1, -1])),
+    # a last unit of one row
+    "one_row_remainder_1088": ([1, 8, 3264], ([3], [2]), ([1], [-1])),
+    # the DeepSeek-V3 hidden dim from a TP3 source: 2,368-element rows, 3 per
+    # unit at 300 slots
+    "dsv3_like_2368": ([4, 64, 7168], ([3], [2]), ([2], [1])),
+}
+
+
+@pytest.mark.parametrize("shifts", [(0, 0), (2, 3)])
+@pytest.mark.parametrize("name", sorted(MX_PITCHED))
+def test_mxfp8_pitched_units(name, shifts):
+    """MXFP8 regions whose rows are staged at a slot pitch that is not a
+    power of two (the second MXFP8 kernel, which also takes the two-piece
+    regions): several rows per unit, row and scale slots found by a
+    multiply by a reciprocal, byte for byte against the oracle."""
+    shape, (sm, sp), (dm, dp) = MX_PITCHED[name]
+    t = {"name": "w", "shape": shape, "dtype": "bf16", "src": synth.side(sm, sp),
+         "dst": synth.side(dm, dp, quant="mxfp8"), "values": {"kind": "normal", "std": 0.02, "seed": 83}}
+    gh.log("mx pitched %s %s" % (name, shifts))
+    gh.check_against_oracle({"name": "mx_pitch_" + name, "buffers": {}, "tensors": [t]},
+                            src_shift=shifts[0], dst_shift=shifts[1])
+
+
 @pytest.mark.parametrize("shifts", [(0, 0), (2, 3), (6, 0)])
 @pytest.mark.parametrize("name", sorted(MX_MISALIGNED))
 def test_mxfp8_misaligned_source_rows(name, shifts):
