@@ -1393,9 +1393,13 @@ __device__ __forceinline__ u32x4 keep_elems(u32x4 x, int n) {
   return u32x4{keep(x.x, 0), keep(x.y, 1), keep(x.z, 2), keep(x.w, 3)};
 }
 
+// Rows of a pitched unit whose offsets the second MXFP8 kernel keeps in LDS.
+constexpr uint32_t kMxRowTab = 64;
+static_assert(mx_max_pitched_rows() <= kMxRowTab, "a pitched unit's rows fit the row table");
+
 template <bool kOneRow, bool kFan1, bool kTwo = false, bool kPitch = false, class Args>
 __device__ __forceinline__ void mx_unit(const Args& a, const MxRegion* R, const MxFields& f, uint32_t r0,
-                                        uint32_t nr, u32x4* stage, uint8_t* sc_stage) {
+                                        uint32_t nr, u32x4* stage, uint8_t* sc_stage, uint64_t* rt = nullptr) {
   constexpr uint32_t K = kMxSlots / kMxThreads;
   const uint32_t tid = threadIdx.x;
   const uint64_t s0 = f.s0, s1 = f.s1, s2 = f.s2;
@@ -1419,6 +1423,27 @@ __device__ __forceinline__ void mx_unit(const Args& a, const MxRegion* R, const 
   const uint32_t msc = kPitch ? 0xFFFFFFFFu / (Lp >> 2) + 1u : 0u;
   auto row_of = [&](uint32_t s) -> uint32_t { return kPitch ? __umulhi(s, mrow) : s >> lg; };
   auto col_of = [&](uint32_t s, uint32_t rl) -> uint32_t { return kPitch ? s - rl * Lp : s & (Lp - 1u); };
+  // Byte offsets of row rl of the unit (source from sp; destination and
+  // scale including the region's offsets).  kPitch: computed once per row,
+  // by one lane each, into the LDS row table rt, and read from there (no
+  // division per slot).
+  if (kPitch) {
+    if (tid < nr) {
+      rt[tid] = row_off(r0 + tid, e0, e1, nouter, s0, s1, s2);
+      rt[kMxRowTab + tid] = dst_off_r + row_off(r0 + tid, e0, e1, nouter, d0, d1, d2);
+      rt[2 * kMxRowTab + tid] = sc_off_r + row_off(r0 + tid, e0, e1, nouter, c0, c1, c2);
+    }
+    __syncthreads();
+  }
+  auto src_row = [&](uint32_t rl) -> uint64_t {
+    return kPitch ? rt[rl] : kOneRow ? so1 : row_off(r0 + rl, e0, e1, nouter, s0, s1, s2);
+  };
+  auto dst_row = [&](uint32_t rl) -> uint64_t {
+    return kPitch ? rt[kMxRowTab + rl] : dst_off_r + (kOneRow ? do1 : row_off(r0 + rl, e0, e1, nouter, d0, d1, d2));
+  };
+  auto sc_row = [&](uint32_t rl) -> uint64_t {
+    return kPitch ? rt[2 * kMxRowTab + rl] : sc_off_r + row_off(r0 + rl, e0, e1, nouter, c0, c1, c2);
+  };
 
   // Phase 1: every group of the unit into its LDS slot.  Whole, 16-byte
   // aligned groups load straight into LDS; a partial or misaligned group is
@@ -1444,7 +1469,7 @@ __device__ __forceinline__ void mx_unit(const Args& a, const MxRegion* R, const 
     uint32_t pb = 0, pn = 0;   // LDS byte of the first element, element count
     if (tid < 2u * nr) {
       const uint32_t rl = tid >> 1, side = tid & 1u;
-      const char* rs = sp + (kOneRow ? so1 : row_off(r0 + rl, e0, e1, nouter, s0, s1, s2));
+      const char* rs = sp + src_row(rl);
       const uint32_t h = uint32_t(reinterpret_cast<uintptr_t>(rs) & 15u), nb = 2u * inner;
       const uint32_t jl = (h + nb - 1u) >> 4;   // last line
       uint32_t b0 = 0, b1 = 0;                  // row bytes [b0, b1) of this partial line
@@ -1465,7 +1490,7 @@ __device__ __forceinline__ void mx_unit(const Args& a, const MxRegion* R, const 
       const uint32_t s = k * kMxThreads + tid;
       const uint32_t rl = row_of(s), j = col_of(s, rl);
       if (rl < nr) {
-        const char* rs = sp + (kOneRow ? so1 : row_off(r0 + rl, e0, e1, nouter, s0, s1, s2));
+        const char* rs = sp + src_row(rl);
         const int x0 = int(16u * j) - int(reinterpret_cast<uintptr_t>(rs) & 15u);   // row byte at line j
         if (x0 >= 0 && uint32_t(x0) + 16u <= 2u * inner)
           __builtin_amdgcn_global_load_lds(rs + x0, (lds_void*)(stage + k * kMxThreads + (tid & ~63u)), 16, 0,
@@ -1491,7 +1516,7 @@ __device__ __forceinline__ void mx_unit(const Args& a, const MxRegion* R, const 
         fun[kk] = false;
         sh[kk] = 0;
         if (rl < nr && g < ng) {
-          const char* rs = sp + (kOneRow ? so1 : row_off(r0 + rl, e0, e1, nouter, s0, s1, s2));
+          const char* rs = sp + src_row(rl);
           const char* p = rs + uint64_t(g) * 16u;
           const uint32_t r = uint32_t(reinterpret_cast<uintptr_t>(p) & 15u);
           const char* L = p - r;
@@ -1512,7 +1537,7 @@ __device__ __forceinline__ void mx_unit(const Args& a, const MxRegion* R, const 
           stage[s] = sh[kk] ? funnel16(A[kk], B[kk], sh[kk]) : A[kk];
         } else if (rl < nr && g < ng) {
           stage[s] = gather8(reinterpret_cast<const uint16_t*>(
-                                 sp + (kOneRow ? so1 : row_off(r0 + rl, e0, e1, nouter, s0, s1, s2)) +
+                                 sp + src_row(rl) +
                                  uint64_t(g) * 16u),
                              min(inner - g * 8u, 8u));
         }
@@ -1536,7 +1561,7 @@ __device__ __forceinline__ void mx_unit(const Args& a, const MxRegion* R, const 
       }
       stage[s] = pack8(v, min(inner - g * 8u, 8u));
     } else if (rl < nr && g < ng) {
-      const char* p = sp + (kOneRow ? so1 : row_off(r0 + rl, e0, e1, nouter, s0, s1, s2)) +
+      const char* p = sp + src_row(rl) +
                       uint64_t(g) * 16u;
       if (g * 8u + 8u <= inner && (reinterpret_cast<uintptr_t>(p) & 15u) == 0) {
         __builtin_amdgcn_global_load_lds(p, (lds_void*)(stage + k * kMxThreads + (tid & ~63u)), 16, 0,
@@ -1559,10 +1584,20 @@ __device__ __forceinline__ void mx_unit(const Args& a, const MxRegion* R, const 
     const int nvalid = rl < nr ? int(min(inner, col + 16u)) - int(min(inner, col)) : 0;
     u32x4 xa = nvalid > 0 ? stage[s] : u32x4{0u, 0u, 0u, 0u};
     u32x4 xb = nvalid > 8 ? stage[s + 1] : u32x4{0u, 0u, 0u, 0u};
-    if (lines && nvalid > 0) {
+    if (kPitch && lines && nvalid > 0) {
+      // Groups g, g + 1 of the row read straight from bytes h .. h + 31 of
+      // its lines g .. g + 2 (unaligned LDS reads), elements past the row's
+      // end zeroed.
+      const uint32_t h = uint32_t((reinterpret_cast<uintptr_t>(sp) + src_row(rl)) & 15u);
+      const char* lb = reinterpret_cast<const char*>(stage) + 16u * s + h;
+      __builtin_memcpy(&xa, lb, 16);
+      if (nvalid > 8) __builtin_memcpy(&xb, lb + 16, 16);
+      xa = keep_elems(xa, nvalid);
+      xb = keep_elems(xb, nvalid - 8);
+    } else if (lines && nvalid > 0) {
       // Groups g, g + 1 of the row: bytes h .. h + 31 of lines g .. g + 2,
       // elements past the row's end zeroed.
-      const char* rs = sp + (kOneRow ? so1 : row_off(r0 + rl, e0, e1, nouter, s0, s1, s2));
+      const char* rs = sp + src_row(rl);
       const uint32_t h = uint32_t(reinterpret_cast<uintptr_t>(rs) & 15u);
       if (h) {
         const u32x4 L2 = nvalid > 8 ? stage[s + 2] : u32x4{0u, 0u, 0u, 0u};
@@ -1575,7 +1610,7 @@ __device__ __forceinline__ void mx_unit(const Args& a, const MxRegion* R, const 
     }
     const MxCodes c = mx_encode(xa, xb);
     if (nvalid > 0) {
-      const uint64_t doff = dst_off_r + (kOneRow ? do1 : row_off(r0 + rl, e0, e1, nouter, d0, d1, d2)) + col;
+      const uint64_t doff = dst_row(rl) + col;
       for (uint32_t j = 0; j < (kFan1 ? 1u : nd); ++j) {
         char* d = (kFan1 ? dk : static_cast<char*>(pool_ptr(a, dst_pool(R, j)))) + doff;
         if (nvalid == 16 && (reinterpret_cast<uintptr_t>(d) & 15u) == 0) {
@@ -1597,7 +1632,7 @@ __device__ __forceinline__ void mx_unit(const Args& a, const MxRegion* R, const 
     const uint32_t rl = kPitch ? __umulhi(t, msc) : t >> (lg - 2);
     const uint32_t b = kPitch ? t - rl * (Lp >> 2) : t & ((Lp >> 2) - 1u);
     if (rl < nr && b < nb) {
-      const uint64_t so = sc_off_r + row_off(r0 + rl, e0, e1, nouter, c0, c1, c2) + uint64_t(b) * sc_inner;
+      const uint64_t so = sc_row(rl) + uint64_t(b) * sc_inner;
       const char v = char(sc_stage[t]);
       for (uint32_t j = 0; j < (kFan1 ? 1u : nd); ++j)
         __builtin_nontemporal_store(v, (kFan1 ? sk : static_cast<char*>(pool_ptr(a, sc_pool(R, j)))) + so);
@@ -1628,12 +1663,13 @@ __global__ __launch_bounds__(kMxThreads, RS_MX_MIN_WAVES) void rs_mx_kernel(Args
   const uint32_t nr = min(R->rows_per_unit, R->rows - r0);
   const MxFields f = mx_fields(a, R);
   if (kAux) {
+    __shared__ uint64_t rt[3 * kMxRowTab];
     if (f.split < f.inner)
       mx_unit<false, false, true>(a, R, f, r0, nr, stage, sc_stage);
     else if (f.nd == 1)
-      mx_unit<false, true, false, true>(a, R, f, r0, nr, stage, sc_stage);
+      mx_unit<false, true, false, true>(a, R, f, r0, nr, stage, sc_stage, rt);
     else
-      mx_unit<false, false, false, true>(a, R, f, r0, nr, stage, sc_stage);
+      mx_unit<false, false, false, true>(a, R, f, r0, nr, stage, sc_stage, rt);
   } else if (nr == 1) {
     mx_unit_fan<true>(a, R, f, r0, nr, stage, sc_stage);
   } else {

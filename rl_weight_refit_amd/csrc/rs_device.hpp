@@ -66,6 +66,13 @@ constexpr uint32_t mx_row_pitch(uint32_t inner) {
   return (p <= kMxSlots && 2 * (kMxSlots / p) >= 3 * (kMxSlots / lp)) ? p : lp;
 }
 constexpr bool mx_pitched(uint32_t inner) { return (mx_row_pitch(inner) & (mx_row_pitch(inner) - 1)) != 0; }
+// Most rows a unit at a pitch that is not a power of two holds.
+constexpr uint32_t mx_max_pitched_rows() {
+  uint32_t m = 0;
+  for (uint32_t inner = 1; inner <= kMxBatchElems; ++inner)
+    if (mx_pitched(inner) && kMxSlots / mx_row_pitch(inner) > m) m = kMxSlots / mx_row_pitch(inner);
+  return m;
+}
 
 enum Bucket : uint32_t { kBulk = 0, kThin = 1, kTiny = 2, kMx = 3, kBuckets = 4 };
 // Launch kind of thin sibling groups loaded whole (reported as thin regions;
