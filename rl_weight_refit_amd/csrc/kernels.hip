@@ -205,6 +205,16 @@ __device__ __forceinline__ void* pool_ptr(const TableArgs& a, uint32_t i) {
   return (void*)(global_char*)(((const_u64*)(a.ptab))[i]);
 }
 
+// Replica j's destination pointer (j uniform), taken from lane j of the
+// wave, which read it at the unit's start: a pool index read from the table
+// inside a store loop is a vector load, and its wait would also wait for
+// the stores of the replicas before it.
+__device__ __forceinline__ char* replica(uint64_t dl, uint32_t j) {
+  const uint32_t lo = __builtin_amdgcn_readlane(uint32_t(dl), j);
+  const uint32_t hi = __builtin_amdgcn_readlane(uint32_t(dl >> 32), j);
+  return (char*)(global_char*)((uint64_t(hi) << 32) | lo);
+}
+
 // Region of a work unit: the chunk table brackets it, a short binary search
 // over the regions' first units finds it (all loads are uniform).
 template <class Reg, class Args>
@@ -318,7 +328,7 @@ __device__ __forceinline__ void bulk_short_rows(const Args& a, const CopyRegion*
                                                 uint32_t r0, uint32_t r1, uint32_t vpr, uint32_t L,
                                                 uint32_t e0, uint32_t e1, uint32_t nouter,
                                                 uint64_t s0, uint64_t s1, uint64_t s2,
-                                                uint64_t d0, uint64_t d1, uint64_t d2, uint32_t nd) {
+                                                uint64_t d0, uint64_t d1, uint64_t d2, uint32_t nd, uint64_t dl) {
   constexpr int U = RS_UNROLL / M > 0 ? RS_UNROLL / M : 1;
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63u, wave = tid >> 6;
@@ -341,7 +351,7 @@ __device__ __forceinline__ void bulk_short_rows(const Args& a, const CopyRegion*
       }
     }
     for (uint32_t j = 0; j < nd; ++j) {
-      char* d = kFan1 ? dp0 : static_cast<char*>(pool_ptr(a, dst_pool(R, j))) + dst_off;
+      char* d = kFan1 ? dp0 : replica(dl, j);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint32_t r = rb + u * step;
@@ -366,7 +376,7 @@ template <bool kFan1, class Args>
 __device__ __forceinline__ void bulk_short_flat(const Args& a, const CopyRegion* R,
                                                 const char* sp, uint64_t dst_off, uint32_t r0,
                                                 uint32_t r1, uint32_t vpr, uint64_t s0, uint64_t d0,
-                                                uint32_t nd) {
+                                                uint32_t nd, uint64_t dl) {
   constexpr int U = RS_UNROLL;
   const uint32_t tid = threadIdx.x;
   const uint64_t magic = ((uint64_t(1) << 32) + vpr - 1) / vpr;
@@ -384,7 +394,7 @@ __device__ __forceinline__ void bulk_short_flat(const Args& a, const CopyRegion*
       if (f < nvec) x[k] = ld16(sp + uint64_t(r) * s0 + 16ull * v);
     }
     for (uint32_t j = 0; j < nd; ++j) {
-      char* d = static_cast<char*>(pool_ptr(a, dst_pool(R, kFan1 ? 0 : j))) + dst_off;
+      char* d = kFan1 ? static_cast<char*>(pool_ptr(a, dst_pool(R, 0))) + dst_off : replica(dl, j);
 #pragma unroll
       for (int k = 0; k < U; ++k)
         if (f0 + k * kThreads + tid < nvec) st16(d + o[k], x[k]);
@@ -409,7 +419,7 @@ template <bool kFan1, class Args>
 __device__ __forceinline__ void bulk_spread_flat(const Args& a, const CopyRegion* R,
                                                  const char* sp, uint64_t dst_off, uint32_t g0,
                                                  uint32_t j, uint32_t nvec, uint32_t vpr,
-                                                 uint64_t s0, uint64_t d0, uint32_t nd) {
+                                                 uint64_t s0, uint64_t d0, uint32_t nd, uint64_t dl) {
   constexpr int U = RS_UNROLL;
   const uint32_t tid = threadIdx.x;
   const uint64_t magic = ((uint64_t(1) << 32) + vpr - 1) / vpr;
@@ -427,7 +437,7 @@ __device__ __forceinline__ void bulk_spread_flat(const Args& a, const CopyRegion
       if (t < nvec) x[k] = ld16(sp + r * s0 + 16ull * v);
     }
     for (uint32_t jd = 0; jd < nd; ++jd) {
-      char* d = static_cast<char*>(pool_ptr(a, dst_pool(R, kFan1 ? 0 : jd))) + dst_off;
+      char* d = kFan1 ? static_cast<char*>(pool_ptr(a, dst_pool(R, 0))) + dst_off : replica(dl, jd);
 #pragma unroll
       for (int k = 0; k < U; ++k)
         if (t0 + k * kThreads + tid < nvec) st16(d + o[k], x[k]);
@@ -446,7 +456,7 @@ __device__ __forceinline__ void bulk_spread_rows(const Args& a, const CopyRegion
                                                  uint32_t j, uint32_t npu, uint32_t ppr,
                                                  uint32_t e0, uint32_t e1, uint32_t nouter,
                                                  uint64_t s0, uint64_t s1, uint64_t s2,
-                                                 uint64_t d0, uint64_t d1, uint64_t d2, uint32_t nd) {
+                                                 uint64_t d0, uint64_t d1, uint64_t d2, uint32_t nd, uint64_t dl) {
   constexpr int U = RS_UNROLL;
   constexpr uint32_t kStep = kWaves * kSpread;
   const uint32_t lane = threadIdx.x & 63u;
@@ -491,7 +501,7 @@ __device__ __forceinline__ void bulk_spread_rows(const Args& a, const CopyRegion
       }
     }
     for (uint32_t jd = 0; jd < nd; ++jd) {
-      char* d = static_cast<char*>(pool_ptr(a, dst_pool(R, kFan1 ? 0 : jd))) + dst_off;
+      char* d = kFan1 ? static_cast<char*>(pool_ptr(a, dst_pool(R, 0))) + dst_off : replica(dl, jd);
 #pragma unroll
       for (int k = 0; k < U; ++k)
         if (l0 + k * kWaves + wave < npu) st16(d + o[k], x[k]);
@@ -641,7 +651,7 @@ __device__ __forceinline__ void bulk_misaligned_lds(const Args& a, const CopyReg
                                                     uint32_t n, uint32_t lm, uint32_t e0, uint32_t e1,
                                                     uint32_t nouter, uint64_t s0, uint64_t s1, uint64_t s2,
                                                     uint64_t d0, uint64_t d1, uint64_t d2, uint32_t nd,
-                                                    char* lds) {
+                                                    char* lds, uint64_t dl) {
   const uint32_t tid = threadIdx.x;
   // Phase 1: partial-line bytes into registers (edge slot e < 16: row byte
   // e; e >= 16: row byte f1 + e - 16), whole lines into LDS.
@@ -679,7 +689,7 @@ __device__ __forceinline__ void bulk_misaligned_lds(const Args& a, const CopyReg
   const uint32_t blocks = rows * mb;
   const uint64_t magb = ((uint64_t(1) << 32) + mb - 1) / mb;
   for (uint32_t jd = 0; jd < nd; ++jd) {
-    char* dp = kFan1 ? dp0 : static_cast<char*>(pool_ptr(a, dst_pool(R, jd))) + dst_off;
+    char* dp = kFan1 ? dp0 : replica(dl, jd);
     for (uint32_t f = tid; f < blocks; f += kThreads) {
       const uint32_t i = uint32_t((uint64_t(f) * magb) >> 32), b = f - i * mb;
       char* dst = dp + row_off(r0 + i, e0, e1, nouter, d0, d1, d2);
@@ -721,6 +731,10 @@ __device__ __forceinline__ void bulk_body(const Args& a, const CopyRegion* R, ui
   const uint32_t nouter = flags & kFlagOuterMask;
   const char* sp = static_cast<const char*>(pool_ptr(a, src_pool(R))) + src_off;
   char* dp0 = static_cast<char*>(pool_ptr(a, dst_pool(R, 0))) + dst_off;
+  // Several replicas: lane j of each wave holds replica j's pointer.
+  uint64_t dl = 0;
+  if (!kFan1 && (tid & 63u) < nd)
+    dl = reinterpret_cast<uint64_t>(pool_ptr(a, dst_pool(R, tid & 63u))) + dst_off;
 
   uint32_t al = (flags >> 8) & 15u;
   al |= uint32_t(reinterpret_cast<uintptr_t>(sp) & 15u);
@@ -738,12 +752,12 @@ __device__ __forceinline__ void bulk_body(const Args& a, const CopyRegion* R, ui
     const uint64_t g0 = uint64_t(ul - j) * rpu;
     if (g0 + uint64_t(kSpread) * rpu <= rows && nvec % kPieceVec == 0) {
       if (nouter <= 1 && nvec * kSpread * vpr < (uint64_t(1) << 32)) {
-        bulk_spread_flat<kFan1>(a, R, sp, dst_off, uint32_t(g0), j, uint32_t(nvec), vpr, s0, d0, nd);
+        bulk_spread_flat<kFan1>(a, R, sp, dst_off, uint32_t(g0), j, uint32_t(nvec), vpr, s0, d0, nd, dl);
         return;
       }
       if (kPieceVec == 64 && vpr % kPieceVec == 0) {
         bulk_spread_rows<kFan1>(a, R, sp, dst_off, uint32_t(g0), j, uint32_t(nvec / kPieceVec),
-                                vpr / kPieceVec, e0, e1, nouter, s0, s1, s2, d0, d1, d2, nd);
+                                vpr / kPieceVec, e0, e1, nouter, s0, s1, s2, d0, d1, d2, nd, dl);
         return;
       }
     }
@@ -762,7 +776,7 @@ __device__ __forceinline__ void bulk_body(const Args& a, const CopyRegion* R, ui
         for (int k = 0; k < RS_UNROLL; ++k)
           if (v + k * kThreads < vpr) x[k] = ld16(s + 16ull * (v + k * kThreads));
         for (uint32_t j = 0; j < nd; ++j) {
-          char* d = (kFan1 ? dp0 : static_cast<char*>(pool_ptr(a, dst_pool(R, j))) + dst_off) + dof;
+          char* d = (kFan1 ? dp0 : replica(dl, j)) + dof;
 #pragma unroll
           for (int k = 0; k < RS_UNROLL; ++k)
             if (v + k * kThreads < vpr) st16(d + 16ull * (v + k * kThreads), x[k]);
@@ -776,17 +790,17 @@ __device__ __forceinline__ void bulk_body(const Args& a, const CopyRegion* R, ui
     // vectors of each of several rows per iteration.
     const uint32_t vpr = inner >> 4;
     if (nouter <= 1) {
-      bulk_short_flat<kFan1>(a, R, sp, dst_off, r0, r1, vpr, s0, d0, nd);
+      bulk_short_flat<kFan1>(a, R, sp, dst_off, r0, r1, vpr, s0, d0, nd, dl);
       return;
     }
     uint32_t L = 1;
     while (L < vpr && L < 64u) L <<= 1;
     if (vpr > L)
       bulk_short_rows<kFan1, 2>(a, R, sp, dp0, dst_off, r0, r1, vpr, L, e0, e1, nouter,
-                                s0, s1, s2, d0, d1, d2, nd);
+                                s0, s1, s2, d0, d1, d2, nd, dl);
     else
       bulk_short_rows<kFan1, 1>(a, R, sp, dp0, dst_off, r0, r1, vpr, L, e0, e1, nouter,
-                                s0, s1, s2, d0, d1, d2, nd);
+                                s0, s1, s2, d0, d1, d2, nd, dl);
   } else {
 #if RS_MIS_LDS
     // Misaligned rows that fit the staging area, replicas at one alignment:
@@ -799,14 +813,14 @@ __device__ __forceinline__ void bulk_body(const Args& a, const CopyRegion* R, ui
     if (congruent && inner >= kMisMinRow && uint64_t(r1 - r0) * lm * 16u <= kMisTile &&
         (r1 - r0) * 32u <= uint32_t(kMisEdge) * kThreads) {
       bulk_misaligned_lds<kFan1>(a, R, sp, dp0, dst_off, r0, r1 - r0, inner, lm, e0, e1, nouter, s0, s1, s2,
-                                 d0, d1, d2, nd, mis_tile);
+                                 d0, d1, d2, nd, mis_tile, dl);
       return;
     }
 #endif
     // Misaligned: funnel-shifted 16-byte vectors numbered across the unit,
     // once per destination (each replica may sit at its own alignment).
     for (uint32_t j = 0; j < nd; ++j) {
-      char* dp = kFan1 ? dp0 : static_cast<char*>(pool_ptr(a, dst_pool(R, j))) + dst_off;
+      char* dp = kFan1 ? dp0 : replica(dl, j);
       bulk_misaligned_rows(sp, dp, r0, r1, inner, e0, e1, nouter, s0, s1, s2, d0, d1, d2);
     }
   }
