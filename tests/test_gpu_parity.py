@@ -201,6 +201,19 @@ def test_moe_experts_per_expert_sources(shape, quant):
     gh.check_against_oracle(synth.moe_experts(*shape, seed=9, quant=quant, src_split=True))
 
 
+@pytest.mark.parametrize("quant", [None, "mxfp8"])
+def test_per_expert_sources_table_form(quant):
+    """256 per-expert source buffers (768 source pointers, more than one
+    launch's arguments hold): reshard_execute runs the plan's table form (one
+    launch per kernel kind, pointers read from a device table of the plan;
+    the bf16 plan's thin regions as sibling groups loaded whole) against the
+    oracle."""
+    wl = synth.moe_experts(256, 256, 96, 8, 4, 2, seed=9, quant=quant, src_split=True)
+    plan = gh.check_against_oracle(wl)
+    info = plan.info()
+    assert info["n_launches"] < info["n_launches_pooled"], info
+
+
 @pytest.mark.parametrize("shape", MOE_SMALL)
 def test_moe_experts_small_mxfp8(shape):
     gh.check_against_oracle(synth.moe_experts(*shape, seed=9, quant="mxfp8"))

@@ -80,6 +80,9 @@ def test_no_alloc_matches_execute_twice_smaller_second():
 @pytest.mark.parametrize("first,second", [
     (("dense", {}), ("uneven", {"seed": 3})),
     (("moe", {"quant": None}), ("uneven", {"seed": 17})),
+    # 768 per-expert source pointers: reshard_execute runs the plan's table
+    # form (one launch), the no-alloc call its pooled form (two launches)
+    (("experts", {"quant": "mxfp8"}), ("uneven", {"seed": 29})),
 ])
 def test_no_alloc_sequences(first, second):
     """More pairs of calls, larger plan first, each checked against
@@ -93,6 +96,8 @@ def test_no_alloc_sequences(first, second):
             return synth.dense_ffn(hidden=64, inter=320, src_tp=4, dst_tp=2, dst_dp=2)
         if kind == "moe":
             return synth.moe_experts(16, 512, 128, 4, 2, 2, seed=5, **kw)
+        if kind == "experts":
+            return synth.moe_experts(256, 256, 96, 8, 4, 2, seed=5, src_split=True, **kw)
         return synth.uneven_case(kw["seed"], shapes=[[100, 300], [7, 51, 25]])
 
     wa, wb = make(*first), make(*second)
@@ -100,6 +105,8 @@ def test_no_alloc_sequences(first, second):
     pa, ref_a, mine_a = _prepare(wa)
     pb, ref_b, mine_b = _prepare(wb)
     assert pa.info()["n_regions"] > pb.info()["n_regions"]
+    if first[0] == "experts":
+        assert pa.info()["n_launches"] < pa.info()["n_launches_pooled"]
     stream = torch.cuda.current_stream().cuda_stream
     binding.reshard_execute(pa, ref_a[1], ref_a[2], stream)
     binding.reshard_execute(pb, ref_b[1], ref_b[2], stream)
