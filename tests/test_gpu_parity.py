@@ -201,6 +201,19 @@ def test_moe_experts_per_expert_sources(shape, quant):
     gh.check_against_oracle(synth.moe_experts(*shape, seed=9, quant=quant, src_split=True))
 
 
+@pytest.mark.parametrize("shifts", [(0, 0), (2, 6)])
+def test_destination_siblings_interleaved(shifts):
+    """Two pieces of every destination row (TP3 -> TP2 over a 2,049-wide bf16
+    dim, meeting off the 16-byte grid), cut into interleaved chunks of 64
+    units' rows by the planner: byte for byte against the oracle."""
+    t = {"name": "w", "shape": [4, 2049, 2049], "dtype": "bf16", "src": synth.side([3], [2]),
+         "dst": synth.side([2], [2]), "values": {"kind": "normal", "std": 0.02, "seed": 21}}
+    gh.log("siblings %s" % (shifts,))
+    plan = gh.check_against_oracle({"name": "dst_siblings", "buffers": {}, "tensors": [t]},
+                                   src_shift=shifts[0], dst_shift=shifts[1])
+    assert plan.info()["n_regions"] > 4
+
+
 @pytest.mark.parametrize("quant", [None, "mxfp8"])
 def test_per_expert_sources_table_form(quant):
     """256 per-expert source buffers (768 source pointers, more than one

@@ -73,10 +73,13 @@ def test_one_plan_on_several_streams(name):
         gh.check_device(wl["name"], flat)
 
 
-def test_one_plan_from_several_threads():
+@pytest.mark.parametrize("name", ["moe_small_mxfp8", "misc_unpack_many_ptrs"])
+def test_one_plan_from_several_threads(name):
     """Host threads share one plan (the first execute uploads its tables
-    under the plan's lock); each thread has its own stream and buffers."""
-    wl, plan, bufs = _setup("moe_small_mxfp8", copies=4)
+    under the plan's lock; with more pointers than one launch's arguments
+    hold, each thread's pointer set gets its device table under that lock
+    too); each thread has its own stream and buffers."""
+    wl, plan, bufs = _setup(name, copies=4)
     errors = []
 
     def work(k):

@@ -184,6 +184,32 @@ def test_split_mxfp8_destination_needs_two_dims():
     assert e.value.status == 3
 
 
+def test_destination_siblings_interleaved():
+    """A TP3 -> TP2 split of a 2,049-wide bf16 dim cuts each destination row
+    into two pieces from two sources, meeting off a 128-byte boundary: the
+    planner cuts both pieces into chunks of 64 units' rows and interleaves
+    them (each chunk of one piece followed by the same rows of the other),
+    so the 64-byte line the two pieces share is written twice close together
+    in time.  The chunks still cover every row exactly once."""
+    t = {"name": "w", "shape": [4, 2049, 2049], "dtype": "bf16", "src": synth.side([3], [2]),
+         "dst": synth.side([2], [2]), "values": {"kind": "index"}}
+    p = lh.plan_workload({"name": "siblings", "buffers": {}, "tensors": [t]})
+    regs = [p.region(k) for k in range(p.info()["n_regions"])]
+    assert len(regs) > 4
+    rows = {}
+    for a, b in zip(regs[0::2], regs[1::2]):
+        if a["dst_index"] != b["dst_index"]:
+            continue
+        # same destination rows, pieces side by side in them
+        assert a["ext"] == b["ext"] and a["dst_stride"] == b["dst_stride"]
+        assert b["dst_off"] == a["dst_off"] + a["inner"]
+        assert a["src_index"] != b["src_index"]
+    for r in regs:
+        key = (r["dst_index"][0], r["dst_off"] % r["dst_stride"][0])
+        rows[key] = rows.get(key, 0) + r["ext"][0]
+    assert sorted(rows.values()) == [4 * 2049] * 4
+
+
 def test_region_counts_at_full_sizes():
     """Region counts (before fan-out splits) on the layer-sized layouts."""
     p = lh.plan_workload(synth.dense_ffn())
