@@ -1232,26 +1232,50 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
       // boundaries: elsewhere no line is written by two pieces.
       return d.ds > r.inner && ((r.dst_off | r.inner | d.ds) & 127u) != 0;
     };
+    // Group the candidates by key (sorted, so planning stays n log n), each
+    // group led by its first member in plan order.
+    struct Cand {
+      uint64_t k[4];
+      size_t i;
+    };
+    std::vector<Cand> cand;
+    for (size_t i = 0; i < fin.size(); ++i) {
+      Cand c;
+      if (key_of(fin[i], c.k)) {
+        c.i = i;
+        cand.push_back(c);
+      }
+    }
+    std::sort(cand.begin(), cand.end(), [](const Cand& x, const Cand& y) {
+      for (int q = 0; q < 4; ++q)
+        if (x.k[q] != y.k[q]) return x.k[q] < y.k[q];
+      return x.i < y.i;
+    });
+    std::vector<int32_t> group_of_fin(fin.size(), -1);   // group number, -1: none
+    std::vector<std::vector<size_t>> groups;
+    for (size_t a0 = 0; a0 < cand.size();) {
+      size_t a1 = a0 + 1;
+      while (a1 < cand.size() && std::equal(cand[a1].k, cand[a1].k + 4, cand[a0].k)) ++a1;
+      if (a1 - a0 >= 2) {
+        std::vector<size_t> g;
+        for (size_t q = a0; q < a1; ++q) {
+          g.push_back(cand[q].i);
+          group_of_fin[cand[q].i] = int32_t(groups.size());
+        }
+        groups.push_back(std::move(g));
+      }
+      a0 = a1;
+    }
     std::vector<Final> out_fin;
     out_fin.reserve(fin.size());
-    std::vector<uint8_t> done(fin.size(), 0);
     for (size_t i = 0; i < fin.size(); ++i) {
-      if (done[i]) continue;
-      uint64_t ki[4];
-      if (!key_of(fin[i], ki)) {
+      const int32_t gi = group_of_fin[i];
+      if (gi < 0) {
         out_fin.push_back(fin[i]);
         continue;
       }
-      std::vector<size_t> grp{i};
-      for (size_t j = i + 1; j < fin.size(); ++j) {
-        uint64_t kj[4];
-        if (!done[j] && key_of(fin[j], kj) && kj[0] == ki[0] && kj[1] == ki[1] && kj[2] == ki[2] && kj[3] == ki[3])
-          grp.push_back(j);
-      }
-      if (grp.size() < 2) {
-        out_fin.push_back(fin[i]);
-        continue;
-      }
+      const std::vector<size_t>& grp = groups[size_t(gi)];
+      if (grp[0] != i) continue;   // emitted with its group's first member
       uint64_t rpu = 1;
       for (size_t q : grp) rpu = std::max<uint64_t>(rpu, fin[q].rows_per_unit);
       const uint64_t C = uint64_t(RS_DST_CHUNK) * rpu, rows = fin[i].rows;
@@ -1271,7 +1295,6 @@ rs_status build_plan(const rs_tensor_desc* src, const rs_tensor_desc* dst, int32
           out_fin.push_back(g);
         }
       }
-      for (size_t q : grp) done[q] = 1;
     }
     fin.swap(out_fin);
   }
