@@ -15,7 +15,11 @@ Checks, per layer:
 * the A -> B -> A round trip, every source byte.
 A 16-expert slice of the DeepSeek-V3-shaped layer (the same hidden and
 intermediate sizes, meshes and unit shapes) is compared with the oracle
-element by element in full.
+element by element in full.  So are the other large layouts the benchmark
+times: the uneven [16, 8193, 2049] bf16 TP3 -> TP2 layout and the 16M-row
+column slabs, every byte; the MXFP8 install of the DeepSeek-V3 gate and up
+projections from a source cut TP3 along the hidden dim, three whole slots
+per tensor and sampled blocks.
 """
 
 import numpy as np
@@ -92,11 +96,22 @@ def run(wl):
     return plan, src, named
 
 
+def dsv3_gate_up_mxfp8_tp3_source():
+    """The DSV3 gate and up projections installed as MXFP8 from a source cut
+    TP3 along the 7,168-wide hidden dim: rows of 2,390 elements off the
+    16-byte grid, and blocks that straddle two source shards."""
+    wl = synth.moe_dsv3(quant="mxfp8")
+    wl["tensors"] = [dict(t, src=synth.side([3], [2])) for t in wl["tensors"][:2]]
+    wl["name"] += "_gate_up_tp3_hidden_src"
+    return wl
+
+
 WORKLOADS = {
     "moe_128e": synth.moe_128e,
     "moe_dsv3": synth.moe_dsv3,
     "moe_dsv3_per_expert_src": lambda: synth.moe_dsv3(src_split=True),
     "moe_dsv3_mxfp8": lambda: synth.moe_dsv3(quant="mxfp8"),
+    "moe_dsv3_mxfp8_tp3_src": dsv3_gate_up_mxfp8_tp3_source,
 }
 _RUNS = {}
 
@@ -301,9 +316,51 @@ def test_full_size_mxfp8_slots_against_oracle(ti):
     check_slots_against_oracle(wl, ti, src, named, three_slots(wl))
 
 
+def test_full_size_mxfp8_tp3_source_sampled():
+    """MXFP8 install from the TP3-on-hidden source at full size: no poison
+    left in the gate/up element and scale buffers, and sampled blocks (the
+    oracle locates each of a block's 32 values in its own source shard)."""
+    wl, src, named = layer_run("moe_dsv3_mxfp8_tp3_src")
+    for key, buf in named.items():
+        if key.startswith(("w13/", "s13/")):
+            assert no_poison(buf, wl["buffers"][key]["dtype"]), key
+    sampled_mx_check(wl, src, named, 600, np.random.default_rng(3))
+
+
+@pytest.mark.parametrize("ti", [0, 1], ids=["gate", "up"])
+def test_full_size_mxfp8_tp3_source_slots_against_oracle(ti):
+    wl, src, named = layer_run("moe_dsv3_mxfp8_tp3_src")
+    check_slots_against_oracle(wl, ti, src, named, three_slots(wl))
+
+
 def test_release_layer_buffers():
     _RUNS.clear()
     torch.cuda.empty_cache()
+
+
+def test_uneven_bf16_16x8193x2049_tp3_to_tp2_every_byte():
+    """The large uneven bf16 layout, [16, 8193, 2049] TP3 -> TP2 on the last
+    dim (rows of 683 / 342 / 341 elements at offsets that differ modulo 16
+    on the two sides, and destination rows two source pieces share), at full
+    size: every destination byte, poison guards included, against the
+    oracle."""
+    t = {"name": "w", "shape": [16, 8193, 2049], "dtype": "bf16", "src": synth.side([3], [2]),
+         "dst": synth.side([2], [2]), "values": {"kind": "normal", "std": 0.02, "seed": 9}}
+    wl = {"name": "uneven_bf16_16x8193x2049_tp3_to_tp2", "buffers": {}, "tensors": [t]}
+    gh.log("full size %s" % wl["name"])
+    gh.check_against_oracle(wl, poison=POISON)
+
+
+def test_column_slabs_16M_rows_every_byte():
+    """Tall-thin column slabs at full size, [16M, 8] int32 (index values): 2
+    row shards -> 4 column shards through the thin group kernel, every
+    destination byte against the oracle."""
+    t = {"name": "w", "shape": [1 << 24, 8], "dtype": "i32", "src": synth.side([2], [0]),
+         "dst": synth.side([4], [1]), "values": {"kind": "index"}}
+    wl = {"name": "column_slabs_16Mx8_i32_2row_to_4col", "buffers": {}, "tensors": [t]}
+    gh.log("full size %s" % wl["name"])
+    plan = gh.check_against_oracle(wl, poison=POISON)
+    assert plan.info()["regions"]["thin"] == 8
 
 
 @pytest.mark.parametrize("quant,ti", [(None, None), ("mxfp8", 0), ("mxfp8", 1), ("mxfp8", 2)],
