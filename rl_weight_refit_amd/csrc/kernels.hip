@@ -922,6 +922,21 @@ __device__ __forceinline__ void thin_group_body(const Args& a, const CopyRegion*
   const uint64_t s0 = R->sstr[0], s1 = R->sstr[1], s2 = R->sstr[2];
   const char* base = static_cast<const char*>(pool_ptr(a, src_pool(R))) + lo;
   const uint32_t r0 = ul * rpu, r1 = min(r0 + rpu, rows), T = r1 - r0;
+  // The members' fields, read before any store, lane m of every wave holding
+  // member m's (members past 64 read theirs in the store loop): a table read
+  // after a store is a vector load, and its wait would also wait for the
+  // stores of the members before it.  Not in the swizzled instantiation,
+  // where the extra registers would cost it two workgroups per CU.
+  const uint32_t lane = tid & 63u;
+  uint32_t m_cm = 0, m_inner = 0, m_nd = 0;
+  uint64_t m_dst = 0;
+  if (!kSw && lane < gm) {
+    const CopyRegion* M = R + lane;
+    m_cm = uint32_t(M->src_off - lo);
+    m_inner = M->inner;
+    m_nd = n_dst_of(M);
+    m_dst = reinterpret_cast<uint64_t>(pool_ptr(a, dst_pool(M, 0))) + M->dst_off;
+  }
   uint32_t sh = 0;
   bool swz = false;
   if (nouter <= 1 && s0 == S) {
@@ -985,11 +1000,28 @@ __device__ __forceinline__ void thin_group_body(const Args& a, const CopyRegion*
   const char* lds = tile + sh;
   for (uint32_t m = 0; m < gm; ++m) {
     const CopyRegion* M = R + m;
-    const uint32_t cm = uint32_t(M->src_off - lo), inner = M->inner, nd = n_dst_of(M);
+    uint32_t cm, inner, nd;
+    uint64_t d0;
+    if (!kSw && m < 64u) {
+      cm = __builtin_amdgcn_readlane(m_cm, m);
+      inner = __builtin_amdgcn_readlane(m_inner, m);
+      nd = __builtin_amdgcn_readlane(m_nd, m);
+      // readlane returns an int: each half goes through uint32_t, so the
+      // low half is not sign-extended into the high one.
+      const uint32_t dlo = __builtin_amdgcn_readlane(uint32_t(m_dst), m);
+      const uint32_t dhi = __builtin_amdgcn_readlane(uint32_t(m_dst >> 32), m);
+      d0 = (uint64_t(dhi) << 32) | dlo;
+    } else {
+      cm = uint32_t(M->src_off - lo);
+      inner = M->inner;
+      nd = n_dst_of(M);
+      d0 = reinterpret_cast<uint64_t>(pool_ptr(a, dst_pool(M, 0))) + M->dst_off;
+    }
     const uint32_t nbytes = T * inner;
     const uint32_t G = low_granule((sh + cm) | S | inner);
     for (uint32_t j = 0; j < nd; ++j) {
-      char* D = static_cast<char*>(pool_ptr(a, dst_pool(M, j))) + M->dst_off + uint64_t(r0) * inner;
+      char* D = (j == 0 ? (char*)(global_char*)d0 : static_cast<char*>(pool_ptr(a, dst_pool(M, j))) + M->dst_off) +
+                uint64_t(r0) * inner;
       if (kSw && swz) {
         switch (G) {
           case 4: group_store<4, true>(D, lds, cm, S, inner, nbytes, tid); break;
